@@ -1,0 +1,193 @@
+"""MI355X (gfx950) SageBwd trainable INT8 attention: Python binding.
+
+A thin ctypes layer over ``libsagebwd.so`` (declared in include/sagebwd.h).
+It only checks and marshals arguments -- device pointers, sizes, flags and the
+current HIP stream -- and allocates the caller-side buffers with torch; every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is not built, or no GPU is present, the calls raise.
+
+    o, lse = fwd(q, k, v, causal=True, smooth_q=False, smooth_k=True)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True, smooth_q=False, smooth_k=True)
+    o = SageBwdAttention.apply(q, k, v, causal, smooth_q, smooth_k)   # autograd
+
+q, k, v, do: torch.bfloat16 CUDA tensors [B, H, N, 64], contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["fwd", "bwd", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
+           "SageBwdError", "REGIONS", "load_library", "LIB_PATH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsagebwd.so")
+
+REGIONS = {"MU_Q": 0, "MU_K": 1, "Q_R": 2, "K_R": 3, "V_T": 4, "Q_T": 5, "K_T": 6, "DO_T": 7,
+           "S_Q": 8, "S_K": 9, "S_V": 10, "S_DO": 11, "CORR": 12, "BIAS": 13, "DELTA": 14,
+           "LSE2": 15, "DO16": 16, "V16": 17}
+
+
+class SageBwdError(RuntimeError):
+    pass
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32), ("smooth_k", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.POINTER(Params)
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsagebwd.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SageBwdError(f"{LIB_PATH} is not built (run: python bit_trainable_attention_amd/build.py)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.sagebwd_fwd_workspace_size.argtypes = [_P]
+        lib.sagebwd_fwd_workspace_size.restype = _sz
+        lib.sagebwd_bwd_workspace_size.argtypes = [_P]
+        lib.sagebwd_bwd_workspace_size.restype = _sz
+        lib.sagebwd_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_fwd.restype = ctypes.c_int
+        lib.sagebwd_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_bwd.restype = ctypes.c_int
+        lib.sagebwd_prepare.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_prepare.restype = ctypes.c_int
+        lib.sagebwd_ws_region.argtypes = [_P, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
+        lib.sagebwd_ws_region.restype = ctypes.c_int
+        lib.sagebwd_status_string.argtypes = [ctypes.c_int]
+        lib.sagebwd_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def make_params(B, H, N, causal, smooth_q, smooth_k, D=64) -> Params:
+    return Params(int(B), int(H), int(N), int(D), int(bool(causal)), int(bool(smooth_q)), int(bool(smooth_k)))
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load_library().sagebwd_status_string(rc).decode()
+        raise SageBwdError(f"{what} failed: {msg} ({rc})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_qkv(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous()):
+            raise SageBwdError("inputs must be contiguous bfloat16 CUDA tensors [B, H, N, 64]")
+        if t.shape != ref.shape or t.dim() != 4:
+            raise SageBwdError(f"shape mismatch: {tuple(t.shape)} vs {tuple(ref.shape)}")
+
+
+def workspace_size(B, H, N, causal=False, smooth_q=False, smooth_k=True, backward=False) -> int:
+    p = make_params(B, H, N, causal, smooth_q, smooth_k)
+    lib = load_library()
+    n = (lib.sagebwd_bwd_workspace_size if backward else lib.sagebwd_fwd_workspace_size)(ctypes.byref(p))
+    if n == 0:
+        raise SageBwdError("invalid parameters")
+    return int(n)
+
+
+def _workspace(nbytes, device, ws=None):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise SageBwdError("workspace too small")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None):
+    """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N])."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
+    lib = load_library()
+    ws = _workspace(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    rc = lib.sagebwd_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream())
+    _check(rc, "sagebwd_fwd")
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None):
+    """Backward.  Returns (dQ, dK, dV) bf16 [B,H,N,64]."""
+    _check_qkv(q, k, v, o, do)
+    if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3]):
+        raise SageBwdError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
+    B, H, N, D = q.shape
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
+    lib = load_library()
+    ws = _workspace(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    rc = lib.sagebwd_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _check(rc, "sagebwd_bwd")
+    return dq, dk, dv
+
+
+def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True):
+    """Run only the preparation kernels into a fresh backward-sized workspace
+    (uint8 tensor) for inspection; see ws_region for the layout."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
+    lib = load_library()
+    nbytes = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
+    rc = lib.sagebwd_prepare(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                             _ptr(ws), nbytes, _stream())
+    _check(rc, "sagebwd_prepare")
+    return ws
+
+
+def ws_region(params: Params, region) -> tuple:
+    """(byte offset, byte size) of a workspace region (name or id)."""
+    rid = REGIONS[region] if isinstance(region, str) else int(region)
+    off, nb = _sz(), _sz()
+    _check(load_library().sagebwd_ws_region(ctypes.byref(params), rid, ctypes.byref(off), ctypes.byref(nb)),
+           "sagebwd_ws_region")
+    return int(off.value), int(nb.value)
+
+
+class SageBwdAttention(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run the HIP library."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.flags = (causal, smooth_q, smooth_k)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags)
+        return dq, dk, dv, None, None, None

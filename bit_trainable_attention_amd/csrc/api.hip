@@ -1,0 +1,292 @@
+// C ABI of the library: argument validation, workspace layout and the launch
+// sequence of the forward and backward passes.  Declarations and the full
+// contract are in include/sagebwd.h.
+#include "sagebwd.h"
+
+#include "attn.h"
+#include "prep.h"
+
+namespace {
+
+using namespace sagebwd;
+
+enum Region {
+    R_MU_Q = 0, R_MU_K, R_Q_R, R_K_R, R_V_T, R_Q_T, R_K_T, R_DO_T,
+    R_S_Q, R_S_K, R_S_V, R_S_DO, R_CORR, R_BIAS, R_DELTA, R_LSE2, R_DO16, R_V16,
+    R_SUMS, R_COUNT
+};
+
+struct Layout {
+    size_t off[R_COUNT];
+    size_t bytes[R_COUNT];
+    size_t total;
+};
+
+constexpr int32_t MAX_N = 1 << 20;
+constexpr int64_t MAX_BH = 65535;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Which regions a pass uses: the forward needs Q/K row codes and V
+// transposed codes; the backward needs Q/K in both layouts and its own
+// per-row data; the inspection call prepares everything.
+enum Pass { PASS_FWD, PASS_BWD };
+
+Layout make_layout(const sagebwd_params& p, Pass pass) {
+    Layout L{};
+    const size_t BH = (size_t)p.B * p.H;
+    const size_t T = ((size_t)p.N + BLK - 1) / BLK;
+    const size_t Np = T * BLK;
+    const size_t nchunk = ((size_t)p.N + SUM_CHUNK - 1) / SUM_CHUNK;
+    const bool bwd = pass == PASS_BWD;
+    size_t sz[R_COUNT] = {};
+    sz[R_MU_Q] = BH * HD * 4;
+    sz[R_MU_K] = BH * HD * 4;
+    sz[R_Q_R] = BH * T * 4096;
+    sz[R_K_R] = BH * T * 4096;
+    sz[R_V_T] = BH * T * 4096;
+    sz[R_Q_T] = bwd ? BH * T * 4096 : 0;
+    sz[R_K_T] = bwd ? BH * T * 4096 : 0;
+    sz[R_DO_T] = bwd ? BH * T * 4096 : 0;
+    sz[R_S_Q] = BH * T * 4;
+    sz[R_S_K] = BH * T * 4;
+    sz[R_S_V] = BH * T * 4;
+    sz[R_S_DO] = bwd ? BH * T * 4 : 0;
+    sz[R_CORR] = BH * Np * 4;
+    sz[R_BIAS] = BH * Np * 4;
+    sz[R_DELTA] = bwd ? BH * Np * 4 : 0;
+    sz[R_LSE2] = bwd ? BH * Np * 4 : 0;
+    sz[R_DO16] = bwd ? BH * Np * HD * 2 : 0;
+    sz[R_V16] = bwd ? BH * Np * HD * 2 : 0;
+    sz[R_SUMS] = BH * 2 * nchunk * HD * 8;
+    size_t o = 0;
+    for (int r = 0; r < R_COUNT; ++r) {
+        L.off[r] = o;
+        L.bytes[r] = sz[r];
+        o += align256(sz[r]);
+    }
+    L.total = o;
+    return L;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_params(const sagebwd_params* p) {
+    if (!p) return SAGEBWD_ERR_INVALID_ARG;
+    if (p->B < 1 || p->H < 1 || p->N < 1) return SAGEBWD_ERR_INVALID_ARG;
+    if ((p->causal != 0 && p->causal != 1) || (p->smooth_q != 0 && p->smooth_q != 1) ||
+        (p->smooth_k != 0 && p->smooth_k != 1))
+        return SAGEBWD_ERR_INVALID_ARG;
+    if (p->D != HD) return SAGEBWD_ERR_UNSUPPORTED;
+    if (p->N > MAX_N || (int64_t)p->B * p->H > MAX_BH) return SAGEBWD_ERR_UNSUPPORTED;
+    return SAGEBWD_OK;
+}
+
+int check_tensor(const void* ptr) {
+    if (!ptr) return SAGEBWD_ERR_INVALID_ARG;
+    if (!aligned(ptr, 16)) return SAGEBWD_ERR_INVALID_ARG;
+    return SAGEBWD_OK;
+}
+
+int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, 256)) return SAGEBWD_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return SAGEBWD_ERR_WORKSPACE;
+    return SAGEBWD_OK;
+}
+
+template <class T>
+T* region(void* ws, const Layout& L, int r) {
+    return L.bytes[r] ? (T*)((char*)ws + L.off[r]) : nullptr;
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP; }
+
+// Means + quantization of Q, K, V into the regions of this layout.
+void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, const void* K, const void* V,
+                     void* ws, bool want_row, bool want_vt, bool want_qkt, hipStream_t st) {
+    const int BH = p.B * p.H;
+    const int T = (p.N + BLK - 1) / BLK;
+    MeansArgs m{};
+    m.q = (const uint16_t*)Q;
+    m.k = (const uint16_t*)K;
+    m.sums = region<double>(ws, L, R_SUMS);
+    m.mu_q = region<float>(ws, L, R_MU_Q);
+    m.mu_k = region<float>(ws, L, R_MU_K);
+    m.N = p.N;
+    m.BH = BH;
+    m.smooth_q = p.smooth_q;
+    m.smooth_k = p.smooth_k;
+    launch_means(m, st);
+
+    QuantArgs a{};
+    a.q = (const uint16_t*)Q;
+    a.k = (const uint16_t*)K;
+    a.v = (const uint16_t*)V;
+    a.mu_q = m.mu_q;
+    a.mu_k = m.mu_k;
+    a.q_r = want_row ? region<int8_t>(ws, L, R_Q_R) : nullptr;
+    a.k_r = want_row ? region<int8_t>(ws, L, R_K_R) : nullptr;
+    a.q_t = want_qkt ? region<int8_t>(ws, L, R_Q_T) : nullptr;
+    a.k_t = want_qkt ? region<int8_t>(ws, L, R_K_T) : nullptr;
+    a.v_t = want_vt ? region<int8_t>(ws, L, R_V_T) : nullptr;
+    a.sq = region<float>(ws, L, R_S_Q);
+    a.sk = region<float>(ws, L, R_S_K);
+    a.sv = region<float>(ws, L, R_S_V);
+    a.corr = region<float>(ws, L, R_CORR);
+    a.bias = region<float>(ws, L, R_BIAS);
+    a.N = p.N;
+    a.T = T;
+    a.smooth_q = p.smooth_q;
+    a.smooth_k = p.smooth_k;
+    // V's block scales are only needed by the forward and the inspection call
+    launch_quantize(a, BH, want_vt ? 3 : 2, st);
+}
+
+void run_bwd_pre(const sagebwd_params& p, const Layout& L, const void* V, const void* O, const float* LSE,
+                 const void* dO, void* ws, hipStream_t st) {
+    BwdPreArgs b{};
+    b.dout = (const uint16_t*)dO;
+    b.o = (const uint16_t*)O;
+    b.v = (const uint16_t*)V;
+    b.lse = LSE;
+    b.corr = region<float>(ws, L, R_CORR);
+    b.delta = region<float>(ws, L, R_DELTA);
+    b.lse2 = region<float>(ws, L, R_LSE2);
+    b.do_t = region<int8_t>(ws, L, R_DO_T);
+    b.sdo = region<float>(ws, L, R_S_DO);
+    b.do16 = region<_Float16>(ws, L, R_DO16);
+    b.v16 = region<_Float16>(ws, L, R_V16);
+    b.N = p.N;
+    b.T = (p.N + BLK - 1) / BLK;
+    launch_bwd_pre(b, p.B * p.H, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sagebwd_fwd_workspace_size(const sagebwd_params* p) {
+    if (check_params(p) != SAGEBWD_OK) return 0;
+    return make_layout(*p, PASS_FWD).total;
+}
+
+size_t sagebwd_bwd_workspace_size(const sagebwd_params* p) {
+    if (check_params(p) != SAGEBWD_OK) return 0;
+    return make_layout(*p, PASS_BWD).total;
+}
+
+const char* sagebwd_status_string(int status) {
+    switch (status) {
+        case SAGEBWD_OK: return "ok";
+        case SAGEBWD_ERR_INVALID_ARG: return "invalid argument";
+        case SAGEBWD_ERR_UNSUPPORTED: return "unsupported shape";
+        case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
+        case SAGEBWD_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, (const void*)O}) {
+        if ((rc = check_tensor(t))) return rc;
+    }
+    if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
+    const Layout L = make_layout(*p, PASS_FWD);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+
+    run_prepare_qkv(*p, L, Q, K, V, ws, true, true, false, st);
+    FwdArgs a{};
+    a.q_r = region<int8_t>(ws, L, R_Q_R);
+    a.k_r = region<int8_t>(ws, L, R_K_R);
+    a.v_t = region<int8_t>(ws, L, R_V_T);
+    a.sq = region<float>(ws, L, R_S_Q);
+    a.sk = region<float>(ws, L, R_S_K);
+    a.sv = region<float>(ws, L, R_S_V);
+    a.corr = region<float>(ws, L, R_CORR);
+    a.bias = region<float>(ws, L, R_BIAS);
+    a.o = (uint16_t*)O;
+    a.lse = LSE;
+    a.N = p->N;
+    a.T = (p->N + BLK - 1) / BLK;
+    a.ngroups = (a.T + 3) / 4;
+    launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, st);
+    return hip_status();
+}
+
+int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
+                const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                void* stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV}) {
+        if ((rc = check_tensor(t))) return rc;
+    }
+    if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
+    const Layout L = make_layout(*p, PASS_BWD);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+
+    run_prepare_qkv(*p, L, Q, K, V, ws, true, false, true, st);
+    run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+    BwdArgs a{};
+    a.q_r = region<int8_t>(ws, L, R_Q_R);
+    a.k_r = region<int8_t>(ws, L, R_K_R);
+    a.q_t = region<int8_t>(ws, L, R_Q_T);
+    a.k_t = region<int8_t>(ws, L, R_K_T);
+    a.do_t = region<int8_t>(ws, L, R_DO_T);
+    a.sq = region<float>(ws, L, R_S_Q);
+    a.sk = region<float>(ws, L, R_S_K);
+    a.sdo = region<float>(ws, L, R_S_DO);
+    a.bias = region<float>(ws, L, R_BIAS);
+    a.delta = region<float>(ws, L, R_DELTA);
+    a.lse2 = region<float>(ws, L, R_LSE2);
+    a.do16 = region<_Float16>(ws, L, R_DO16);
+    a.v16 = region<_Float16>(ws, L, R_V16);
+    a.mu_q = region<float>(ws, L, R_MU_Q);
+    a.dq = (uint16_t*)dQ;
+    a.dk = (uint16_t*)dK;
+    a.dv = (uint16_t*)dV;
+    a.N = p->N;
+    a.T = (p->N + BLK - 1) / BLK;
+    a.ngroups = (a.T + 3) / 4;
+    launch_bwd(a, p->B * p->H, p->causal, p->smooth_q, st);
+    return hip_status();
+}
+
+int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
+                    const float* LSE, const void* dO, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V}) {
+        if ((rc = check_tensor(t))) return rc;
+    }
+    const bool with_bwd = dO != nullptr;
+    if (with_bwd) {
+        if ((rc = check_tensor(O)) || (rc = check_tensor(dO))) return rc;
+        if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
+    } else if (O || LSE) {
+        return SAGEBWD_ERR_INVALID_ARG;
+    }
+    const Layout L = make_layout(*p, PASS_BWD);
+    if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    run_prepare_qkv(*p, L, Q, K, V, ws, true, true, true, st);
+    if (with_bwd) run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+    return hip_status();
+}
+
+int sagebwd_ws_region(const sagebwd_params* p, int region_id, size_t* offset, size_t* bytes) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    if (region_id < 0 || region_id >= R_SUMS || !offset || !bytes) return SAGEBWD_ERR_INVALID_ARG;
+    const Layout L = make_layout(*p, PASS_BWD);
+    *offset = L.off[region_id];
+    *bytes = L.bytes[region_id];
+    return SAGEBWD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Argument blocks and launchers of the attention kernels.
+#pragma once
+#include "common.h"
+
+namespace sagebwd {
+
+struct FwdArgs {
+    const int8_t *q_r, *k_r, *v_t;     // code blocks [BH][T][4096]
+    const float *sq, *sk, *sv;         // [BH][T]
+    const float *corr, *bias;          // [BH][Np]
+    uint16_t* o;                       // bf16 [BH][N][64]
+    float* lse;                        // [BH][N]
+    int N, T, ngroups;                 // ngroups = ceil(T / 4) (4 waves per group)
+};
+
+struct BwdArgs {
+    const int8_t *q_r, *k_r, *q_t, *k_t, *do_t;
+    const float *sq, *sk, *sdo;        // [BH][T]
+    const float *bias, *delta, *lse2;  // [BH][Np]
+    const _Float16 *do16, *v16;        // [BH][Np][64]
+    const float* mu_q;                 // [BH][64]
+    uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
+    int N, T, ngroups;
+};
+
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
+int launch_bwd(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
+
+// Score-to-probability step shared by both backward kernels, so that the two
+// recompute bit-identical P (and hence identical dS codes): z is the
+// log2-domain score, lse2 the log2-domain log-sum-exp of its row.
+template <bool SMOOTHQ>
+__device__ __forceinline__ float bwd_prob(int acc, float sc, float bias, float lse2) {
+    const float a = (float)acc;
+    if (SMOOTHQ) return __builtin_amdgcn_exp2f(__builtin_fmaf(a, sc, bias) - lse2);
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(a, sc, -lse2));
+}
+__device__ __forceinline__ float tile_scale(float sq, float sk) { return (sq * sk) * SCORE_SCALE_LOG2; }
+
+}  // namespace sagebwd

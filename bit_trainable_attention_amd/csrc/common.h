@@ -1,0 +1,105 @@
+// Shared device helpers for the gfx950 SageBwd kernels.
+//
+// MFMA conventions used throughout (32x32 tiles, one wave of 64 lanes; lane
+// l, half h = l/32):
+//   INT8  v_mfma_i32_32x32x32_i8 : A lane l holds row l%32 and 16 k-bytes,
+//                                  B lane l holds column l%32 and the same 16
+//                                  k positions; D lane l, register r holds
+//                                  element (row 8*(r/4) + 4*h + r%4, column l%32).
+//   FP16  v_mfma_f32_32x32x16_f16: A/B lane l hold 8 halves of row/column l%32;
+//                                  D as above.
+// Because the k positions of A and B in one lane agree, any fixed assignment
+// of the contraction index to (half, byte) works as long as both operands use
+// it.  Two code layouts per 64x64 block follow from this:
+//   row operand  (token is the M/N index, channel the k index),
+//   transposed   (channel is the M/N index, token the k index, with the
+//                 token order of a D register column: byte b of half h is
+//                 token 8*(b/4) + 4*h + b%4 of the 32-token k-step),
+// so the P / dS codes produced in D registers feed the next MFMA directly.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sagebwd {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int BLK = 64;                    // tokens per block, tile side
+constexpr int HD = 64;                     // head dimension
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float LOG2_127 = 6.988684686772166f;
+constexpr float SCORE_SCALE_LOG2 = LOG2E * 0.125f;   // 1/sqrt(64) folded into log2 domain
+// 1.5 * 2^23: adding it rounds a float in (-2^22, 2^22) to the nearest
+// integer (ties to even) and leaves that integer in the low mantissa bits.
+constexpr float MAGIC = 12582912.0f;
+constexpr uint32_t MAGIC_BITS = 0x4B400000u;
+constexpr float A_MIN = 0x1p-100f;         // smaller block absmax -> all-zero block
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Per-block scale from an absmax: s = a/127 and inv = 127/a, both correctly
+// rounded float32 divisions; blocks with a < 2^-100 are all-zero.
+__device__ __forceinline__ void block_scale(float a, float& s, float& inv) {
+    if (a >= A_MIN) {
+        s = a / 127.0f;
+        inv = 127.0f / a;
+    } else {
+        s = 0.0f;
+        inv = 0.0f;
+    }
+}
+
+// round-half-even(x * inv) of the exact product, as magic-biased float bits:
+// the low byte is the two's-complement int8 code.
+__device__ __forceinline__ uint32_t code_bits(float x, float inv) {
+    return __float_as_uint(__builtin_fmaf(x, inv, MAGIC));
+}
+__device__ __forceinline__ int code_int(float x, float inv) {
+    return (int)(code_bits(x, inv) - MAGIC_BITS);
+}
+// rne(v) for v already scaled (0 <= v < 2^22), as magic-biased bits.
+__device__ __forceinline__ uint32_t round_bits(float v) {
+    return __float_as_uint(v + MAGIC);
+}
+
+// Pack the low bytes of four words into one dword (byte 0 from a).
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);   // [a0, b0, 0, 0]
+    uint32_t hi = __builtin_amdgcn_perm(d, c, 0x04000c0cu);   // [0, 0, c0, d0]
+    return lo | hi;
+}
+
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Wave-wide reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float half_swap(float v) { return __shfl_xor(v, 32, 64); }
+
+// Byte offsets of element (token r, channel c) inside a 64x64 code block.
+__host__ __device__ constexpr int row_operand_offset(int r, int c) {
+    return (((r / 32) * 2 + c / 32) * 64 + 32 * ((c % 32) / 16) + r % 32) * 16 + c % 16;
+}
+__host__ __device__ constexpr int transposed_operand_offset(int r, int c) {
+    return (((c / 32) * 2 + r / 32) * 64 + 32 * ((r % 8) / 4) + c % 32) * 16 + 4 * ((r % 32) / 8) + r % 4;
+}
+
+}  // namespace sagebwd

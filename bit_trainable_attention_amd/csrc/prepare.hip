@@ -1,0 +1,272 @@
+// Preparation kernels: K/Q smoothing means, per-block INT8 quantization of
+// Q, K, V into the MFMA operand layouts, and the backward's per-row
+// preprocessing (Delta, log2-domain LSE, dO codes, FP16 copies of dO and V).
+//
+// SageBwd (abstract, insight iv): K-smoothing subtracts the token mean of K
+// per head, which shifts every score row by a constant that softmax ignores;
+// Q-smoothing is optional.  Quantization is symmetric INT8 with one
+// absmax/127 scale per block of 64 tokens x 64 channels.  These kernels are
+// bound by HBM bandwidth: every input element is read once and one code byte
+// (plus, for the backward, one FP16 copy) is written.
+#include "prep.h"
+
+namespace sagebwd {
+
+// ---------------------------------------------------------------- means
+// Partial float64 column sums of K (tensor 0) and Q (tensor 1) over chunks
+// of SUM_CHUNK tokens.  The order of additions is fixed; for bf16 inputs
+// every partial sum is exact in practice (the oracle checks the condition),
+// so the final mean does not depend on the order at all.
+__global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ q,
+                                                const uint16_t* __restrict__ k,
+                                                double* __restrict__ sums, int N, int nchunk,
+                                                int do_q, int do_k) {
+    const int chunk = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+    if ((tensor == 0 && !do_k) || (tensor == 1 && !do_q)) return;
+    const uint16_t* src = (tensor == 0 ? k : q) + (size_t)bh * N * HD;
+    const int g = threadIdx.x % 8;            // 8 channels per thread
+    const int tr = threadIdx.x / 8;           // 32 token rows
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int t0 = chunk * SUM_CHUNK;
+    for (int s = 0; s < SUM_CHUNK / 32; ++s) {
+        const int tok = t0 + tr + 32 * s;
+        if (tok < N) {
+            const uint4 u = *(const uint4*)(src + (size_t)tok * HD + 8 * g);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += (double)bf16_to_f32(w[j] & 0xFFFFu);
+                acc[2 * j + 1] += (double)bf16_to_f32(w[j] >> 16);
+            }
+        }
+    }
+    __shared__ double part[32][HD];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[tr][8 * g + j] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < HD) {
+        double s = 0.0;
+        for (int r = 0; r < 32; ++r) s += part[r][threadIdx.x];
+        sums[(((size_t)bh * 2 + tensor) * nchunk + chunk) * HD + threadIdx.x] = s;
+    }
+}
+
+// mu = fp32(fp64(sum) / N); zero when the tensor is not smoothed.
+__global__ __launch_bounds__(128) void k_means(const double* __restrict__ sums, float* __restrict__ mu_q,
+                                               float* __restrict__ mu_k, int N, int nchunk, int do_q,
+                                               int do_k) {
+    const int bh = blockIdx.x, tensor = threadIdx.x / HD, c = threadIdx.x % HD;
+    const int on = tensor == 0 ? do_k : do_q;
+    float m = 0.0f;
+    if (on) {
+        double s = 0.0;
+        const double* p = sums + ((size_t)bh * 2 + tensor) * nchunk * HD + c;
+        for (int i = 0; i < nchunk; ++i) s += p[(size_t)i * HD];
+        m = (float)(s / (double)N);
+    }
+    (tensor == 0 ? mu_k : mu_q)[(size_t)bh * HD + c] = m;
+}
+
+// ---------------------------------------------------------------- quantize
+// One workgroup per 64-token block of one tensor.  Thread (r = tid/4,
+// g = tid%4) owns token r, channels 16g..16g+15.
+__device__ __forceinline__ float block_absmax_256(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    return a;
+}
+
+// Write the 4 KB code block held in LDS (codes[token][channel]) in the
+// transposed operand layout: thread tid builds 16-byte chunk tid.
+__device__ __forceinline__ void store_transposed(const int8_t (*codes)[HD], int8_t* dst) {
+    const int tid = threadIdx.x;
+    const int db = tid / 128, ks = (tid / 64) % 2, lane = tid % 64, h = lane / 32;
+    const int c = 32 * db + lane % 32;
+    uint32_t w[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 32 * ks + 8 * q4 + 4 * h + j;
+            x |= (uint32_t)(uint8_t)codes[r][c] << (8 * j);
+        }
+        w[q4] = x;
+    }
+    *(uint4*)(dst + tid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// tensor 0 = Q, 1 = K, 2 = V.
+__global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
+    const int t = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+    const int r = threadIdx.x / 4, g = threadIdx.x % 4;
+    const int tok = t * BLK + r;
+    const bool valid = tok < a.N;
+    const uint16_t* src = (tensor == 0 ? a.q : tensor == 1 ? a.k : a.v) + ((size_t)bh * a.N + tok) * HD + 16 * g;
+    const float* mu = tensor == 0 ? a.mu_q : tensor == 1 ? a.mu_k : nullptr;
+    float raw[16], x[16];
+    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+    if (valid) {
+        u0 = *(const uint4*)src;
+        u1 = *(const uint4*)(src + 8);
+    }
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        raw[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+        raw[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        x[j] = mu ? raw[j] - mu[(size_t)bh * HD + 16 * g + j] : raw[j];
+        if (!valid) x[j] = 0.0f;
+        amax = fmaxf(amax, fabsf(x[j]));
+    }
+    __shared__ float red[4];
+    __shared__ int8_t codes[BLK][HD];
+    const float a_blk = block_absmax_256(amax, red);
+    float s, inv;
+    block_scale(a_blk, s, inv);
+    const size_t blk = (size_t)bh * a.T + t;
+    float* scale_out = tensor == 0 ? a.sq : tensor == 1 ? a.sk : a.sv;
+    if (threadIdx.x == 0) scale_out[blk] = s;
+
+    uint32_t cw[4] = {0, 0, 0, 0};
+    float mu_dot = 0.0f;   // K only: sum_c mu_q[c] * code[c]
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int cq = code_int(x[j], inv);
+        codes[r][16 * g + j] = (int8_t)cq;
+        cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
+        if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], (float)cq, mu_dot);
+    }
+    int8_t* rdst = tensor == 0 ? a.q_r : tensor == 1 ? a.k_r : nullptr;
+    if (rdst) *(uint4*)(rdst + blk * 4096 + row_operand_offset(r, 16 * g)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+
+    // per-token side outputs
+    if (tensor == 0) {
+        float cd = 0.0f;
+        if (a.smooth_k) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], a.mu_k[(size_t)bh * HD + 16 * g + j], cd);
+        }
+        cd += __shfl_xor(cd, 1, 64);
+        cd += __shfl_xor(cd, 2, 64);
+        if (g == 0) a.corr[(size_t)bh * a.T * BLK + tok] = valid ? cd * 0.125f : 0.0f;
+    } else if (tensor == 1) {
+        mu_dot += __shfl_xor(mu_dot, 1, 64);
+        mu_dot += __shfl_xor(mu_dot, 2, 64);
+        if (g == 0) a.bias[(size_t)bh * a.T * BLK + tok] = (valid && a.smooth_q) ? mu_dot * s * SCORE_SCALE_LOG2 : 0.0f;
+    }
+
+    int8_t* tdst = tensor == 0 ? a.q_t : tensor == 1 ? a.k_t : a.v_t;
+    if (tdst) {
+        __syncthreads();
+        store_transposed(codes, tdst + blk * 4096);
+    }
+}
+
+// ---------------------------------------------------------------- backward prep
+// One workgroup per 64-token block: Delta = rowsum(dO*O) (fp32), the
+// log2-domain LSE of the smoothed scores, dO codes (transposed operand
+// layout) and scale, FP16 copies of dO and V.  Rows past N are zeroed (their
+// LSE is +inf so every P of such a row is 0).
+__global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
+    const int t = blockIdx.x, bh = blockIdx.y;
+    const int r = threadIdx.x / 4, g = threadIdx.x % 4;
+    const int tok = t * BLK + r;
+    const bool valid = tok < a.N;
+    const size_t in_off = ((size_t)bh * a.N + tok) * HD + 16 * g;
+    float dov[16], ov[16], vv[16];
+    uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0, o0 = d0, o1 = d0, v0 = d0, v1 = d0;
+    if (valid) {
+        d0 = *(const uint4*)(a.dout + in_off);
+        d1 = *(const uint4*)(a.dout + in_off + 8);
+        o0 = *(const uint4*)(a.o + in_off);
+        o1 = *(const uint4*)(a.o + in_off + 8);
+        v0 = *(const uint4*)(a.v + in_off);
+        v1 = *(const uint4*)(a.v + in_off + 8);
+    }
+    const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const uint32_t ow[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float delta = 0.0f, amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        dov[2 * j] = bf16_to_f32(dw[j] & 0xFFFFu);
+        dov[2 * j + 1] = bf16_to_f32(dw[j] >> 16);
+        ov[2 * j] = bf16_to_f32(ow[j] & 0xFFFFu);
+        ov[2 * j + 1] = bf16_to_f32(ow[j] >> 16);
+        vv[2 * j] = bf16_to_f32(vw[j] & 0xFFFFu);
+        vv[2 * j + 1] = bf16_to_f32(vw[j] >> 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        delta = __builtin_fmaf(dov[j], ov[j], delta);
+        amax = fmaxf(amax, fabsf(dov[j]));
+    }
+    delta += __shfl_xor(delta, 1, 64);
+    delta += __shfl_xor(delta, 2, 64);
+    const size_t row = (size_t)bh * a.T * BLK + tok;
+    if (g == 0) {
+        a.delta[row] = valid ? delta : 0.0f;
+        a.lse2[row] = valid ? (a.lse[(size_t)bh * a.N + tok] - a.corr[row]) * LOG2E : __builtin_inff();
+    }
+    // FP16 copies (natural layout [Np][64])
+    {
+        uint32_t hw[8], vh[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            _Float16 a0 = (_Float16)dov[2 * j], a1 = (_Float16)dov[2 * j + 1];
+            _Float16 b0 = (_Float16)vv[2 * j], b1 = (_Float16)vv[2 * j + 1];
+            hw[j] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+            vh[j] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        }
+        uint4* dd = (uint4*)(a.do16 + row * HD + 16 * g);
+        dd[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        dd[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        uint4* vd = (uint4*)(a.v16 + row * HD + 16 * g);
+        vd[0] = make_uint4(vh[0], vh[1], vh[2], vh[3]);
+        vd[1] = make_uint4(vh[4], vh[5], vh[6], vh[7]);
+    }
+    // dO codes
+    __shared__ float red[4];
+    __shared__ int8_t codes[BLK][HD];
+    const float a_blk = block_absmax_256(amax, red);
+    float s, inv;
+    block_scale(a_blk, s, inv);
+    const size_t blk = (size_t)bh * a.T + t;
+    if (threadIdx.x == 0) a.sdo[blk] = s;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) codes[r][16 * g + j] = (int8_t)code_int(dov[j], inv);
+    __syncthreads();
+    store_transposed(codes, a.do_t + blk * 4096);
+}
+
+// ---------------------------------------------------------------- launchers
+int launch_means(const MeansArgs& m, hipStream_t st) {
+    const int nchunk = (m.N + SUM_CHUNK - 1) / SUM_CHUNK;
+    if (m.smooth_q || m.smooth_k) {
+        hipLaunchKernelGGL(k_colsum, dim3(nchunk, m.BH, 2), dim3(256), 0, st, m.q, m.k, m.sums, m.N, nchunk,
+                           m.smooth_q, m.smooth_k);
+    }
+    hipLaunchKernelGGL(k_means, dim3(m.BH), dim3(128), 0, st, m.sums, m.mu_q, m.mu_k, m.N, nchunk, m.smooth_q,
+                       m.smooth_k);
+    return 0;
+}
+
+int launch_quantize(const QuantArgs& a, int BH, int ntensors, hipStream_t st) {
+    hipLaunchKernelGGL(k_quantize, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
+    return 0;
+}
+
+int launch_bwd_pre(const BwdPreArgs& a, int BH, hipStream_t st) {
+    hipLaunchKernelGGL(k_bwd_pre, dim3(a.T, BH), dim3(256), 0, st, a);
+    return 0;
+}
+
+}  // namespace sagebwd

@@ -1,0 +1,135 @@
+/*
+ * sagebwd.h -- C ABI of the MI355X (gfx950) SageBwd trainable INT8 attention.
+ *
+ * What is computed (SageBwd: A Trainable Low-bit Attention, abstract; the
+ * SageAttention3 summary page, sections "Approach" and "Measured effects"):
+ * softmax attention forward and backward in which six of the seven matmuls
+ * run on INT8 operands with 32-bit integer accumulation -- forward Q K^T and
+ * P~ V, backward Q K^T (recomputed), P^T dO, dS K and dS^T Q -- while the
+ * seventh, dO V^T, runs in FP16 with FP32 accumulation.  Operands are
+ * prepared with K-smoothing (subtract the per-head token mean of K; softmax
+ * ignores the resulting per-row shift) and optional Q-smoothing, then
+ * quantized symmetrically per block of 64 tokens x 64 channels with scale
+ * absmax/127.  P~ in [0,1] uses the fixed scale 1/127 against its tile-row
+ * maximum; P and dS in the backward use one absmax/127 scale per 64x64 tile.
+ * The forward/backward structure (online softmax, log-sum-exp, Delta =
+ * rowsum(dO*O)) is FlashAttention-2's, listed under "Builds on" on the
+ * SageBwd page.
+ *
+ * Layout and types (every call):
+ *   Q, K, V, O, dO, dQ, dK, dV : bfloat16, contiguous [B, H, N, D], D = 64
+ *                                innermost, 16-byte aligned device pointers.
+ *   LSE                        : float32 [B, H, N], natural log of the row sum
+ *                                of exp(score) with score = q.k / 8 (the
+ *                                un-smoothed scores), device pointer.
+ *   softmax scale              : fixed 1/sqrt(64) = 1/8.
+ *   causal                     : keep key j <= query i (top-left aligned).
+ *
+ * Ownership: the caller owns every buffer, including the workspace, whose
+ * size the *_workspace_size calls give (256-byte aligned device memory).
+ * The library allocates nothing, keeps no global state, never synchronizes
+ * the host, and enqueues all work on ``stream`` (a hipStream_t; NULL means
+ * the default stream).  Outputs are overwritten, never accumulated into, and
+ * must not alias inputs or the workspace.  Calls on distinct streams with
+ * distinct workspaces may run concurrently.
+ *
+ * Errors: 0 on success, a negative SAGEBWD_ERR_* code otherwise.  Argument
+ * checks (null pointers, sizes, flags, alignment, workspace size) happen
+ * before any HIP call, so a failing call launches nothing.  A launch failure
+ * reported by the HIP runtime returns SAGEBWD_ERR_HIP.  Not checked:
+ * finiteness of the inputs, and |dO|, |V| <= 65504 (they are converted to
+ * FP16 for dO V^T).
+ */
+#ifndef SAGEBWD_H
+#define SAGEBWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sagebwd_params {
+    int32_t B;          /* batch, >= 1 */
+    int32_t H;          /* heads, >= 1 */
+    int32_t N;          /* tokens (queries = keys), 1 <= N <= 2^20 */
+    int32_t D;          /* head dimension, must be 64 */
+    int32_t causal;     /* 0 or 1 */
+    int32_t smooth_q;   /* 0 or 1: subtract the per-head token mean of Q */
+    int32_t smooth_k;   /* 0 or 1: subtract the per-head token mean of K */
+} sagebwd_params;
+
+#define SAGEBWD_OK               0
+#define SAGEBWD_ERR_INVALID_ARG (-1)   /* null pointer, size < 1, flag not 0/1, misaligned */
+#define SAGEBWD_ERR_UNSUPPORTED (-2)   /* D != 64, or N or B*H beyond the supported range */
+#define SAGEBWD_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the required size */
+#define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
+
+/* Workspace bytes needed by sagebwd_fwd / sagebwd_bwd for these params;
+ * 0 if the params are invalid. */
+size_t sagebwd_fwd_workspace_size(const sagebwd_params* p);
+size_t sagebwd_bwd_workspace_size(const sagebwd_params* p);
+
+/* Forward.  Reads Q, K, V; writes O [B,H,N,64] bf16 and LSE [B,H,N] fp32. */
+int sagebwd_fwd(const sagebwd_params* p,
+                const void* Q, const void* K, const void* V,
+                void* O, float* LSE,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Backward.  Reads Q, K, V, the forward's O and LSE, and dO (all as above,
+ * with the same params as the forward call); writes dQ, dK, dV
+ * [B,H,N,64] bf16.  It re-quantizes Q, K, V itself (bit-identical codes to
+ * the forward's). */
+int sagebwd_bwd(const sagebwd_params* p,
+                const void* Q, const void* K, const void* V,
+                const void* O, const float* LSE, const void* dO,
+                void* dQ, void* dK, void* dV,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* sagebwd_status_string(int status);
+
+/* ---- inspection entry points (used by the bit-exact tests) ---------------
+ *
+ * sagebwd_prepare runs only the preparation kernels of sagebwd_bwd
+ * (smoothing means, block quantization of Q, K, V and dO, Delta and the
+ * backward's log2-domain LSE) into a backward-sized workspace, so the codes,
+ * scales and means can be read back and compared bit for bit.  O and LSE may
+ * be NULL together with dO (then only Q, K, V are prepared).
+ *
+ * sagebwd_ws_region returns the byte offset and size of one region of that
+ * workspace; the region ids and their layouts are:
+ *   0  MU_Q   float32 [BH][64]       Q token means (0 if !smooth_q)
+ *   1  MU_K   float32 [BH][64]       K token means (0 if !smooth_k)
+ *   2  Q_R    int8  [BH][T][4096]    Q codes, "row operand" layout
+ *   3  K_R    int8  [BH][T][4096]    K codes, row operand layout
+ *   4  V_T    int8  [BH][T][4096]    V codes, "transposed operand" layout
+ *   5  Q_T    int8  [BH][T][4096]    Q codes, transposed operand layout
+ *   6  K_T    int8  [BH][T][4096]    K codes, transposed operand layout
+ *   7  DO_T   int8  [BH][T][4096]    dO codes, transposed operand layout
+ *   8  S_Q    float32 [BH][T]        block scales (likewise 9 S_K, 10 S_V, 11 S_DO)
+ *   12 CORR   float32 [BH][Np]       q_raw . mu_K / 8 per query (0 past N)
+ *   13 BIAS   float32 [BH][Np]       Q-smoothing key bias mu_Q . K^_j times log2(e)/8
+ *   14 DELTA  float32 [BH][Np]       rowsum(dO * O)
+ *   15 LSE2   float32 [BH][Np]       (LSE - CORR) * log2(e); +inf past N
+ *   16 DO16   fp16 [BH][Np][64]      dO in FP16, natural layout
+ *   17 V16    fp16 [BH][Np][64]      V in FP16, natural layout
+ * with T = ceil(N/64), Np = 64 T.  Within a 4096-byte block of 64 tokens x
+ * 64 channels, element (token r, channel c) sits at byte
+ *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16
+ *   transposed operand:  ((c/32*2 + r/32)*64 + 32*((r%8)/4) + c%32)*16
+ *                          + 4*((r%32)/8) + r%4
+ * so that one 16-byte load per lane feeds a 32x32x32 INT8 MFMA operand.
+ * Returns SAGEBWD_ERR_INVALID_ARG for an unknown region id. */
+int sagebwd_prepare(const sagebwd_params* p,
+                    const void* Q, const void* K, const void* V,
+                    const void* O, const float* LSE, const void* dO,
+                    void* ws, size_t ws_bytes, void* stream);
+int sagebwd_ws_region(const sagebwd_params* p, int region, size_t* offset, size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGEBWD_H */

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/sagebwd.h declares, and rejects bad arguments with the
+documented status codes before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_trainable_attention_amd as sb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sb.load_library()
+
+
+def declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names |= set(re.findall(r"\b(sagebwd_\w+)\s*\(", txt))
+    return sorted(names)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"sagebwd_fwd", "sagebwd_bwd", "sagebwd_fwd_workspace_size", "sagebwd_bwd_workspace_size",
+            "sagebwd_status_string", "sagebwd_prepare", "sagebwd_ws_region"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def P(**kw):
+    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64)
+    d.update(kw)
+    return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"])
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
+
+
+def call_fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, nbytes=1 << 40):
+    return lib.sagebwd_fwd(None if p is None else ctypes.byref(p), q, k, v, o, lse, ws, nbytes, None)
+
+
+def call_bwd(lib, p, ptrs=None, lse=FAKE, ws=FAKE, nbytes=1 << 40):
+    q, k, v, o, do, dq, dk, dv = ptrs or [FAKE] * 8
+    return lib.sagebwd_bwd(None if p is None else ctypes.byref(p), q, k, v, o, lse, do, dq, dk, dv, ws, nbytes, None)
+
+
+def test_param_validation(lib):
+    assert call_fwd(lib, None) == INVALID
+    assert call_fwd(lib, P(B=0)) == INVALID
+    assert call_fwd(lib, P(H=-1)) == INVALID
+    assert call_fwd(lib, P(N=0)) == INVALID
+    assert call_fwd(lib, P(causal=2)) == INVALID
+    assert call_fwd(lib, P(smooth_q=-1)) == INVALID
+    assert call_fwd(lib, P(smooth_k=7)) == INVALID
+    assert call_fwd(lib, P(D=128)) == UNSUPPORTED
+    assert call_fwd(lib, P(N=(1 << 20) + 1)) == UNSUPPORTED
+    assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED
+    assert call_bwd(lib, P(D=32)) == UNSUPPORTED
+    assert call_bwd(lib, P(N=-5)) == INVALID
+
+
+def test_pointer_validation(lib):
+    p = P()
+    assert call_fwd(lib, p, q=None) == INVALID
+    assert call_fwd(lib, p, v=FAKE + 2) == INVALID          # bf16 tensors need 16-byte alignment
+    assert call_fwd(lib, p, lse=None) == INVALID
+    assert call_fwd(lib, p, lse=FAKE + 2) == INVALID
+    assert call_fwd(lib, p, ws=None) == INVALID
+    assert call_fwd(lib, p, ws=FAKE + 128) == INVALID       # workspace needs 256-byte alignment
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert call_bwd(lib, p, ptrs) == INVALID
+        ptrs[i] = FAKE + 8
+        assert call_bwd(lib, p, ptrs) == INVALID
+    assert call_bwd(lib, p, lse=None) == INVALID
+
+
+def test_workspace_validation(lib):
+    p = P(N=1000, causal=1, smooth_q=1)
+    nf = lib.sagebwd_fwd_workspace_size(ctypes.byref(p))
+    nb = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
+    assert 0 < nf < nb
+    assert call_fwd(lib, p, nbytes=nf - 1) == WORKSPACE
+    assert call_bwd(lib, p, nbytes=nb - 1) == WORKSPACE
+    assert call_bwd(lib, p, nbytes=nf) == WORKSPACE
+    bad = P(D=16)
+    assert lib.sagebwd_fwd_workspace_size(ctypes.byref(bad)) == 0
+    assert lib.sagebwd_bwd_workspace_size(ctypes.byref(bad)) == 0
+    assert lib.sagebwd_fwd_workspace_size(None) == 0
+
+
+def test_prepare_validation(lib):
+    p = P()
+    f = lambda *a: lib.sagebwd_prepare(ctypes.byref(p), *a, None)
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 40) == INVALID   # LSE without dO
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40) == INVALID   # dO without LSE
+    assert f(None, FAKE, FAKE, None, None, None, FAKE, 1 << 40) == INVALID
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, 10) == WORKSPACE
+
+
+def test_ws_regions_layout(lib):
+    for N in (1, 63, 64, 65, 1000, 17776):
+        p = P(B=2, H=3, N=N)
+        BH, T = 6, (N + 63) // 64
+        Np = 64 * T
+        expect = {"MU_Q": BH * 256, "MU_K": BH * 256, "Q_R": BH * T * 4096, "K_R": BH * T * 4096,
+                  "V_T": BH * T * 4096, "Q_T": BH * T * 4096, "K_T": BH * T * 4096, "DO_T": BH * T * 4096,
+                  "S_Q": BH * T * 4, "S_K": BH * T * 4, "S_V": BH * T * 4, "S_DO": BH * T * 4,
+                  "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "DELTA": BH * Np * 4, "LSE2": BH * Np * 4,
+                  "DO16": BH * Np * 128, "V16": BH * Np * 128}
+        spans = []
+        for name, rid in sb.REGIONS.items():
+            off, nb = sb.ws_region(p, rid)
+            assert off % 256 == 0
+            assert nb == expect[name], (name, nb)
+            spans.append((off, off + nb))
+        spans.sort()
+        for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        total = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
+        assert spans[-1][1] <= total
+    off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sagebwd_ws_region(ctypes.byref(P()), 18, ctypes.byref(off), ctypes.byref(nb)) == INVALID
+    assert lib.sagebwd_ws_region(ctypes.byref(P()), -1, ctypes.byref(off), ctypes.byref(nb)) == INVALID
+
+
+def test_status_strings(lib):
+    for rc, s in ((OK, b"ok"), (INVALID, b"invalid argument"), (UNSUPPORTED, b"unsupported shape"),
+                  (WORKSPACE, b"workspace too small"), (HIPERR, b"HIP launch error"), (-99, b"unknown status")):
+        assert lib.sagebwd_status_string(rc) == s
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(sb.SageBwdError):
+        sb.fwd(q, q, q)
