@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
+__all__ = ["fwd", "bwd", "fwd_stage", "bwd_stage", "STAGES", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
            "SageBwdError", "REGIONS", "load_library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,6 +28,9 @@ LIB_PATH = os.path.join(_HERE, "libsagebwd.so")
 REGIONS = {"MU_Q": 0, "MU_K": 1, "Q_R": 2, "K_R": 3, "V_T": 4, "Q_T": 5, "K_T": 6, "DO_T": 7,
            "S_Q": 8, "S_K": 9, "S_V": 10, "S_DO": 11, "CORR": 12, "BIAS": 13, "DELTA": 14,
            "LSE2": 15, "DO16": 16, "V16": 17}
+
+
+STAGES = {"FWD_PREPARE": 0, "FWD_ATTN": 1, "BWD_PREPARE": 2, "BWD_DKDV": 3, "BWD_DQ": 4}
 
 
 class SageBwdError(RuntimeError):
@@ -60,6 +63,10 @@ def load_library() -> ctypes.CDLL:
         lib.sagebwd_fwd.restype = ctypes.c_int
         lib.sagebwd_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_bwd.restype = ctypes.c_int
+        lib.sagebwd_fwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_fwd_stage.restype = ctypes.c_int
+        lib.sagebwd_bwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_bwd_stage.restype = ctypes.c_int
         lib.sagebwd_prepare.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_prepare.restype = ctypes.c_int
         lib.sagebwd_ws_region.argtypes = [_P, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
@@ -149,6 +156,23 @@ def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, worksp
                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(rc, "sagebwd_bwd")
     return dq, dk, dv
+
+
+def fwd_stage(stage, q, k, v, o, lse, ws, params: Params):
+    """Run one forward stage (see STAGES) on caller-owned buffers; no checks
+    beyond the library's own."""
+    rc = load_library().sagebwd_fwd_stage(ctypes.byref(params), STAGES[stage] if isinstance(stage, str) else stage,
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream())
+    _check(rc, f"sagebwd_fwd_stage({stage})")
+
+
+def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params):
+    """Run one backward stage (see STAGES) on caller-owned buffers."""
+    rc = load_library().sagebwd_bwd_stage(ctypes.byref(params), STAGES[stage] if isinstance(stage, str) else stage,
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _check(rc, f"sagebwd_bwd_stage({stage})")
 
 
 def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True):

@@ -186,10 +186,11 @@ const char* sagebwd_status_string(int status) {
     }
 }
 
-int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                void* ws, size_t ws_bytes, void* stream) {
+int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const void* K, const void* V, void* O,
+                      float* LSE, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (stage != SAGEBWD_STAGE_FWD_PREPARE && stage != SAGEBWD_STAGE_FWD_ATTN) return SAGEBWD_ERR_INVALID_ARG;
     for (const void* t : {Q, K, V, (const void*)O}) {
         if ((rc = check_tensor(t))) return rc;
     }
@@ -197,8 +198,10 @@ int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const voi
     const Layout L = make_layout(*p, PASS_FWD);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
-
-    run_prepare_qkv(*p, L, Q, K, V, ws, true, true, false, st);
+    if (stage == SAGEBWD_STAGE_FWD_PREPARE) {
+        run_prepare_qkv(*p, L, Q, K, V, ws, true, true, false, st);
+        return hip_status();
+    }
     FwdArgs a{};
     a.q_r = region<int8_t>(ws, L, R_Q_R);
     a.k_r = region<int8_t>(ws, L, R_K_R);
@@ -217,11 +220,20 @@ int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const voi
     return hip_status();
 }
 
-int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
-                const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
-                void* stream) {
+int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                void* ws, size_t ws_bytes, void* stream) {
+    int rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_ATTN, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const void* K, const void* V,
+                      const void* O, const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws,
+                      size_t ws_bytes, void* stream) {
     int rc = check_params(p);
     if (rc) return rc;
+    if (stage != SAGEBWD_STAGE_BWD_PREPARE && stage != SAGEBWD_STAGE_BWD_DKDV && stage != SAGEBWD_STAGE_BWD_DQ)
+        return SAGEBWD_ERR_INVALID_ARG;
     for (const void* t : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV}) {
         if ((rc = check_tensor(t))) return rc;
     }
@@ -229,9 +241,11 @@ int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const voi
     const Layout L = make_layout(*p, PASS_BWD);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
-
-    run_prepare_qkv(*p, L, Q, K, V, ws, true, false, true, st);
-    run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+    if (stage == SAGEBWD_STAGE_BWD_PREPARE) {
+        run_prepare_qkv(*p, L, Q, K, V, ws, true, false, true, st);
+        run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+        return hip_status();
+    }
     BwdArgs a{};
     a.q_r = region<int8_t>(ws, L, R_Q_R);
     a.k_r = region<int8_t>(ws, L, R_K_R);
@@ -253,8 +267,19 @@ int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const voi
     a.N = p->N;
     a.T = (p->N + BLK - 1) / BLK;
     a.ngroups = (a.T + 3) / 4;
-    launch_bwd(a, p->B * p->H, p->causal, p->smooth_q, st);
+    if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, st);
+    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();
+}
+
+int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
+                const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+                void* stream) {
+    for (int stage : {SAGEBWD_STAGE_BWD_PREPARE, SAGEBWD_STAGE_BWD_DKDV, SAGEBWD_STAGE_BWD_DQ}) {
+        const int rc = sagebwd_bwd_stage(p, stage, Q, K, V, O, LSE, dO, dQ, dK, dV, ws, ws_bytes, stream);
+        if (rc) return rc;
+    }
+    return SAGEBWD_OK;
 }
 
 int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,

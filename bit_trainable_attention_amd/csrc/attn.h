@@ -24,7 +24,8 @@ struct BwdArgs {
 };
 
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
-int launch_bwd(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
 
 // Score-to-probability step shared by both backward kernels, so that the two
 // recompute bit-identical P (and hence identical dS codes): z is the

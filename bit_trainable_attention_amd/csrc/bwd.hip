@@ -394,21 +394,27 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
     }
 }
 
-int launch_bwd(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
     dim3 grid(a.ngroups, BH), block(256);
-#define SAGEBWD_LAUNCH2(C, S)                                                   \
-    do {                                                                        \
-        hipLaunchKernelGGL((k_bwd_dkdv<C, S>), grid, block, 0, st, a);          \
-        hipLaunchKernelGGL((k_bwd_dq<C, S>), grid, block, 0, st, a);            \
-    } while (0)
     if (causal) {
-        if (smooth_q) SAGEBWD_LAUNCH2(true, true);
-        else SAGEBWD_LAUNCH2(true, false);
+        if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv<true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dkdv<true, false>), grid, block, 0, st, a);
     } else {
-        if (smooth_q) SAGEBWD_LAUNCH2(false, true);
-        else SAGEBWD_LAUNCH2(false, false);
+        if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dkdv<false, false>), grid, block, 0, st, a);
     }
-#undef SAGEBWD_LAUNCH2
+    return 0;
+}
+
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
+    dim3 grid(a.ngroups, BH), block(256);
+    if (causal) {
+        if (smooth_q) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);
+    } else {
+        if (smooth_q) hipLaunchKernelGGL((k_bwd_dq<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<false, false>), grid, block, 0, st, a);
+    }
     return 0;
 }
 

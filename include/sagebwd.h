@@ -87,6 +87,32 @@ int sagebwd_bwd(const sagebwd_params* p,
                 void* dQ, void* dK, void* dV,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* Stages.  sagebwd_fwd runs FWD_PREPARE then FWD_ATTN; sagebwd_bwd runs
+ * BWD_PREPARE, BWD_DKDV, BWD_DQ, all on the same stream.  The stage calls run
+ * one stage each, for callers that schedule or time them separately; a stage
+ * reads what the earlier stages of its pass wrote into ``ws`` (same params,
+ * inputs and workspace), and the full sequence is exactly the pass.
+ *   FWD_PREPARE  smoothing means; Q, K, V block quantization
+ *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
+ *   BWD_PREPARE  means and quantization again; Delta, log2 LSE, dO codes,
+ *                FP16 copies of dO and V
+ *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T)
+ *   BWD_DQ       dQ (INT8 QK^T and dS K; FP16 dO V^T) */
+#define SAGEBWD_STAGE_FWD_PREPARE 0
+#define SAGEBWD_STAGE_FWD_ATTN    1
+#define SAGEBWD_STAGE_BWD_PREPARE 2
+#define SAGEBWD_STAGE_BWD_DKDV    3
+#define SAGEBWD_STAGE_BWD_DQ      4
+int sagebwd_fwd_stage(const sagebwd_params* p, int stage,
+                      const void* Q, const void* K, const void* V,
+                      void* O, float* LSE,
+                      void* ws, size_t ws_bytes, void* stream);
+int sagebwd_bwd_stage(const sagebwd_params* p, int stage,
+                      const void* Q, const void* K, const void* V,
+                      const void* O, const float* LSE, const void* dO,
+                      void* dQ, void* dK, void* dV,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* sagebwd_status_string(int status);
 

@@ -146,3 +146,15 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(sb.SageBwdError):
         sb.fwd(q, q, q)
+
+
+def test_stage_validation(lib):
+    p = P()
+    f = lambda stage, nb=1 << 40: lib.sagebwd_fwd_stage(ctypes.byref(p), stage, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nb, None)
+    b = lambda stage, nb=1 << 40: lib.sagebwd_bwd_stage(ctypes.byref(p), stage, *([FAKE] * 10), nb, None)
+    for bad in (-1, 2, 3, 4, 5):
+        assert f(bad) == INVALID
+    for bad in (-1, 0, 1, 5):
+        assert b(bad) == INVALID
+    assert f(0, nb=1) == WORKSPACE and f(1, nb=1) == WORKSPACE
+    assert b(2, nb=1) == WORKSPACE and b(3, nb=1) == WORKSPACE and b(4, nb=1) == WORKSPACE
