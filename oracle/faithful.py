@@ -25,7 +25,10 @@ with its reason, in the design notes that ship with the library):
                        P^ = exp(S - m); code = round_half_even(127 P^) in [0,127]
                        (fixed scale 1/127 on P~ in [0,1]).
   F7  PV tile          B = P~_code V_code_t (exact integers).
-  F8  combine          M = max_t m_t, w_t = exp(m_t - M), l = sum_t w_t sum_j P^,
+  F8  combine          M = max_t m_t, w_t = exp(m_t - M),
+                       l = sum_t w_t sum_j P~_code / 127   (the row sum of the
+                       quantized probabilities, so O is exactly the normalized
+                       product of the dequantized P~ and V),
                        O = sum_t w_t (s_V,t / 127) B_t / l,
                        LSE = M + ln l + (q_raw . mu_k) / 8   (true-score frame).
   B1  backward prep    same codes as the forward; dO quantized with F3 (no
@@ -264,7 +267,7 @@ def fwd_head(pp: Prepared, causal: bool, qblocks=None, reading: str = "B",
         M = np.max(m, axis=1)                                    # [R]
         with np.errstate(invalid="ignore"):
             w = np.where(np.isfinite(m), np.exp(mf - M[:, None]), 0.0)   # [R, T]
-        l = np.sum(w * np.sum(phat, axis=2), axis=1)             # [R]
+        l = np.sum(w * np.sum(codes, axis=2), axis=1) / 127.0    # [R]
         acc = np.einsum("rt,trc->rc", w * (svt / 127.0)[None, :], Bt)
         with np.errstate(invalid="ignore", divide="ignore"):
             o = acc / l[:, None]
@@ -315,7 +318,7 @@ def fwd_head_loop(pp: Prepared, causal: bool, reading: str = "B"):
             with np.errstate(invalid="ignore"):
                 alpha = np.where(np.isfinite(M), np.exp(M - M_new), 0.0)
                 w = np.where(live, np.exp(mr - M_new), 0.0)
-            l = l * alpha + w * np.sum(phat, axis=1)
+            l = l * alpha + w * np.sum(c, axis=1) / 127.0
             acc = acc * alpha[:, None] + (w * float(pp.sv[t]) / 127.0)[:, None] * Bt
             M = M_new
         with np.errstate(invalid="ignore", divide="ignore"):
