@@ -215,7 +215,8 @@ int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     a.lse = LSE;
     a.N = p->N;
     a.T = (p->N + BLK - 1) / BLK;
-    a.ngroups = (a.T + 3) / 4;
+    a.ngroups = (a.T + 1) / 2;
+    a.BH = p->B * p->H;
     launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();
 }

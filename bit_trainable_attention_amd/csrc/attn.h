@@ -10,7 +10,7 @@ struct FwdArgs {
     const float *corr, *bias;          // [BH][Np]
     uint16_t* o;                       // bf16 [BH][N][64]
     float* lse;                        // [BH][N]
-    int N, T, ngroups;                 // ngroups = ceil(T / 4) (4 waves per group)
+    int N, T, ngroups, BH;             // ngroups = ceil(T / 2): 128 query rows per workgroup
 };
 
 struct BwdArgs {

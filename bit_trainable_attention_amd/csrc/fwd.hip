@@ -2,190 +2,231 @@
 // online softmax in registers, P~ codes with the fixed scale 1/127 against
 // the tile-row maximum, O^T += V^T P~^T on INT8 MFMA, then O and LSE.
 //
-// SageBwd (abstract): the two forward matmuls are among the six INT8 ones.
-// The tile loop and the online softmax (running max, running sum, rescaling)
+// SageBwd (abstract): both forward matmuls are among the six INT8 ones.  The
+// tile loop and the online softmax (running max, running sum, rescaling)
 // follow FlashAttention-2 (under "Builds on" on the SageBwd page).
 //
-// Work split: one wave owns 64 query rows (one quantization block of Q) and
-// walks the key blocks; 4 waves per workgroup, each independent.  Computing
-// S^T instead of S puts one query per lane column, so every softmax row
-// statistic lives in one lane (plus its partner in the other half-wave), and
-// the P~ codes leave the accumulator already in the B-operand layout of the
-// V^T P~^T product.  K and V code tiles are loaded from L2 straight into
-// registers (16 bytes per lane per 32x32 operand).
+// Work split (gfx950): a workgroup of 4 waves owns 128 query rows (two
+// quantization blocks of Q); each wave owns 32 of them.  The K and V code
+// tiles of each 64-key step are loaded once per workgroup into LDS, double
+// buffered and fetched one step ahead, and every wave reads its MFMA operands
+// from there (16 bytes per lane per 32x32 operand).  Computing S^T rather than
+// S puts one query per lane column, so every softmax row statistic lives in
+// one lane and its partner in the other half-wave, and the P~ codes leave the
+// accumulator already in the B-operand layout of V^T P~^T.  At most 256
+// registers per wave keep two waves resident per SIMD.  Workgroups of one
+// head are dealt to one XCD (its K/V codes then stay in that XCD's L2),
+// longest causal rows first.
 #include "attn.h"
 
 namespace sagebwd {
 
-template <bool CAUSAL, bool SMOOTHQ>
-__global__ __launch_bounds__(256) void k_fwd(FwdArgs a) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32, l32 = lane % 32;
-    const int bh = blockIdx.y;
-    const int iq = (a.ngroups - 1 - blockIdx.x) * 4 + wave;   // longest causal rows first
-    if (iq >= a.T) return;
-    const size_t bt = (size_t)bh * a.T;
-    const size_t np = (size_t)a.T * BLK;
+constexpr int FWD_WAVES = 4;
+constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 units; O and L may grow by up to 2^8
 
-    v4i qop[2][2];
-    {
-        const v4i* src = (const v4i*)(a.q_r + (bt + iq) * 4096);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) qop[qb][ks] = src[(qb * 2 + ks) * 64 + lane];
+struct FwdSmem {
+    v4i k[2][256];       // K row-operand code tile, 2 buffers
+    v4i v[2][256];       // V transposed-operand code tile
+    float bias[2][64];   // Q-smoothing key bias (log2 domain)
+};
+
+// Workgroup -> (head, query group).  Consecutive workgroup ids are dealt to
+// the 8 XCDs in turn; when the head count allows, all groups of a head go to
+// the same XCD.  Within a head the longest causal rows come first.
+__device__ __forceinline__ void map_group(int ngroups, int BH, int& bh, int& g) {
+    const int L = blockIdx.x;
+    if ((BH & 7) == 0) {
+        const int xcd = L & 7, s = L >> 3;
+        bh = (s / ngroups) * 8 + xcd;
+        g = ngroups - 1 - (s % ngroups);
+    } else {
+        bh = L / ngroups;
+        g = ngroups - 1 - (L % ngroups);
     }
-    const float sQ = a.sq[bt + iq];
+}
 
-    float M[2] = {-__builtin_inff(), -__builtin_inff()};
-    float L[2] = {0.0f, 0.0f};          // per half-wave partial sums of 127 * P^
-    v16f O[2][2];                        // [qb][db]: lane = query, registers = channels
+// One 64-key step of one wave: scores, tile-row max, P~ codes, online update
+// and the P~V product.  MASK is set only for the causal diagonal tile and the
+// ragged last tile, so the common path carries no per-element selects.
+template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+__device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (&qop)[2], float sc, float sv,
+                                         int t, int q, int N, int lane, int h, float& M, float& L, v16f (&O)[2]) {
+    v16i s[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
+        s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qop[1], s[kb]);
+    }
+    float z[2][16];
 #pragma unroll
-        for (int db = 0; db < 2; ++db) O[qb][db] = v16f{};
-
-    const int t_end = CAUSAL ? iq : a.T - 1;
-    const bool ragged = (a.N % BLK) != 0;
-    for (int t = 0; t <= t_end; ++t) {
-        v4i kop[2][2], vop[2][2];
-        {
-            const v4i* ks_ = (const v4i*)(a.k_r + (bt + t) * 4096);
-            const v4i* vs_ = (const v4i*)(a.v_t + (bt + t) * 4096);
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    kop[x][ks] = ks_[(x * 2 + ks) * 64 + lane];
-                    vop[x][ks] = vs_[(x * 2 + ks) * 64 + lane];
-                }
-        }
-        const float sc = tile_scale(sQ, a.sk[bt + t]);
-        const float sv = a.sv[bt + t];
-
-        v16i s[2][2];   // [kb][qb]
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[kb][qb] = mfma_i8(kop[kb][0], qop[qb][0], v16i{});
-                s[kb][qb] = mfma_i8(kop[kb][1], qop[qb][1], s[kb][qb]);
-            }
-
-        float z[2][2][16];
-        float bias[2][16];
+    for (int kb = 0; kb < 2; ++kb) {
+        float bias[16];
         if (SMOOTHQ) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 b4 = *(const float4*)(a.bias + bh * np + t * BLK + 32 * kb + 8 * r4 + 4 * h);
-                    bias[kb][4 * r4 + 0] = b4.x;
-                    bias[kb][4 * r4 + 1] = b4.y;
-                    bias[kb][4 * r4 + 2] = b4.z;
-                    bias[kb][4 * r4 + 3] = b4.w;
-                }
-        }
-        const bool need_mask = (CAUSAL && t == iq) || (ragged && t == a.T - 1);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float af = (float)s[kb][qb][r];
-                    z[kb][qb][r] = SMOOTHQ ? __builtin_fmaf(af, sc, bias[kb][r]) : af * sc;
-                }
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-                        const int q = iq * BLK + 32 * qb + l32;
-                        if (key >= a.N || (CAUSAL && key > q)) z[kb][qb][r] = -__builtin_inff();
-                    }
-        }
-
-        v4i pc[2][2];   // [qb][kb] B operand of V^T P~^T (k = keys of step kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, z[kb][qb][r]);
-            mx = fmaxf(mx, half_swap(mx));
-            const bool live = mx > -__builtin_inff();
-            const float mref = live ? mx - LOG2_127 : 0.0f;
-            float ls = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                uint32_t bits[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float v = __builtin_amdgcn_exp2f(z[kb][qb][r] - mref);   // 127 * P^
-                    ls += v;
-                    bits[r] = round_bits(v);
-                }
-                pc[qb][kb] = v4i{(int)pack4(bits[0], bits[1], bits[2], bits[3]),
-                                 (int)pack4(bits[4], bits[5], bits[6], bits[7]),
-                                 (int)pack4(bits[8], bits[9], bits[10], bits[11]),
-                                 (int)pack4(bits[12], bits[13], bits[14], bits[15])};
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                bias[4 * r4 + 0] = b4.x;
+                bias[4 * r4 + 1] = b4.y;
+                bias[4 * r4 + 2] = b4.z;
+                bias[4 * r4 + 3] = b4.w;
             }
-            // online update (tile weight exp2(mx - M) folds in the V scale)
-            const float m_new = live ? fmaxf(M[qb], mx) : M[qb];
-            const float alpha = M[qb] > -__builtin_inff() ? __builtin_amdgcn_exp2f(M[qb] - m_new) : 0.0f;
-            const float e = live ? __builtin_amdgcn_exp2f(mx - m_new) : 0.0f;
-            L[qb] = __builtin_fmaf(L[qb], alpha, e * ls);
-            M[qb] = m_new;
-            if (__any(alpha != 1.0f)) {
+        }
 #pragma unroll
-                for (int db = 0; db < 2; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) O[qb][db][r] *= alpha;
-            }
-            const float w = e * sv;
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                v16i pv = mfma_i8(vop[db][0], pc[qb][0], v16i{});
-                pv = mfma_i8(vop[db][1], pc[qb][1], pv);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) O[qb][db][r] = __builtin_fmaf((float)pv[r], w, O[qb][db][r]);
+        for (int r = 0; r < 16; ++r) {
+            const float af = (float)s[kb][r];
+            z[kb][r] = SMOOTHQ ? __builtin_fmaf(af, sc, bias[r]) : af;
+            if (MASK) {
+                const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+                if (key >= N || (CAUSAL && key > q)) z[kb][r] = -__builtin_inff();
             }
         }
     }
-
-    // epilogue: O / L in bf16, LSE in natural log of the un-smoothed scores
+    float mx = -__builtin_inff();
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float Lt = L[qb] + half_swap(L[qb]);
-        const int q = iq * BLK + 32 * qb + l32;
-        if (q < a.N) {
-            const float inv_l = 1.0f / Lt;
-            uint16_t* orow = a.o + ((size_t)bh * a.N + q) * HD;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(z[kb][r], z[kb][r + 1]));
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+    }
+    // tile-row max in log2 units; the code is rne(127 * exp2(score - max))
+    const float mt = SMOOTHQ ? mx : mx * sc;
+    const float off = LOG2_127 - mt;
+    const bool row_live = !MASK || mx > -__builtin_inff();
+    v4i pc[2];
+    uint32_t csum = 0;
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * db + 8 * r4 + 4 * h;
-                    const uint32_t w0 = f32_to_bf16_rne(O[qb][db][4 * r4 + 0] * inv_l) |
-                                        (f32_to_bf16_rne(O[qb][db][4 * r4 + 1] * inv_l) << 16);
-                    const uint32_t w1 = f32_to_bf16_rne(O[qb][db][4 * r4 + 2] * inv_l) |
-                                        (f32_to_bf16_rne(O[qb][db][4 * r4 + 3] * inv_l) << 16);
-                    *(uint2*)(orow + d) = make_uint2(w0, w1);
-                }
-            if (h == 0) {
-                const float lse2 = M[qb] + log2f(Lt) - LOG2_127;   // log2 of the row sum
-                a.lse[(size_t)bh * a.N + q] = lse2 * LN2 + a.corr[bh * np + q];
+    for (int kb = 0; kb < 2; ++kb) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+            uint32_t pk4 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float zz = z[kb][4 * d4 + j];
+                float v = __builtin_amdgcn_exp2f(SMOOTHQ ? zz + off : __builtin_fmaf(zz, sc, off));
+                if (MASK && !(zz > -__builtin_inff())) v = 0.0f;
+                pk4 = __builtin_amdgcn_cvt_pk_u8_f32(v, j, pk4);
             }
+            w4[d4] = pk4;
+            csum = __builtin_amdgcn_udot4(pk4, 0x01010101u, csum, false);
+        }
+        pc[kb] = v4i{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+    }
+    // online update with a lazily raised reference max
+    if (row_live && mt > M + RESCALE_THRESHOLD) {
+        const float alpha = M > -__builtin_inff() ? __builtin_amdgcn_exp2f(M - mt) : 0.0f;
+        M = mt;
+        L *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+    const float e = row_live ? __builtin_amdgcn_exp2f(mt - M) : 0.0f;
+    L = __builtin_fmaf(e, (float)csum, L);
+    const float wv = e * sv;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        v16i pvacc = mfma_i8(sm.v[buf][(db * 2 + 0) * 64 + lane], pc[0], v16i{});
+        pvacc = mfma_i8(sm.v[buf][(db * 2 + 1) * 64 + lane], pc[1], pvacc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] = __builtin_fmaf((float)pvacc[r], wv, O[db][r]);
+    }
+}
+
+template <bool CAUSAL, bool SMOOTHQ>
+__global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
+    __shared__ FwdSmem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group(a.ngroups, a.BH, bh, g);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
+    const bool live = qblk < T;
+    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;
+    const int t_last = CAUSAL ? qblk : T - 1;
+    const bool ragged = (a.N & (BLK - 1)) != 0;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
+    const v4i* kg = (const v4i*)(a.k_r + bt * 4096);
+    const v4i* vg = (const v4i*)(a.v_t + bt * 4096);
+    const float* bg = a.bias + bh * np;
+
+    v4i qop[2] = {v4i{}, v4i{}};
+    float sQ = 0.0f;
+    if (live) {
+        const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
+        qop[0] = src[(qhalf * 2 + 0) * 64 + lane];
+        qop[1] = src[(qhalf * 2 + 1) * 64 + lane];
+        sQ = a.sq[bt + qblk];
+    }
+    const int q = qblk * BLK + 32 * qhalf + l32;
+
+    // prologue: tile 0 into buffer 0
+    v4i pk = kg[tid], pv = vg[tid];
+    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
+    sm.k[0][tid] = pk;
+    sm.v[0][tid] = pv;
+    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
+    __syncthreads();
+
+    float M = -__builtin_inff();   // reference max (log2), raised lazily
+    float L = 0.0f;                // sum over tiles of exp2(m_t - M) * (code sum of this half-wave)
+    v16f O[2] = {v16f{}, v16f{}};  // [db]: lane = query, registers = channels
+
+    for (int t = 0; t <= t_last_wg; ++t) {
+        const int buf = t & 1;
+        const bool more = t < t_last_wg;
+        if (more) {
+            pk = kg[(size_t)(t + 1) * 256 + tid];
+            pv = vg[(size_t)(t + 1) * 256 + tid];
+            if (SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
+        }
+        if (live && t <= t_last) {
+            const float sc = tile_scale(sQ, a.sk[bt + t]);
+            const float sv = a.sv[bt + t];
+            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+                fwd_tile<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O);
+            else
+                fwd_tile<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O);
+        }
+        if (more) {
+            sm.k[buf ^ 1][tid] = pk;
+            sm.v[buf ^ 1][tid] = pv;
+            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
+        }
+        __syncthreads();
+    }
+
+    // epilogue: O / L in bf16; LSE in natural log of the un-smoothed scores
+    if (live && q < a.N) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(L), __float_as_uint(L), false, false);
+        const float Lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float inv_l = 1.0f / Lt;
+        uint16_t* orow = a.o + ((size_t)bh * a.N + q) * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * h;
+                const uint32_t w0 = f32_to_bf16_rne(O[db][4 * r4 + 0] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 1] * inv_l) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(O[db][4 * r4 + 2] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 3] * inv_l) << 16);
+                *(uint2*)(orow + d) = make_uint2(w0, w1);
+            }
+        if (h == 0) {
+            const float lse2 = M + log2f(Lt) - LOG2_127;   // log2 of the row sum of exp2(score)
+            a.lse[(size_t)bh * a.N + q] = lse2 * LN2 + a.corr[bh * np + q];
         }
     }
 }
 
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
-    dim3 grid(a.ngroups, BH), block(256);
+    dim3 grid(a.ngroups * BH), block(64 * FWD_WAVES);
     if (causal) {
         if (smooth_q) hipLaunchKernelGGL((k_fwd<true, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_fwd<true, false>), grid, block, 0, st, a);
