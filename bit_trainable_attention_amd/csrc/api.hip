@@ -267,7 +267,8 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     a.dv = (uint16_t*)dV;
     a.N = p->N;
     a.T = (p->N + BLK - 1) / BLK;
-    a.ngroups = (a.T + 3) / 4;
+    a.ngroups = (a.T + 1) / 2;
+    a.BH = p->B * p->H;
     if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, st);
     else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();

@@ -20,7 +20,7 @@ struct BwdArgs {
     const _Float16 *do16, *v16;        // [BH][Np][64]
     const float* mu_q;                 // [BH][64]
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
-    int N, T, ngroups;
+    int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
 };
 
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);

@@ -4,398 +4,457 @@
 //
 // SageBwd (abstract): five of the six INT8 matmuls are in the backward, and
 // the score gradient dS is where quantization error mainly arises; the
-// SageAttention3 summary ("Approach", ablation table, "Surprising findings")
-// keeps dO V^T in FP16 because quantizing it hurts dQ.  The gradient formulas
-// are FlashAttention-2's (under "Builds on").
+// SageAttention3 summary ("Approach", the ablation table, "Surprising
+// findings") keeps dO V^T in FP16 because quantizing it hurts dQ.  The
+// gradient formulas are FlashAttention-2's (under "Builds on").
 //
-// Two kernels, no atomics:
-//   k_bwd_dkdv  one wave per key block, loops over query blocks; computes S
-//               (lane = key), so P and dS codes leave the accumulator as the
-//               A operand of P^T dO and dS^T Q (contraction over queries).
-//   k_bwd_dq    one wave per query block, loops over key blocks; computes
-//               S^T (lane = query), so dS^T codes feed K^T dS^T directly.
-// Both evaluate P and dS with the same float32 operations on bit-identical
-// operands (the FP16 MFMA gives the same bits for dO V^T and V dO^T), so the
-// dS tile, its scale and its codes are identical in the two kernels.
+// Two kernels, no atomics, bitwise repeatable:
+//   k_bwd_dkdv  a workgroup of 4 waves owns two 64-key blocks (each wave 32
+//               keys) and walks the query blocks.  It computes S (lane = key),
+//               so P and dS codes leave the accumulator as the A operand of
+//               P^T dO and dS^T Q (contraction over queries).
+//   k_bwd_dq    a workgroup of 4 waves owns two 64-query blocks (each wave 32
+//               queries) and walks the key blocks.  It computes S^T (lane =
+//               query), so dS^T codes feed K^T dS^T directly.
+// A 64x64 quantization tile of P or dS is held by a pair of waves, which
+// exchange their partial maxima through LDS.  Both kernels evaluate P and dS
+// with the same float32 operations on bit-identical operands (the FP16 MFMA
+// gives the same bits for dO V^T and V dO^T), so each dS tile, its scale and
+// its codes are identical in the two kernels.  The streamed operand tiles go
+// through double-buffered LDS, fetched one step ahead; FP16 rows are stored
+// with their 16-byte chunks XOR-swizzled by row so column reads do not
+// collide on LDS banks.
 #include "attn.h"
 
 namespace sagebwd {
 
-__device__ __forceinline__ int dot4_sum(int packed) {
-    return __builtin_amdgcn_sdot4(packed, 0x01010101, 0, false);
+constexpr int BWD_WAVES = 4;
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Maximum over the 64 lanes of a wave, returned in every lane.
+__device__ __forceinline__ float wave_max64(float v) {
+    v = __builtin_fmaxf(v, dppf<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = __builtin_fmaxf(v, dppf<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = __builtin_fmaxf(v, dppf<0x141>(v));   // row_half_mirror
+    v = __builtin_fmaxf(v, dppf<0x140>(v));   // row_mirror
+    v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __builtin_fmaxf(v, __builtin_fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1])));
+}
+
+// Four signed codes rne(x * inv) packed into one dword.
+__device__ __forceinline__ int pack_codes(float x0, float x1, float x2, float x3, float inv) {
+    return (int)pack4(code_bits(x0, inv), code_bits(x1, inv), code_bits(x2, inv), code_bits(x3, inv));
+}
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+// Workgroup -> (head, group) as in the forward: the groups of a head share an
+// XCD when the head count allows.  first_small selects the order of groups
+// within a head (smallest index first for the key-block kernel, whose causal
+// work is largest at small key blocks).
+__device__ __forceinline__ void map_group_bwd(int ngroups, int BH, bool first_small, int& bh, int& g) {
+    const int L = blockIdx.x;
+    int s_in_head;
+    if ((BH & 7) == 0) {
+        const int xcd = L & 7, s = L >> 3;
+        bh = (s / ngroups) * 8 + xcd;
+        s_in_head = s % ngroups;
+    } else {
+        bh = L / ngroups;
+        s_in_head = L % ngroups;
+    }
+    g = first_small ? s_in_head : ngroups - 1 - s_in_head;
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+struct DkdvSmem {
+    v4i q_r[2][256];     // Q row-operand codes (A operand of Q K^T)
+    v4i q_t[2][256];     // Q transposed codes (B operand of dS^T Q)
+    v4i do_t[2][256];    // dO transposed codes (B operand of P^T dO)
+    v8h do16[2][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
+    float lse2[2][64];
+    float delta[2][64];
+    float red[2][4];     // partial tile maxima of P [0] and dS [1], per wave
+};
+
 template <bool CAUSAL, bool SMOOTHQ>
-__global__ __launch_bounds__(256) void k_bwd_dkdv(BwdArgs a) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32, l32 = lane % 32;
-    const int bh = blockIdx.y;
-    const int t = blockIdx.x * 4 + wave;                     // key block (longest causal first)
-    if (t >= a.T) return;
-    const size_t bt = (size_t)bh * a.T;
-    const size_t np = (size_t)a.T * BLK;
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
+    __shared__ DkdvSmem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group_bwd(a.ngroups, a.BH, true, bh, g);
+    const int T = a.T;
+    const int kvb = 2 * g + wave / 2, kh = wave % 2;
+    const bool live = kvb < T;
+    const int key = kvb * BLK + 32 * kh + l32;                // this lane's key (S layout)
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
 
-    v4i kop[2][2];                                           // B operand of Q K^T: lane = key
-    {
-        const v4i* src = (const v4i*)(a.k_r + (bt + t) * 4096);
+    // persistent operands of this wave's 32 keys
+    v4i kop[2] = {v4i{}, v4i{}};
+    v8h vh[4];
+    float kbias = 0.0f, sK = 0.0f;
+    if (live) {
+        const v4i* src = (const v4i*)(a.k_r + (bt + kvb) * 4096);
+        kop[0] = src[(kh * 2 + 0) * 64 + lane];
+        kop[1] = src[(kh * 2 + 1) * 64 + lane];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < 4; ++ks) vh[ks] = *(const v8h*)(a.v16 + (rowbase + key) * HD + 16 * ks + 8 * h);
+        if (SMOOTHQ) kbias = a.bias[rowbase + key];
+        sK = a.sk[bt + kvb];
+    } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) kop[kb][ks] = src[(kb * 2 + ks) * 64 + lane];
+        for (int ks = 0; ks < 4; ++ks) vh[ks] = v8h{};
     }
-    v8h vh[2][4];                                            // B operand of dO V^T: lane = key
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            vh[kb][ks] = *(const v8h*)(a.v16 + (rowbase + t * BLK + 32 * kb + l32) * HD + 16 * ks + 8 * h);
-    float kbias[2] = {0.0f, 0.0f};
-    if (SMOOTHQ) {
-        kbias[0] = a.bias[rowbase + t * BLK + l32];
-        kbias[1] = a.bias[rowbase + t * BLK + 32 + l32];
-    }
-    const float sK = a.sk[bt + t];
 
-    v16f dk[2][2], dv[2][2];                                 // [kb][db]: lane = channel, regs = keys
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            dk[kb][db] = v16f{};
-            dv[kb][db] = v16f{};
-        }
-    float gsum[2] = {0.0f, 0.0f};                            // sum_i s_dS colsum(dS codes), per half
-
-    const bool ragged_keys = (t == a.T - 1) && (a.N % BLK) != 0;
-    for (int i = CAUSAL ? t : 0; i < a.T; ++i) {
-        v4i qop[2][2];                                       // A operand: lane = query
+    const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
+    // staging of query block i into buffer b
+    const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
+    const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
+    const v4i* dtg = (const v4i*)(a.do_t + bt * 4096);
+    v4i s_qr, s_qt, s_dt, s_h0, s_h1;
+    float4 s_rv;
+    auto fetch = [&](int i) {
+        s_qr = qrg[(size_t)i * 256 + tid];
+        s_qt = qtg[(size_t)i * 256 + tid];
+        s_dt = dtg[(size_t)i * 256 + tid];
+        const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
+        s_h0 = hs[tid];
+        s_h1 = hs[tid + 256];
+        if (tid < 16) s_rv = ((const float4*)(a.lse2 + rowbase + i * BLK))[tid];
+        else if (tid < 32) s_rv = ((const float4*)(a.delta + rowbase + i * BLK))[tid - 16];
+    };
+    auto stage = [&](int b) {
+        sm.q_r[b][tid] = s_qr;
+        sm.q_t[b][tid] = s_qt;
+        sm.do_t[b][tid] = s_dt;
         {
-            const v4i* src = (const v4i*)(a.q_r + (bt + i) * 4096);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) qop[qb][ks] = src[(qb * 2 + ks) * 64 + lane];
+            const int c0 = tid, c1 = tid + 256;
+            ((v4i*)sm.do16[b])[swz(c0 / 8, c0 % 8)] = s_h0;
+            ((v4i*)sm.do16[b])[swz(c1 / 8, c1 % 8)] = s_h1;
         }
+        if (tid < 16) ((float4*)sm.lse2[b])[tid] = s_rv;
+        else if (tid < 32) ((float4*)sm.delta[b])[tid - 16] = s_rv;
+    };
+
+    v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
+    float gsum = 0.0f;                                          // sum_i s_dS colsum(dS codes), this half
+
+    fetch(i0);
+    stage(0);
+    __syncthreads();
+    const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
+    for (int i = i0; i < T; ++i) {
+        const int buf = (i - i0) & 1;
+        const bool more = i + 1 < T;
+        if (more) fetch(i + 1);
+        const bool active = live && (!CAUSAL || i >= kvb);
+        const bool masked = (CAUSAL && i == kvb) || ragged_keys;
+        float p[2][16];                      // [qb]: lane = key, regs = queries
         const float sQ = a.sq[bt + i];
         const float sc = tile_scale(sQ, sK);
-        v16i s[2][2];                                        // [qb][kb]: lane = key, regs = queries
+        if (active) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < 2; ++qb) {
+                v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
+                s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[qb][kb] = mfma_i8(qop[qb][0], kop[kb][0], v16i{});
-                s[qb][kb] = mfma_i8(qop[qb][1], kop[kb][1], s[qb][kb]);
-            }
-        float p[2][2][16];
-        float pmax = 0.0f;
-        const bool diag = CAUSAL && i == t;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 l4 = *(const float4*)(a.lse2 + rowbase + i * BLK + 32 * qb + 8 * r4 + 4 * h);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 4 * r4 + j;
-                        float pv = bwd_prob<SMOOTHQ>(s[qb][kb][r], sc, kbias[kb], lv[j]);
-                        if (diag || ragged_keys) {
-                            const int key = t * BLK + 32 * kb + l32;
+                        float pv = bwd_prob<SMOOTHQ>(s[r], sc, kbias, lv[j]);
+                        if (masked) {
                             const int q = i * BLK + 32 * qb + 8 * r4 + 4 * h + j;
                             if (key >= a.N || (CAUSAL && key > q)) pv = 0.0f;
                         }
-                        p[qb][kb][r] = pv;
-                        pmax = fmaxf(pmax, pv);
+                        p[qb][r] = pv;
                     }
-            }
-        pmax = wave_max(pmax);
-        float sP, invP;
-        block_scale(pmax, sP, invP);
-
-        // dV += s_P s_dO (P codes^T dO codes)
-        {
-            v4i pc[2][2];                                    // [kb][qs]: A operand, k = queries
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int d4 = 0; d4 < 4; ++d4)
-                        w[d4] = pack4(code_bits(p[qs][kb][4 * d4 + 0], invP), code_bits(p[qs][kb][4 * d4 + 1], invP),
-                                      code_bits(p[qs][kb][4 * d4 + 2], invP), code_bits(p[qs][kb][4 * d4 + 3], invP));
-                    pc[kb][qs] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
                 }
-            const v4i* dsrc = (const v4i*)(a.do_t + (bt + i) * 4096);
+            }
+            float pm = 0.0f;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(p[qb][r], p[qb][r + 1]));
+            pm = wave_max64(pm);
+            if (lane == 0) sm.red[0][wave] = pm;
+        }
+        __syncthreads();
+        float dsm = 0.0f;
+        if (active) {
+            float sP, invP;
+            block_scale(__builtin_fmaxf(sm.red[0][wave], sm.red[0][wave ^ 1]), sP, invP);
+            // dV += s_P s_dO (P codes^T dO codes)
+            v4i pc[2];
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+                pc[qs] = v4i{pack_codes(p[qs][0], p[qs][1], p[qs][2], p[qs][3], invP),
+                             pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invP),
+                             pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invP),
+                             pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invP)};
             const float wv = sP * a.sdo[bt + i];
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const v4i d0 = dsrc[(db * 2 + 0) * 64 + lane], d1 = dsrc[(db * 2 + 1) * 64 + lane];
+                v16i acc = mfma_i8(pc[0], sm.do_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
+                acc = mfma_i8(pc[1], sm.do_t[buf][(db * 2 + 1) * 64 + lane], acc);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    v16i acc = mfma_i8(pc[kb][0], d0, v16i{});
-                    acc = mfma_i8(pc[kb][1], d1, acc);
+                for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
+            }
+            // dP = dO V^T (FP16), dS = P * (dP - Delta) in place of P
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) dv[kb][db][r] = __builtin_fmaf((float)acc[r], wv, dv[kb][db][r]);
+            for (int qb = 0; qb < 2; ++qb) {
+                const int row = 32 * qb + l32;
+                v16f dp = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], v16f{});
+                dp = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dp);
+                dp = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dp);
+                dp = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dp);
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 d4 = *(const float4*)&sm.delta[buf][32 * qb + 8 * r4 + 4 * h];
+                    const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * r4 + j;
+                        p[qb][r] = p[qb][r] * (dp[r] - dl[j]);
+                    }
                 }
             }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2)
+                    dsm = __builtin_fmaxf(dsm, __builtin_fmaxf(__builtin_fabsf(p[qb][r]), __builtin_fabsf(p[qb][r + 1])));
+            dsm = wave_max64(dsm);
+            if (lane == 0) sm.red[1][wave] = dsm;
         }
-
-        // dP = dO V^T (FP16), dS = P * (dP - Delta), in place of P
-        float dsmax = 0.0f;
+        __syncthreads();
+        if (active) {
+            float sdS, invdS;
+            block_scale(__builtin_fmaxf(sm.red[1][wave], sm.red[1][wave ^ 1]), sdS, invdS);
+            v4i dc[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            v8h doh[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                doh[ks] = *(const v8h*)(a.do16 + (rowbase + i * BLK + 32 * qb + l32) * HD + 16 * ks + 8 * h);
-            float dl[16];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 d4 = *(const float4*)(a.delta + rowbase + i * BLK + 32 * qb + 8 * r4 + 4 * h);
-                dl[4 * r4 + 0] = d4.x;
-                dl[4 * r4 + 1] = d4.y;
-                dl[4 * r4 + 2] = d4.z;
-                dl[4 * r4 + 3] = d4.w;
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                v16f dp = mfma_f16(doh[0], vh[kb][0], v16f{});
-                dp = mfma_f16(doh[1], vh[kb][1], dp);
-                dp = mfma_f16(doh[2], vh[kb][2], dp);
-                dp = mfma_f16(doh[3], vh[kb][3], dp);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float ds = p[qb][kb][r] * (dp[r] - dl[r]);
-                    p[qb][kb][r] = ds;
-                    dsmax = fmaxf(dsmax, fabsf(ds));
-                }
-            }
-        }
-        dsmax = wave_max(dsmax);
-        float sdS, invdS;
-        block_scale(dsmax, sdS, invdS);
-
-        // dK += s_dS s_Q (dS codes^T Q codes) [+ colsum term for Q-smoothing]
-        {
-            v4i dc[2][2];                                    // [kb][qs]
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int d4 = 0; d4 < 4; ++d4)
-                        w[d4] = pack4(code_bits(p[qs][kb][4 * d4 + 0], invdS), code_bits(p[qs][kb][4 * d4 + 1], invdS),
-                                      code_bits(p[qs][kb][4 * d4 + 2], invdS), code_bits(p[qs][kb][4 * d4 + 3], invdS));
-                    dc[kb][qs] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-                }
+            for (int qs = 0; qs < 2; ++qs)
+                dc[qs] = v4i{pack_codes(p[qs][0], p[qs][1], p[qs][2], p[qs][3], invdS),
+                             pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invdS),
+                             pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invdS),
+                             pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invdS)};
             if (SMOOTHQ) {
+                int cs = 0;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    int cs = 0;
+                for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-                    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-                        for (int d4 = 0; d4 < 4; ++d4) cs += dot4_sum(dc[kb][qs][d4]);
-                    gsum[kb] = __builtin_fmaf((float)cs, sdS, gsum[kb]);
-                }
+                    for (int d4 = 0; d4 < 4; ++d4) cs = __builtin_amdgcn_sdot4(dc[qs][d4], 0x01010101, cs, false);
+                gsum = __builtin_fmaf((float)cs, sdS, gsum);
             }
-            const v4i* qsrc = (const v4i*)(a.q_t + (bt + i) * 4096);
             const float wk = sdS * sQ;
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const v4i q0 = qsrc[(db * 2 + 0) * 64 + lane], q1 = qsrc[(db * 2 + 1) * 64 + lane];
+                v16i acc = mfma_i8(dc[0], sm.q_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
+                acc = mfma_i8(dc[1], sm.q_t[buf][(db * 2 + 1) * 64 + lane], acc);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    v16i acc = mfma_i8(dc[kb][0], q0, v16i{});
-                    acc = mfma_i8(dc[kb][1], q1, acc);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dk[kb][db][r] = __builtin_fmaf((float)acc[r], wk, dk[kb][db][r]);
-                }
+                for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
         }
+        if (more) stage(buf ^ 1);
+        __syncthreads();
     }
 
-    // epilogue: dK (x 1/8, plus g_j mu_q) and dV in bf16; lane = channel, regs = keys
-    float gfull[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) gfull[kb] = gsum[kb] + half_swap(gsum[kb]);
+    // epilogue: dK (x 1/8, plus colsum(dS) mu_q for Q-smoothing) and dV in bf16;
+    // lane = channel, registers = keys of this wave's half block
+    if (!live) return;
+    float gfull = 0.0f;
+    if (SMOOTHQ) {
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(gsum), __float_as_uint(gsum), false, false);
+        gfull = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
         const int d = 32 * db + l32;
         const float muq = SMOOTHQ ? a.mu_q[(size_t)bh * HD + d] : 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kr = 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-                const int key = t * BLK + kr;
-                float gk = 0.0f;
-                if (SMOOTHQ) gk = __shfl(gfull[kb], 8 * (r / 4) + 4 * h + (r % 4), 64);
-                if (key < a.N) {
-                    const float dkv = (SMOOTHQ ? __builtin_fmaf(gk, muq, dk[kb][db][r]) : dk[kb][db][r]) * 0.125f;
-                    a.dk[((size_t)bh * a.N + key) * HD + d] = (uint16_t)f32_to_bf16_rne(dkv);
-                    a.dv[((size_t)bh * a.N + key) * HD + d] = (uint16_t)f32_to_bf16_rne(dv[kb][db][r]);
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int kr = 8 * (r / 4) + 4 * h + (r % 4);
+            const int kk = kvb * BLK + 32 * kh + kr;
+            const float gk = SMOOTHQ ? __shfl(gfull, kr, 64) : 0.0f;
+            if (kk < a.N) {
+                const float dkv = (SMOOTHQ ? __builtin_fmaf(gk, muq, dk[db][r]) : dk[db][r]) * 0.125f;
+                a.dk[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dkv);
+                a.dv[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dv[db][r]);
             }
+        }
     }
 }
 
+// ------------------------------------------------------------------ dQ
+
+struct DqSmem {
+    v4i k_r[2][256];     // K row-operand codes (A operand of K Q^T)
+    v4i k_t[2][256];     // K transposed codes (A operand of K^T dS^T)
+    v8h v16[2][512];     // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
+    float bias[2][64];   // Q-smoothing key bias (log2 domain)
+    float red[4];        // partial dS tile maxima, per wave
+};
+
 template <bool CAUSAL, bool SMOOTHQ>
-__global__ __launch_bounds__(256) void k_bwd_dq(BwdArgs a) {
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64, h = lane / 32, l32 = lane % 32;
-    const int bh = blockIdx.y;
-    const int iq = (a.ngroups - 1 - blockIdx.x) * 4 + wave;   // longest causal rows first
-    if (iq >= a.T) return;
-    const size_t bt = (size_t)bh * a.T;
-    const size_t np = (size_t)a.T * BLK;
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
+    __shared__ DqSmem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group_bwd(a.ngroups, a.BH, false, bh, g);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qh = wave % 2;
+    const bool live = qblk < T;
+    const int q = qblk * BLK + 32 * qh + l32;                 // this lane's query (S^T layout)
+    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
 
-    v4i qop[2][2];                                            // B operand of K Q^T: lane = query
-    {
-        const v4i* src = (const v4i*)(a.q_r + (bt + iq) * 4096);
+    v4i qop[2] = {v4i{}, v4i{}};
+    v8h doh[4];
+    float lq = 0.0f, dlq = 0.0f, sQ = 0.0f;
+    if (live) {
+        const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
+        qop[0] = src[(qh * 2 + 0) * 64 + lane];
+        qop[1] = src[(qh * 2 + 1) * 64 + lane];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int ks = 0; ks < 4; ++ks) doh[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+        lq = a.lse2[rowbase + q];
+        dlq = a.delta[rowbase + q];
+        sQ = a.sq[bt + qblk];
+    } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) qop[qb][ks] = src[(qb * 2 + ks) * 64 + lane];
+        for (int ks = 0; ks < 4; ++ks) doh[ks] = v8h{};
     }
-    v8h doh[2][4];                                            // B operand of V dO^T: lane = query
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            doh[qb][ks] = *(const v8h*)(a.do16 + (rowbase + iq * BLK + 32 * qb + l32) * HD + 16 * ks + 8 * h);
-    float lq[2], dlq[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        lq[qb] = a.lse2[rowbase + iq * BLK + 32 * qb + l32];
-        dlq[qb] = a.delta[rowbase + iq * BLK + 32 * qb + l32];
-    }
-    const float sQ = a.sq[bt + iq];
 
-    v16f dq[2][2];                                            // [db][qb]: lane = query, regs = channels
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dq[db][qb] = v16f{};
+    const v4i* krg = (const v4i*)(a.k_r + bt * 4096);
+    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
+    v4i s_kr, s_kt, s_v0, s_v1;
+    float4 s_b;
+    auto fetch = [&](int t) {
+        s_kr = krg[(size_t)t * 256 + tid];
+        s_kt = ktg[(size_t)t * 256 + tid];
+        const v4i* vs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
+        s_v0 = vs[tid];
+        s_v1 = vs[tid + 256];
+        if (SMOOTHQ && tid < 16) s_b = ((const float4*)(a.bias + rowbase + t * BLK))[tid];
+    };
+    auto stage = [&](int b) {
+        sm.k_r[b][tid] = s_kr;
+        sm.k_t[b][tid] = s_kt;
+        const int c0 = tid, c1 = tid + 256;
+        ((v4i*)sm.v16[b])[swz(c0 / 8, c0 % 8)] = s_v0;
+        ((v4i*)sm.v16[b])[swz(c1 / 8, c1 % 8)] = s_v1;
+        if (SMOOTHQ && tid < 16) ((float4*)sm.bias[b])[tid] = s_b;
+    };
 
-    const int t_end = CAUSAL ? iq : a.T - 1;
-    for (int t = 0; t <= t_end; ++t) {
-        v4i kop[2][2];                                        // A operand: lane = key
-        {
-            const v4i* src = (const v4i*)(a.k_r + (bt + t) * 4096);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) kop[kb][ks] = src[(kb * 2 + ks) * 64 + lane];
-        }
+    v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    const bool ragged = (a.N & (BLK - 1)) != 0;
+    for (int t = 0; t <= t_last_wg; ++t) {
+        const int buf = t & 1;
+        const bool more = t < t_last_wg;
+        if (more) fetch(t + 1);
+        const bool active = live && (!CAUSAL || t <= qblk);
+        const bool masked = (CAUSAL && t == qblk) || (ragged && t == T - 1);
         const float sK = a.sk[bt + t];
-        const float sc = tile_scale(sQ, sK);
-        v16i s[2][2];                                         // [kb][qb]: lane = query, regs = keys
+        float ds[2][16];             // [kb]: lane = query, regs = keys
+        if (active) {
+            const float sc = tile_scale(sQ, sK);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
+                v16i s = mfma_i8(sm.k_r[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
+                s = mfma_i8(sm.k_r[buf][(kb * 2 + 1) * 64 + lane], qop[1], s);
+                const int row = 32 * kb + l32;
+                v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], v16f{});
+                dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
+                dp = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dp);
+                dp = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dp);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[kb][qb] = mfma_i8(kop[kb][0], qop[qb][0], v16i{});
-                s[kb][qb] = mfma_i8(kop[kb][1], qop[qb][1], s[kb][qb]);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (SMOOTHQ) {
+                        const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                        bv[0] = b4.x;
+                        bv[1] = b4.y;
+                        bv[2] = b4.z;
+                        bv[3] = b4.w;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * r4 + j;
+                        float pv = bwd_prob<SMOOTHQ>(s[r], sc, bv[j], lq);
+                        if (masked) {
+                            const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
+                            if (key >= a.N || (CAUSAL && key > q)) pv = 0.0f;
+                        }
+                        ds[kb][r] = pv * (dp[r] - dlq);
+                    }
+                }
             }
-        float bias[2][16];
-        if (SMOOTHQ) {
+            float dsm = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 b4 = *(const float4*)(a.bias + rowbase + t * BLK + 32 * kb + 8 * r4 + 4 * h);
-                    bias[kb][4 * r4 + 0] = b4.x;
-                    bias[kb][4 * r4 + 1] = b4.y;
-                    bias[kb][4 * r4 + 2] = b4.z;
-                    bias[kb][4 * r4 + 3] = b4.w;
-                }
+                for (int r = 0; r < 16; r += 2)
+                    dsm = __builtin_fmaxf(dsm, __builtin_fmaxf(__builtin_fabsf(ds[kb][r]), __builtin_fabsf(ds[kb][r + 1])));
+            dsm = wave_max64(dsm);
+            if (lane == 0) sm.red[wave] = dsm;
         }
-        const bool need_mask = (CAUSAL && t == iq) || (t == a.T - 1 && (a.N % BLK) != 0);
-        float ds[2][2][16];                                   // [kb][qb]
-        float dsmax = 0.0f;
+        __syncthreads();
+        if (active) {
+            float sdS, invdS;
+            block_scale(__builtin_fmaxf(sm.red[wave], sm.red[wave ^ 1]), sdS, invdS);
+            v4i dc[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            v8h vh[4];
+            for (int ks = 0; ks < 2; ++ks)
+                dc[ks] = v4i{pack_codes(ds[ks][0], ds[ks][1], ds[ks][2], ds[ks][3], invdS),
+                             pack_codes(ds[ks][4], ds[ks][5], ds[ks][6], ds[ks][7], invdS),
+                             pack_codes(ds[ks][8], ds[ks][9], ds[ks][10], ds[ks][11], invdS),
+                             pack_codes(ds[ks][12], ds[ks][13], ds[ks][14], ds[ks][15], invdS)};
+            const float wq = sdS * sK;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                vh[ks] = *(const v8h*)(a.v16 + (rowbase + t * BLK + 32 * kb + l32) * HD + 16 * ks + 8 * h);
+            for (int db = 0; db < 2; ++db) {
+                v16i acc = mfma_i8(sm.k_t[buf][(db * 2 + 0) * 64 + lane], dc[0], v16i{});
+                acc = mfma_i8(sm.k_t[buf][(db * 2 + 1) * 64 + lane], dc[1], acc);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                v16f dp = mfma_f16(vh[0], doh[qb][0], v16f{});
-                dp = mfma_f16(vh[1], doh[qb][1], dp);
-                dp = mfma_f16(vh[2], doh[qb][2], dp);
-                dp = mfma_f16(vh[3], doh[qb][3], dp);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pv = bwd_prob<SMOOTHQ>(s[kb][qb][r], sc, SMOOTHQ ? bias[kb][r] : 0.0f, lq[qb]);
-                    if (need_mask) {
-                        const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
-                        const int q = iq * BLK + 32 * qb + l32;
-                        if (key >= a.N || (CAUSAL && key > q)) pv = 0.0f;
-                    }
-                    const float d = pv * (dp[r] - dlq[qb]);
-                    ds[kb][qb][r] = d;
-                    dsmax = fmaxf(dsmax, fabsf(d));
-                }
+                for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
             }
         }
-        dsmax = wave_max(dsmax);
-        float sdS, invdS;
-        block_scale(dsmax, sdS, invdS);
-        v4i dc[2][2];                                         // [qb][ks]: B operand, k = keys
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                uint32_t w[4];
-#pragma unroll
-                for (int d4 = 0; d4 < 4; ++d4)
-                    w[d4] = pack4(code_bits(ds[ks][qb][4 * d4 + 0], invdS), code_bits(ds[ks][qb][4 * d4 + 1], invdS),
-                                  code_bits(ds[ks][qb][4 * d4 + 2], invdS), code_bits(ds[ks][qb][4 * d4 + 3], invdS));
-                dc[qb][ks] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-            }
-        const v4i* ksrc = (const v4i*)(a.k_t + (bt + t) * 4096);
-        const float wq = sdS * sK;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            const v4i k0 = ksrc[(db * 2 + 0) * 64 + lane], k1 = ksrc[(db * 2 + 1) * 64 + lane];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                v16i acc = mfma_i8(k0, dc[qb][0], v16i{});
-                acc = mfma_i8(k1, dc[qb][1], acc);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dq[db][qb][r] = __builtin_fmaf((float)acc[r], wq, dq[db][qb][r]);
-            }
-        }
+        if (more) stage(buf ^ 1);
+        __syncthreads();
     }
 
+    if (live && q < a.N) {
+        uint16_t* row = a.dq + ((size_t)bh * a.N + q) * HD;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int q = iq * BLK + 32 * qb + l32;
-        if (q < a.N) {
-            uint16_t* row = a.dq + ((size_t)bh * a.N + q) * HD;
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * db + 8 * r4 + 4 * h;
-                    const uint32_t w0 = f32_to_bf16_rne(dq[db][qb][4 * r4 + 0] * 0.125f) |
-                                        (f32_to_bf16_rne(dq[db][qb][4 * r4 + 1] * 0.125f) << 16);
-                    const uint32_t w1 = f32_to_bf16_rne(dq[db][qb][4 * r4 + 2] * 0.125f) |
-                                        (f32_to_bf16_rne(dq[db][qb][4 * r4 + 3] * 0.125f) << 16);
-                    *(uint2*)(row + d) = make_uint2(w0, w1);
-                }
-        }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * h;
+                const uint32_t w0 = f32_to_bf16_rne(dq[db][4 * r4 + 0] * 0.125f) |
+                                    (f32_to_bf16_rne(dq[db][4 * r4 + 1] * 0.125f) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(dq[db][4 * r4 + 2] * 0.125f) |
+                                    (f32_to_bf16_rne(dq[db][4 * r4 + 3] * 0.125f) << 16);
+                *(uint2*)(row + d) = make_uint2(w0, w1);
+            }
     }
 }
 
 int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
-    dim3 grid(a.ngroups, BH), block(256);
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
     if (causal) {
         if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv<true, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_bwd_dkdv<true, false>), grid, block, 0, st, a);
@@ -407,7 +466,7 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStr
 }
 
 int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
-    dim3 grid(a.ngroups, BH), block(256);
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
     if (causal) {
         if (smooth_q) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);
