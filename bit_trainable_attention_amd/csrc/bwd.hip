@@ -83,6 +83,34 @@ struct DkdvSmem {
     float red[2][4];     // partial tile maxima of P [0] and dS [1], per wave
 };
 
+// P for one 64-query x 32-key half tile in the S layout (lane = key,
+// registers = queries).  MASK only on the causal diagonal tile and the ragged
+// last key block, so the common path carries no per-element selects.
+template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+__device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float kbias,
+                                           int i, int key, int N, int lane, int h, float (&p)[2][16]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
+        s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * r4 + j;
+                float pv = bwd_prob<SMOOTHQ>(s[r], sc, kbias, lv[j]);
+                if (MASK) {
+                    const int q = i * BLK + 32 * qb + 8 * r4 + 4 * h + j;
+                    if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
+                }
+                p[qb][r] = pv;
+            }
+        }
+    }
+}
+
 template <bool CAUSAL, bool SMOOTHQ>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     __shared__ DkdvSmem sm;
@@ -161,26 +189,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         const float sQ = a.sq[bt + i];
         const float sc = tile_scale(sQ, sK);
         if (active) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
-                s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * r4 + j;
-                        float pv = bwd_prob<SMOOTHQ>(s[r], sc, kbias, lv[j]);
-                        if (masked) {
-                            const int q = i * BLK + 32 * qb + 8 * r4 + 4 * h + j;
-                            if (key >= a.N || (CAUSAL && key > q)) pv = 0.0f;
-                        }
-                        p[qb][r] = pv;
-                    }
-                }
-            }
+            if (masked) dkdv_probs<CAUSAL, SMOOTHQ, true>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p);
+            else dkdv_probs<CAUSAL, SMOOTHQ, false>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p);
             float pm = 0.0f;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -305,6 +315,46 @@ struct DqSmem {
     float red[4];        // partial dS tile maxima, per wave
 };
 
+// dS for one 32-query x 64-key half tile in the S^T layout (lane = query,
+// registers = keys); same float32 operations as the key-block kernel.
+template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+__device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i (&qop)[2], const v8h (&doh)[4],
+                                           float sc, float lq, float dlq, int t, int q, int N, int lane, int h,
+                                           float (&ds)[2][16]) {
+    const int l32 = lane % 32;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        v16i s = mfma_i8(sm.k_r[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
+        s = mfma_i8(sm.k_r[buf][(kb * 2 + 1) * 64 + lane], qop[1], s);
+        const int row = 32 * kb + l32;
+        v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], v16f{});
+        dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
+        dp = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dp);
+        dp = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dp);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (SMOOTHQ) {
+                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                bv[0] = b4.x;
+                bv[1] = b4.y;
+                bv[2] = b4.z;
+                bv[3] = b4.w;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * r4 + j;
+                float pv = bwd_prob<SMOOTHQ>(s[r], sc, bv[j], lq);
+                if (MASK) {
+                    const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
+                    if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
+                }
+                ds[kb][r] = pv * (dp[r] - dlq);
+            }
+        }
+    }
+}
+
 template <bool CAUSAL, bool SMOOTHQ>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     __shared__ DqSmem sm;
@@ -373,37 +423,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         float ds[2][16];             // [kb]: lane = query, regs = keys
         if (active) {
             const float sc = tile_scale(sQ, sK);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                v16i s = mfma_i8(sm.k_r[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
-                s = mfma_i8(sm.k_r[buf][(kb * 2 + 1) * 64 + lane], qop[1], s);
-                const int row = 32 * kb + l32;
-                v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], v16f{});
-                dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
-                dp = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dp);
-                dp = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dp);
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (SMOOTHQ) {
-                        const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
-                        bv[0] = b4.x;
-                        bv[1] = b4.y;
-                        bv[2] = b4.z;
-                        bv[3] = b4.w;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * r4 + j;
-                        float pv = bwd_prob<SMOOTHQ>(s[r], sc, bv[j], lq);
-                        if (masked) {
-                            const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
-                            if (key >= a.N || (CAUSAL && key > q)) pv = 0.0f;
-                        }
-                        ds[kb][r] = pv * (dp[r] - dlq);
-                    }
-                }
-            }
+            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds);
+            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds);
             float dsm = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
