@@ -50,7 +50,7 @@ def source_sha(stage: str) -> str:
 def load_traffic(stage: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"counters_{stage.lower()}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"counters_{stage.lower()}_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
