@@ -1,0 +1,82 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (the whole forward and backward over every head on the GPU).
+
+The oracle cannot afford every head of these workloads, so it is run on one
+sampled head per workload: its forward over all query rows of that head (the
+backward of a key block needs every row's O, LSE and Delta), then its
+backward for sampled query blocks (dQ) and key blocks (dK, dV): first, middle
+and last, which covers the causal diagonal and the ragged tail.  Each side
+feeds its own forward into its own backward (end to end)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_trainable_attention_amd as sb
+import workloads as W
+from oracle import exact, faithful as F, metrics as M
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny", None, (0, 1)),
+    ("pretrain", None, (7, 15)),
+    ("llama8k", None, (0, 17)),
+    ("llama16k", None, (0, 29)),
+    ("video", None, (1, 3)),
+    ("video", False, (0, 11)),          # the same layer with Q-smoothing off
+]
+
+
+def _blocks(T):
+    return sorted({0, T // 2, T - 1})
+
+
+@pytest.mark.parametrize("name,smooth_q,head", CASES,
+                         ids=[f"{c[0]}{'' if c[1] is None else '_q' + str(int(c[1]))}" for c in CASES])
+def test_fullsize_sampled_parity(name, smooth_q, head):
+    w = W.WORKLOADS[name]
+    sq = w.smooth_q if smooth_q is None else smooth_q
+    b, h = head
+    print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head}", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = sb.fwd(tq, tk, tv, w.causal, sq, w.smooth_k)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k)
+    torch.cuda.synchronize()
+    o_g = G.host_f32(o[b, h])
+    lse_g = lse[b, h].cpu().numpy()
+    dq_g, dk_g, dv_g = (G.host_f32(t[b, h]) for t in (dq, dk, dv))
+    for t in (o_g, lse_g, dq_g, dk_g, dv_g):
+        assert np.all(np.isfinite(t))
+    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv
+
+    f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
+    N, T = w.N, (w.N + 63) // 64
+    pp = F.prepare(f["q"], f["k"], f["v"], sq, w.smooth_k)
+    o_f, lse_f = F.fwd_head(pp, w.causal)
+    o_f, lse_f = o_f[:N], lse_f[:N]
+    blocks = _blocks(T)
+    rows = np.concatenate([np.arange(i * 64, min(N, i * 64 + 64)) for i in blocks])
+    assert M.rel_l2(o_g[rows], o_f[rows]) <= 1e-2, M.rel_l2(o_g[rows], o_f[rows])
+    assert M.rel_l2(o_g, o_f) <= 1e-2
+    assert np.max(np.abs(lse_g - lse_f)) <= 2e-3
+    # end to end: the oracle's backward takes the oracle's O (bf16) and LSE
+    o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
+    bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"])
+    dq_f, dk_f, dv_f = F.bwd_head(bp, w.causal, blocks, blocks)
+    sel = np.concatenate([np.arange(j * 64, j * 64 + min(64, N - i * 64)) for j, i in enumerate(blocks)])
+    errs = {"dQ": M.rel_l2(dq_g[rows], dq_f[sel]), "dK": M.rel_l2(dk_g[rows], dk_f[sel]),
+            "dV": M.rel_l2(dv_g[rows], dv_f[sel])}
+    print("  rel-L2 vs faithful:", {k: f"{v:.2e}" for k, v in errs.items()},
+          f"O {M.rel_l2(o_g, o_f):.2e}", flush=True)
+    for k, v in errs.items():
+        assert v <= 1e-2, (k, v)
+    # against exact attention, on the same sampled rows
+    oe, le, dqe, dke, dve = exact.sampled(f["q"], f["k"], f["v"], f["do"], w.causal, rows, rows)
+    cos = {"O": M.cos_sim(o_g[rows], oe), "dQ": M.cos_sim(dq_g[rows], dqe), "dK": M.cos_sim(dk_g[rows], dke),
+           "dV": M.cos_sim(dv_g[rows], dve)}
+    print("  cos vs exact:", {k: f"{v:.6f}" for k, v in cos.items()}, flush=True)
+    assert cos["O"] >= 0.999
+    for k in ("dQ", "dK", "dV"):
+        assert cos[k] >= 0.99, (k, cos[k])
