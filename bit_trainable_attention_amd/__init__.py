@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "fwd_stage", "bwd_stage", "STAGES", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
+__all__ = ["debug_tile", "DUMP_BYTES", "fwd", "bwd", "fwd_stage", "bwd_stage", "STAGES", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
            "SageBwdError", "REGIONS", "load_library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,9 @@ def load_library() -> ctypes.CDLL:
         lib.sagebwd_fwd_stage.restype = ctypes.c_int
         lib.sagebwd_bwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_bwd_stage.restype = ctypes.c_int
+        lib.sagebwd_debug_tile.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
+        lib.sagebwd_debug_tile.restype = ctypes.c_int
         lib.sagebwd_prepare.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_prepare.restype = ctypes.c_int
         lib.sagebwd_ws_region.argtypes = [_P, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
@@ -188,6 +191,32 @@ def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, sm
                              _ptr(ws), nbytes, _stream())
     _check(rc, "sagebwd_prepare")
     return ws
+
+
+DUMP_BYTES = 90368
+DEBUG_KERNELS = {"fwd": 0, "dkdv": 1, "dq": 2}
+
+
+def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=False, smooth_q=False,
+               smooth_k=True):
+    """Run one attention kernel's debug instantiation and return the raw
+    SAGEBWD_DUMP_BYTES dump of tile (bh, qblock, kblock) as a CPU uint8
+    tensor (see include/sagebwd.h for the layout).  kernel: "fwd" writes into
+    o and lse; "dkdv" and "dq" read o, lse and do."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
+    lib = load_library()
+    ws = torch.empty(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=q.device)
+    dump = torch.zeros(DUMP_BYTES, dtype=torch.uint8, device=q.device)
+    kid = DEBUG_KERNELS[kernel]
+    grads = [torch.empty_like(q) for _ in range(3)] if kid else [None, None, None]
+    rc = lib.sagebwd_debug_tile(ctypes.byref(p), kid, int(bh), int(qblock), int(kblock), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(o), _ptr(lse), _ptr(do), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]),
+                                _ptr(dump), DUMP_BYTES, _ptr(ws), ws.numel(), _stream())
+    _check(rc, "sagebwd_debug_tile")
+    torch.cuda.synchronize()
+    return dump.cpu()
 
 
 def ws_region(params: Params, region) -> tuple:

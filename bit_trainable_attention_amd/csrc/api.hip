@@ -161,6 +161,55 @@ void run_bwd_pre(const sagebwd_params& p, const Layout& L, const void* V, const 
     launch_bwd_pre(b, p.B * p.H, st);
 }
 
+FwdArgs fwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* O, float* LSE) {
+    FwdArgs a{};
+    a.q_r = region<int8_t>(ws, L, R_Q_R);
+    a.k_r = region<int8_t>(ws, L, R_K_R);
+    a.v_t = region<int8_t>(ws, L, R_V_T);
+    a.sq = region<float>(ws, L, R_S_Q);
+    a.sk = region<float>(ws, L, R_S_K);
+    a.sv = region<float>(ws, L, R_S_V);
+    a.corr = region<float>(ws, L, R_CORR);
+    a.bias = region<float>(ws, L, R_BIAS);
+    a.o = (uint16_t*)O;
+    a.lse = LSE;
+    a.N = p.N;
+    a.T = (p.N + BLK - 1) / BLK;
+    a.ngroups = (a.T + 1) / 2;
+    a.BH = p.B * p.H;
+    a.dump = nullptr;
+    a.dump_bh = a.dump_i = a.dump_t = -1;
+    return a;
+}
+
+BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* dQ, void* dK, void* dV) {
+    BwdArgs a{};
+    a.q_r = region<int8_t>(ws, L, R_Q_R);
+    a.k_r = region<int8_t>(ws, L, R_K_R);
+    a.q_t = region<int8_t>(ws, L, R_Q_T);
+    a.k_t = region<int8_t>(ws, L, R_K_T);
+    a.do_t = region<int8_t>(ws, L, R_DO_T);
+    a.sq = region<float>(ws, L, R_S_Q);
+    a.sk = region<float>(ws, L, R_S_K);
+    a.sdo = region<float>(ws, L, R_S_DO);
+    a.bias = region<float>(ws, L, R_BIAS);
+    a.delta = region<float>(ws, L, R_DELTA);
+    a.lse2 = region<float>(ws, L, R_LSE2);
+    a.do16 = region<_Float16>(ws, L, R_DO16);
+    a.v16 = region<_Float16>(ws, L, R_V16);
+    a.mu_q = region<float>(ws, L, R_MU_Q);
+    a.dq = (uint16_t*)dQ;
+    a.dk = (uint16_t*)dK;
+    a.dv = (uint16_t*)dV;
+    a.N = p.N;
+    a.T = (p.N + BLK - 1) / BLK;
+    a.ngroups = (a.T + 1) / 2;
+    a.BH = p.B * p.H;
+    a.dump = nullptr;
+    a.dump_bh = a.dump_i = a.dump_t = -1;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,21 +251,7 @@ int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         run_prepare_qkv(*p, L, Q, K, V, ws, true, true, false, st);
         return hip_status();
     }
-    FwdArgs a{};
-    a.q_r = region<int8_t>(ws, L, R_Q_R);
-    a.k_r = region<int8_t>(ws, L, R_K_R);
-    a.v_t = region<int8_t>(ws, L, R_V_T);
-    a.sq = region<float>(ws, L, R_S_Q);
-    a.sk = region<float>(ws, L, R_S_K);
-    a.sv = region<float>(ws, L, R_S_V);
-    a.corr = region<float>(ws, L, R_CORR);
-    a.bias = region<float>(ws, L, R_BIAS);
-    a.o = (uint16_t*)O;
-    a.lse = LSE;
-    a.N = p->N;
-    a.T = (p->N + BLK - 1) / BLK;
-    a.ngroups = (a.T + 1) / 2;
-    a.BH = p->B * p->H;
+    const FwdArgs a = fwd_args(*p, L, ws, O, LSE);
     launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();
 }
@@ -247,28 +282,7 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
         return hip_status();
     }
-    BwdArgs a{};
-    a.q_r = region<int8_t>(ws, L, R_Q_R);
-    a.k_r = region<int8_t>(ws, L, R_K_R);
-    a.q_t = region<int8_t>(ws, L, R_Q_T);
-    a.k_t = region<int8_t>(ws, L, R_K_T);
-    a.do_t = region<int8_t>(ws, L, R_DO_T);
-    a.sq = region<float>(ws, L, R_S_Q);
-    a.sk = region<float>(ws, L, R_S_K);
-    a.sdo = region<float>(ws, L, R_S_DO);
-    a.bias = region<float>(ws, L, R_BIAS);
-    a.delta = region<float>(ws, L, R_DELTA);
-    a.lse2 = region<float>(ws, L, R_LSE2);
-    a.do16 = region<_Float16>(ws, L, R_DO16);
-    a.v16 = region<_Float16>(ws, L, R_V16);
-    a.mu_q = region<float>(ws, L, R_MU_Q);
-    a.dq = (uint16_t*)dQ;
-    a.dk = (uint16_t*)dK;
-    a.dv = (uint16_t*)dV;
-    a.N = p->N;
-    a.T = (p->N + BLK - 1) / BLK;
-    a.ngroups = (a.T + 1) / 2;
-    a.BH = p->B * p->H;
+    const BwdArgs a = bwd_args(*p, L, ws, dQ, dK, dV);
     if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, st);
     else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();
@@ -282,6 +296,40 @@ int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const voi
         if (rc) return rc;
     }
     return SAGEBWD_OK;
+}
+
+int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, int kblock, const void* Q,
+                       const void* K, const void* V, void* O, float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                       void* dump, size_t dump_bytes, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    const int T = (p->N + BLK - 1) / BLK;
+    if (kernel < 0 || kernel > 2 || bh < 0 || bh >= p->B * p->H || qblock < 0 || qblock >= T || kblock < 0 ||
+        kblock >= T || (p->causal && kblock > qblock))
+        return SAGEBWD_ERR_INVALID_ARG;
+    if (!dump || dump_bytes < (size_t)dumpoff::BYTES) return SAGEBWD_ERR_INVALID_ARG;
+    if (kernel == 0) {
+        if ((rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream))) return rc;
+        const Layout L = make_layout(*p, PASS_FWD);
+        FwdArgs a = fwd_args(*p, L, ws, O, LSE);
+        a.dump = (uint8_t*)dump;
+        a.dump_bh = bh;
+        a.dump_i = qblock;
+        a.dump_t = kblock;
+        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
+        return hip_status();
+    }
+    if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, ws, ws_bytes, stream)))
+        return rc;
+    const Layout L = make_layout(*p, PASS_BWD);
+    BwdArgs a = bwd_args(*p, L, ws, dQ, dK, dV);
+    a.dump = (uint8_t*)dump;
+    a.dump_bh = bh;
+    a.dump_i = qblock;
+    a.dump_t = kblock;
+    if (kernel == 1) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
+    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
+    return hip_status();
 }
 
 int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,

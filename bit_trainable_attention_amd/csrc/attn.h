@@ -4,6 +4,21 @@
 
 namespace sagebwd {
 
+// Tile dump of the debug instantiations (row-major [row][col] blocks):
+//   A     i32 [64][64]  score accumulator Q_code K_code^T       [query][key]
+//   F1    f32 [64][64]  fwd: 127 P^ before rounding; dkdv: P; dq: dS
+//   C1    u8  [64][64]  fwd: P~ codes; dkdv: P codes; dq: dS codes
+//   ACC1  i32 [64][64]  fwd: P~ V_code [query][ch]; dkdv: P^T dO [key][ch];
+//                       dq: dS K [query][ch]
+//   F2    f32 [64][64]  dkdv: dS
+//   C2    u8  [64][64]  dkdv: dS codes
+//   ACC2  i32 [64][64]  dkdv: dS^T Q [key][ch]
+//   SC    f32 [4]       dkdv: s_P, s_dS; dq: s_dS
+namespace dumpoff {
+constexpr int A = 0, F1 = 16384, C1 = 32768, ACC1 = 36864, F2 = 53248, C2 = 69632, ACC2 = 73728, SC = 90112,
+              BYTES = 90368;
+}
+
 struct FwdArgs {
     const int8_t *q_r, *k_r, *v_t;     // code blocks [BH][T][4096]
     const float *sq, *sk, *sv;         // [BH][T]
@@ -11,6 +26,8 @@ struct FwdArgs {
     uint16_t* o;                       // bf16 [BH][N][64]
     float* lse;                        // [BH][N]
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): 128 query rows per workgroup
+    uint8_t* dump;                     // tile dump (debug instantiation only)
+    int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
 };
 
 struct BwdArgs {
@@ -21,11 +38,16 @@ struct BwdArgs {
     const float* mu_q;                 // [BH][64]
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
+    uint8_t* dump;                     // tile dump (debug instantiation only)
+    int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
 };
 
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st);
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
+
+template <class T>
+__device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }
 
 // Score-to-probability step shared by both backward kernels, so that the two
 // recompute bit-identical P (and hence identical dS codes): z is the

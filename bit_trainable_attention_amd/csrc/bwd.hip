@@ -88,11 +88,17 @@ struct DkdvSmem {
 // last key block, so the common path carries no per-element selects.
 template <bool CAUSAL, bool SMOOTHQ, bool MASK>
 __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float kbias,
-                                           int i, int key, int N, int lane, int h, float (&p)[2][16]) {
+                                           int i, int key, int N, int lane, int h, float (&p)[2][16],
+                                           uint8_t* dp = nullptr) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
         s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
+        if (dp) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<int>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = s[r];
+        }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
@@ -111,7 +117,7 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     __shared__ DkdvSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -188,9 +194,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         float p[2][16];                      // [qb]: lane = key, regs = queries
         const float sQ = a.sq[bt + i];
         const float sc = tile_scale(sQ, sK);
+        uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
         if (active) {
-            if (masked) dkdv_probs<CAUSAL, SMOOTHQ, true>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p);
-            else dkdv_probs<CAUSAL, SMOOTHQ, false>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p);
+            if (masked) dkdv_probs<CAUSAL, SMOOTHQ, true>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+            else dkdv_probs<CAUSAL, SMOOTHQ, false>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+            if (DUMP && dp) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<float>(dp, dumpoff::F1)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
+            }
             float pm = 0.0f;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -212,11 +226,25 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                              pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invP),
                              pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invP),
                              pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invP)};
+            if (DUMP && dp) {
+                if (lane == 0 && kh == 0) dump_at<float>(dp, dumpoff::SC)[0] = sP;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[dumpoff::C1 + (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] =
+                            (uint8_t)code_bits(p[qb][r], invP);
+            }
             const float wv = sP * a.sdo[bt + i];
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 v16i acc = mfma_i8(pc[0], sm.do_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
                 acc = mfma_i8(pc[1], sm.do_t[buf][(db * 2 + 1) * 64 + lane], acc);
+                if (DUMP && dp) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(dp, dumpoff::ACC1)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
             }
@@ -246,11 +274,27 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     dsm = __builtin_fmaxf(dsm, __builtin_fmaxf(__builtin_fabsf(p[qb][r]), __builtin_fabsf(p[qb][r + 1])));
             dsm = wave_max64(dsm);
             if (lane == 0) sm.red[1][wave] = dsm;
+            if (DUMP && dp) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<float>(dp, dumpoff::F2)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
+            }
         }
         __syncthreads();
         if (active) {
             float sdS, invdS;
             block_scale(__builtin_fmaxf(sm.red[1][wave], sm.red[1][wave ^ 1]), sdS, invdS);
+            if (DUMP && dp) {
+                if (lane == 0 && kh == 0) dump_at<float>(dp, dumpoff::SC)[1] = sdS;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[dumpoff::C2 + (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] =
+                            (uint8_t)code_bits(p[qb][r], invdS);
+            }
             v4i dc[2];
 #pragma unroll
             for (int qs = 0; qs < 2; ++qs)
@@ -271,6 +315,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             for (int db = 0; db < 2; ++db) {
                 v16i acc = mfma_i8(dc[0], sm.q_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
                 acc = mfma_i8(dc[1], sm.q_t[buf][(db * 2 + 1) * 64 + lane], acc);
+                if (DUMP && dp) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(dp, dumpoff::ACC2)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
@@ -320,12 +369,17 @@ struct DqSmem {
 template <bool CAUSAL, bool SMOOTHQ, bool MASK>
 __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i (&qop)[2], const v8h (&doh)[4],
                                            float sc, float lq, float dlq, int t, int q, int N, int lane, int h,
-                                           float (&ds)[2][16]) {
+                                           float (&ds)[2][16], uint8_t* dp = nullptr) {
     const int l32 = lane % 32;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         v16i s = mfma_i8(sm.k_r[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
         s = mfma_i8(sm.k_r[buf][(kb * 2 + 1) * 64 + lane], qop[1], s);
+        if (dp) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<int>(dp, dumpoff::A)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[r];
+        }
         const int row = 32 * kb + l32;
         v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], v16f{});
         dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
@@ -355,7 +409,7 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -421,10 +475,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         const bool masked = (CAUSAL && t == qblk) || (ragged && t == T - 1);
         const float sK = a.sk[bt + t];
         float ds[2][16];             // [kb]: lane = query, regs = keys
+        uint8_t* dp = (DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t) ? a.dump : nullptr;
         if (active) {
             const float sc = tile_scale(sQ, sK);
-            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds);
-            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds);
+            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
+            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
+            if (DUMP && dp) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<float>(dp, dumpoff::F1)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = ds[kb][r];
+            }
             float dsm = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -438,6 +500,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         if (active) {
             float sdS, invdS;
             block_scale(__builtin_fmaxf(sm.red[wave], sm.red[wave ^ 1]), sdS, invdS);
+            if (DUMP && dp) {
+                if (lane == 0 && qh == 0) dump_at<float>(dp, dumpoff::SC)[0] = sdS;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[dumpoff::C1 + (q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] =
+                            (uint8_t)code_bits(ds[kb][r], invdS);
+            }
             v4i dc[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -450,6 +521,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
             for (int db = 0; db < 2; ++db) {
                 v16i acc = mfma_i8(sm.k_t[buf][(db * 2 + 0) * 64 + lane], dc[0], v16i{});
                 acc = mfma_i8(sm.k_t[buf][(db * 2 + 1) * 64 + lane], dc[1], acc);
+                if (DUMP && dp) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(dp, dumpoff::ACC1)[(q % 64) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc[r];
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
             }
@@ -474,28 +550,34 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     }
 }
 
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
-    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
-    if (causal) {
-        if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dkdv<true, false>), grid, block, 0, st, a);
-    } else {
-        if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dkdv<false, false>), grid, block, 0, st, a);
-    }
+#define SAGEBWD_LAUNCH_BWD(KERNEL)                                                                 \
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);                                              \
+    if (causal) {                                                                                  \
+        if (smooth_q) {                                                                            \
+            if (dump) hipLaunchKernelGGL((KERNEL<true, true, true>), grid, block, 0, st, a);       \
+            else hipLaunchKernelGGL((KERNEL<true, true, false>), grid, block, 0, st, a);           \
+        } else {                                                                                   \
+            if (dump) hipLaunchKernelGGL((KERNEL<true, false, true>), grid, block, 0, st, a);      \
+            else hipLaunchKernelGGL((KERNEL<true, false, false>), grid, block, 0, st, a);          \
+        }                                                                                          \
+    } else {                                                                                       \
+        if (smooth_q) {                                                                            \
+            if (dump) hipLaunchKernelGGL((KERNEL<false, true, true>), grid, block, 0, st, a);      \
+            else hipLaunchKernelGGL((KERNEL<false, true, false>), grid, block, 0, st, a);          \
+        } else {                                                                                   \
+            if (dump) hipLaunchKernelGGL((KERNEL<false, false, true>), grid, block, 0, st, a);     \
+            else hipLaunchKernelGGL((KERNEL<false, false, false>), grid, block, 0, st, a);         \
+        }                                                                                          \
+    }                                                                                              \
     return 0;
+
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
+    SAGEBWD_LAUNCH_BWD(k_bwd_dkdv)
 }
 
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
-    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
-    if (causal) {
-        if (smooth_q) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);
-    } else {
-        if (smooth_q) hipLaunchKernelGGL((k_bwd_dq<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<false, false>), grid, block, 0, st, a);
-    }
-    return 0;
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
+    SAGEBWD_LAUNCH_BWD(k_bwd_dq)
 }
+#undef SAGEBWD_LAUNCH_BWD
 
 }  // namespace sagebwd

@@ -48,14 +48,22 @@ __device__ __forceinline__ void map_group(int ngroups, int BH, int& bh, int& g) 
 // One 64-key step of one wave: scores, tile-row max, P~ codes, online update
 // and the P~V product.  MASK is set only for the causal diagonal tile and the
 // ragged last tile, so the common path carries no per-element selects.
-template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+template <bool CAUSAL, bool SMOOTHQ, bool MASK, bool DUMP>
 __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (&qop)[2], float sc, float sv,
-                                         int t, int q, int N, int lane, int h, float& M, float& L, v16f (&O)[2]) {
+                                         int t, int q, int N, int lane, int h, float& M, float& L, v16f (&O)[2],
+                                         uint8_t* dp, int qloc) {
     v16i s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
         s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qop[1], s[kb]);
+    }
+    if (DUMP && dp) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<int>(dp, dumpoff::A)[qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[kb][r];
     }
     float z[2][16];
 #pragma unroll
@@ -108,6 +116,11 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
                 float v = __builtin_amdgcn_exp2f(SMOOTHQ ? zz + off : __builtin_fmaf(zz, sc, off));
                 if (MASK && !(zz > -__builtin_inff())) v = 0.0f;
                 pk4 = __builtin_amdgcn_cvt_pk_u8_f32(v, j, pk4);
+                if (DUMP && dp) {
+                    const int kk = 32 * kb + 8 * d4 + 4 * h + j;
+                    dump_at<float>(dp, dumpoff::F1)[qloc * 64 + kk] = v;
+                    dp[dumpoff::C1 + qloc * 64 + kk] = (uint8_t)(pk4 >> (8 * j));
+                }
             }
             w4[d4] = pk4;
             csum = __builtin_amdgcn_udot4(pk4, 0x01010101u, csum, false);
@@ -131,12 +144,17 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
     for (int db = 0; db < 2; ++db) {
         v16i pvacc = mfma_i8(sm.v[buf][(db * 2 + 0) * 64 + lane], pc[0], v16i{});
         pvacc = mfma_i8(sm.v[buf][(db * 2 + 1) * 64 + lane], pc[1], pvacc);
+        if (DUMP && dp) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<int>(dp, dumpoff::ACC1)[qloc * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = pvacc[r];
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] = __builtin_fmaf((float)pvacc[r], wv, O[db][r]);
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -163,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
         sQ = a.sq[bt + qblk];
     }
     const int q = qblk * BLK + 32 * qhalf + l32;
+    uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
     // prologue: tile 0 into buffer 0
     v4i pk = kg[tid], pv = vg[tid];
@@ -188,10 +207,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
         if (live && t <= t_last) {
             const float sc = tile_scale(sQ, a.sk[bt + t]);
             const float sv = a.sv[bt + t];
+            uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
             if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
-                fwd_tile<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O);
+                fwd_tile<CAUSAL, SMOOTHQ, true, DUMP>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O, dp,
+                                                      32 * qhalf + l32);
             else
-                fwd_tile<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O);
+                fwd_tile<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O, dp,
+                                                       32 * qhalf + l32);
         }
         if (more) {
             sm.k[buf ^ 1][tid] = pk;
@@ -225,15 +247,21 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     }
 }
 
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st) {
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * FWD_WAVES);
+#define SAGEBWD_FWD(C, S)                                                                        \
+    do {                                                                                         \
+        if (dump) hipLaunchKernelGGL((k_fwd<C, S, true>), grid, block, 0, st, a);                \
+        else hipLaunchKernelGGL((k_fwd<C, S, false>), grid, block, 0, st, a);                    \
+    } while (0)
     if (causal) {
-        if (smooth_q) hipLaunchKernelGGL((k_fwd<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fwd<true, false>), grid, block, 0, st, a);
+        if (smooth_q) SAGEBWD_FWD(true, true);
+        else SAGEBWD_FWD(true, false);
     } else {
-        if (smooth_q) hipLaunchKernelGGL((k_fwd<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_fwd<false, false>), grid, block, 0, st, a);
+        if (smooth_q) SAGEBWD_FWD(false, true);
+        else SAGEBWD_FWD(false, false);
     }
+#undef SAGEBWD_FWD
     return 0;
 }
 

@@ -148,6 +148,30 @@ const char* sagebwd_status_string(int status);
  *                          + 4*((r%32)/8) + r%4
  * so that one 16-byte load per lane feeds a 32x32x32 INT8 MFMA operand.
  * Returns SAGEBWD_ERR_INVALID_ARG for an unknown region id. */
+/* sagebwd_debug_tile runs one pass of one attention kernel through its
+ * debug instantiation, which also writes the values of a single 64x64 tile
+ * (head ``bh`` = b*H + h, query block ``qblock``, key block ``kblock``) to
+ * ``dump`` (SAGEBWD_DUMP_BYTES bytes, row-major blocks):
+ *   kernel 0 (forward, writes O and LSE; ws of at least the forward size):
+ *     A i32[q][k] at 0, 127*P^ f32[q][k] at 16384, P~ codes u8[q][k] at 32768,
+ *     P~ V i32[q][c] at 36864
+ *   kernel 1 (dK/dV; runs the backward preparation first; writes dK, dV):
+ *     A at 0, P f32[q][k] at 16384, P codes u8[q][k] at 32768,
+ *     P^T dO i32[k][c] at 36864, dS f32[q][k] at 53248, dS codes u8[q][k] at
+ *     69632, dS^T Q i32[k][c] at 73728, s_P and s_dS f32 at 90112
+ *   kernel 2 (dQ; runs the backward preparation first; writes dQ):
+ *     A at 0, dS f32[q][k] at 16384, dS codes u8[q][k] at 32768,
+ *     dS K i32[q][c] at 36864, s_dS f32 at 90112
+ * (q, k: query and key within the blocks; c: channel), so that the INT8
+ * codes, block scales and integer tile products can be re-derived exactly
+ * from the kernel's own pre-quantization values.  Tiles above the causal
+ * diagonal are never computed and are rejected (SAGEBWD_ERR_INVALID_ARG). */
+#define SAGEBWD_DUMP_BYTES 90368
+int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, int kblock,
+                       const void* Q, const void* K, const void* V, void* O, float* LSE, const void* dO,
+                       void* dQ, void* dK, void* dV, void* dump, size_t dump_bytes,
+                       void* ws, size_t ws_bytes, void* stream);
+
 int sagebwd_prepare(const sagebwd_params* p,
                     const void* Q, const void* K, const void* V,
                     const void* O, const float* LSE, const void* dO,
