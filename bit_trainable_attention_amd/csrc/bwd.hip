@@ -248,24 +248,26 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
             }
-            // dP = dO V^T (FP16), dS = P * (dP - Delta) in place of P
+            // dP - Delta = dO V^T + (-Delta) (FP16 MFMA, -Delta as the
+            // accumulator input), dS = P * (dP - Delta) in place of P
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const int row = 32 * qb + l32;
-                v16f dp = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], v16f{});
+                v16f nd;
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4 d4 = *(const float4*)&sm.delta[buf][32 * qb + 8 * r4 + 4 * h];
+                    nd[4 * r4 + 0] = d4.x;
+                    nd[4 * r4 + 1] = d4.y;
+                    nd[4 * r4 + 2] = d4.z;
+                    nd[4 * r4 + 3] = d4.w;
+                }
+                v16f dp = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
                 dp = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dp);
                 dp = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dp);
                 dp = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dp);
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 d4 = *(const float4*)&sm.delta[buf][32 * qb + 8 * r4 + 4 * h];
-                    const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * r4 + j;
-                        p[qb][r] = p[qb][r] * (dp[r] - dl[j]);
-                    }
-                }
+                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dp[r];
             }
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -368,7 +370,7 @@ struct DqSmem {
 // registers = keys); same float32 operations as the key-block kernel.
 template <bool CAUSAL, bool SMOOTHQ, bool MASK>
 __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i (&qop)[2], const v8h (&doh)[4],
-                                           float sc, float lq, float dlq, int t, int q, int N, int lane, int h,
+                                           float sc, float lq, const v16f& nd, int t, int q, int N, int lane, int h,
                                            float (&ds)[2][16], uint8_t* dp = nullptr) {
     const int l32 = lane % 32;
 #pragma unroll
@@ -381,7 +383,7 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
                 dump_at<int>(dp, dumpoff::A)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[r];
         }
         const int row = 32 * kb + l32;
-        v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], v16f{});
+        v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], nd);
         dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
         dp = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dp);
         dp = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dp);
@@ -403,7 +405,7 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
                     const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
                     if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
                 }
-                ds[kb][r] = pv * (dp[r] - dlq);
+                ds[kb][r] = pv * dp[r];
             }
         }
     }
@@ -463,6 +465,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     };
 
     v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
+    v16f nd;                         // -Delta of this lane's query: accumulator input of V dO^T
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nd[r] = dlq;
     fetch(0);
     stage(0);
     __syncthreads();
@@ -478,8 +483,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         uint8_t* dp = (DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t) ? a.dump : nullptr;
         if (active) {
             const float sc = tile_scale(sQ, sK);
-            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
-            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, dlq, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
+            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, nd, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
+            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, nd, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
             if (DUMP && dp) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)

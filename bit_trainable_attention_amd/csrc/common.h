@@ -38,6 +38,7 @@ constexpr float SCORE_SCALE_LOG2 = LOG2E * 0.125f;   // 1/sqrt(64) folded into l
 constexpr float MAGIC = 12582912.0f;
 constexpr uint32_t MAGIC_BITS = 0x4B400000u;
 constexpr float A_MIN = 0x1p-100f;         // smaller block absmax -> all-zero block
+constexpr float R127 = 1.0f / 127.0f;      // correctly rounded float32 of 1/127
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
@@ -48,11 +49,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
-// Per-block scale from an absmax: s = a/127 and inv = 127/a, both correctly
-// rounded float32 divisions; blocks with a < 2^-100 are all-zero.
+// Per-block scale from an absmax: s = a * fp32(1/127) (one rounded
+// multiply) and inv = 127/a (correctly rounded float32 division); blocks with
+// a < 2^-100 are all-zero.
 __device__ __forceinline__ void block_scale(float a, float& s, float& inv) {
     if (a >= A_MIN) {
-        s = a / 127.0f;
+        s = a * R127;
         inv = 127.0f / a;
     } else {
         s = 0.0f;

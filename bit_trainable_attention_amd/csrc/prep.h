@@ -30,7 +30,7 @@ struct BwdPreArgs {
     const uint16_t *dout, *o, *v;      // bf16 [BH][N][64]
     const float* lse;                  // [BH][N]
     const float* corr;                 // [BH][Np]
-    float *delta, *lse2;               // [BH][Np]
+    float *delta, *lse2;               // [BH][Np]: -rowsum(dO*O), log2-domain LSE
     int8_t* do_t;                      // transposed operand layout
     float* sdo;                        // [BH][T]
     _Float16 *do16, *v16;              // [BH][Np][64]

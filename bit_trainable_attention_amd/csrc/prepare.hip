@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
 }
 
 // ---------------------------------------------------------------- backward prep
-// One workgroup per 64-token block: Delta = rowsum(dO*O) (fp32), the
+// One workgroup per 64-token block: -Delta = -rowsum(dO*O) (fp32), the
 // log2-domain LSE of the smoothed scores, dO codes (transposed operand
 // layout) and scale, FP16 copies of dO and V.  Rows past N are zeroed (their
 // LSE is +inf so every P of such a row is 0).
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     delta += __shfl_xor(delta, 2, 64);
     const size_t row = (size_t)bh * a.T * BLK + tok;
     if (g == 0) {
-        a.delta[row] = valid ? delta : 0.0f;
+        a.delta[row] = valid ? -delta : 0.0f;
         a.lse2[row] = valid ? (a.lse[(size_t)bh * a.N + tok] - a.corr[row]) * LOG2E : __builtin_inff();
     }
     // FP16 copies (natural layout [Np][64])

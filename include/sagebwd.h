@@ -137,7 +137,7 @@ const char* sagebwd_status_string(int status);
  *   8  S_Q    float32 [BH][T]        block scales (likewise 9 S_K, 10 S_V, 11 S_DO)
  *   12 CORR   float32 [BH][Np]       q_raw . mu_K / 8 per query (0 past N)
  *   13 BIAS   float32 [BH][Np]       Q-smoothing key bias mu_Q . K^_j times log2(e)/8
- *   14 DELTA  float32 [BH][Np]       rowsum(dO * O)
+ *   14 NDELTA float32 [BH][Np]       -rowsum(dO * O)
  *   15 LSE2   float32 [BH][Np]       (LSE - CORR) * log2(e); +inf past N
  *   16 DO16   fp16 [BH][Np][64]      dO in FP16, natural layout
  *   17 V16    fp16 [BH][Np][64]      V in FP16, natural layout

@@ -117,7 +117,7 @@ def test_ws_regions_layout(lib):
         expect = {"MU_Q": BH * 256, "MU_K": BH * 256, "Q_R": BH * T * 4096, "K_R": BH * T * 4096,
                   "V_T": BH * T * 4096, "Q_T": BH * T * 4096, "K_T": BH * T * 4096, "DO_T": BH * T * 4096,
                   "S_Q": BH * T * 4, "S_K": BH * T * 4, "S_V": BH * T * 4, "S_DO": BH * T * 4,
-                  "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "DELTA": BH * Np * 4, "LSE2": BH * Np * 4,
+                  "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "NDELTA": BH * Np * 4, "LSE2": BH * Np * 4,
                   "DO16": BH * Np * 128, "V16": BH * Np * 128}
         spans = []
         for name, rid in sb.REGIONS.items():

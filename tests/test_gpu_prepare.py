@@ -51,7 +51,7 @@ def _run(w, heads):
         "sv": G.region(wsh, p, "S_V", np.float32).reshape(BH, T), "sdo": G.region(wsh, p, "S_DO", np.float32).reshape(BH, T),
         "corr": G.region(wsh, p, "CORR", np.float32).reshape(BH, Np),
         "bias": G.region(wsh, p, "BIAS", np.float32).reshape(BH, Np),
-        "delta": G.region(wsh, p, "DELTA", np.float32).reshape(BH, Np),
+        "delta": -G.region(wsh, p, "NDELTA", np.float32).reshape(BH, Np),
         "lse2": G.region(wsh, p, "LSE2", np.float32).reshape(BH, Np),
         "do16": G.region(wsh, p, "DO16", np.float16).reshape(BH, Np, 64),
         "v16": G.region(wsh, p, "V16", np.float16).reshape(BH, Np, 64),

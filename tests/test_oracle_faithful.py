@@ -82,7 +82,11 @@ def _f32_round(fr: Fraction) -> Fraction:
 
 def test_quantizer_matches_exact_rationals():
     """Scale, inverse and codes re-derived with exact rationals, with float32
-    rounding done by hand, agree bit for bit with the float32 route."""
+    rounding done by hand, agree bit for bit with the float32 route.  The
+    scale is absmax times the float32 of 1/127 (one rounded multiply), which
+    stays within one float32 ulp of absmax/127; the inverse is the correctly
+    rounded 127/absmax."""
+    r127 = _f32_round(Fraction(1, 127))
     r = np.random.default_rng(7)
     n_checked = 0
     for trial in range(400):
@@ -91,9 +95,10 @@ def test_quantizer_matches_exact_rationals():
         a = np.max(np.abs(x))
         s, inv = F.block_scale(a)
         fa = Fraction(float(a))
-        s_ref = _f32_round(fa / 127)
+        s_ref = _f32_round(fa * r127)
         inv_ref = _f32_round(Fraction(127) / fa)
         assert Fraction(float(s)) == s_ref
+        assert abs(s_ref - fa / 127) <= fa / 127 * Fraction(1, 2 ** 23)
         assert Fraction(float(inv)) == inv_ref
         codes = F.block_codes(x, inv)
         for xi, ci in zip(x.tolist(), codes.tolist()):
