@@ -31,19 +31,25 @@ namespace sagebwd {
 constexpr int BWD_WAVES = 4;
 
 template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
-// Maximum over the 64 lanes of a wave, returned in every lane.
-__device__ __forceinline__ float wave_max64(float v) {
-    v = __builtin_fmaxf(v, dppf<0xB1>(v));    // quad_perm [1,0,3,2]
-    v = __builtin_fmaxf(v, dppf<0x4E>(v));    // quad_perm [2,3,0,1]
-    v = __builtin_fmaxf(v, dppf<0x141>(v));   // row_half_mirror
-    v = __builtin_fmaxf(v, dppf<0x140>(v));   // row_mirror
-    v = __builtin_fmaxf(v, __shfl_xor(v, 16, 64));
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __builtin_fmaxf(v, __builtin_fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1])));
+// Maximum over the 64 lanes of a wave of non-negative floats, returned in
+// every lane.  Non-negative floats order like their bit patterns, so the
+// reduction runs on unsigned integers: DPP within each 16-lane row, then the
+// row-pair and half-wave swaps.
+__device__ __forceinline__ float wave_max64(float f) {
+    uint32_t v = __float_as_uint(f);
+    v = umax(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = umax(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = umax(v, dppu<0x141>(v));   // row_half_mirror
+    v = umax(v, dppu<0x140>(v));   // row_mirror
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = umax(v, umax(s[0], s[1]));
+    const auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(umax(v, umax(t[0], t[1])));
 }
 
 // Four signed codes rne(x * inv) packed into one dword.
@@ -205,12 +211,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     for (int r = 0; r < 16; ++r)
                         dump_at<float>(dp, dumpoff::F1)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
             }
-            float pm = 0.0f;
+            // P >= 0: its maximum is the maximum of the bit patterns
+            uint32_t pm0 = 0, pm1 = 0;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) pm = __builtin_fmaxf(pm, __builtin_fmaxf(p[qb][r], p[qb][r + 1]));
-            pm = wave_max64(pm);
+            for (int r = 0; r < 16; r += 2) {
+                pm0 = umax(pm0, umax(__float_as_uint(p[0][r]), __float_as_uint(p[0][r + 1])));
+                pm1 = umax(pm1, umax(__float_as_uint(p[1][r]), __float_as_uint(p[1][r + 1])));
+            }
+            const float pm = wave_max64(__uint_as_float(umax(pm0, pm1)));
             if (lane == 0) sm.red[0][wave] = pm;
         }
         __syncthreads();
@@ -269,12 +277,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dp[r];
             }
+            {
+                float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2)
-                    dsm = __builtin_fmaxf(dsm, __builtin_fmaxf(__builtin_fabsf(p[qb][r]), __builtin_fabsf(p[qb][r + 1])));
-            dsm = wave_max64(dsm);
+                for (int r = 0; r < 16; r += 2) {
+                    m0 = max_abs2f(m0, p[0][r], p[0][r + 1]);
+                    m1 = max_abs2f(m1, p[1][r], p[1][r + 1]);
+                }
+                dsm = wave_max64(max3f(m0, m1, m1));
+            }
             if (lane == 0) sm.red[1][wave] = dsm;
             if (DUMP && dp) {
 #pragma unroll
@@ -492,13 +503,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
                     for (int r = 0; r < 16; ++r)
                         dump_at<float>(dp, dumpoff::F1)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = ds[kb][r];
             }
-            float dsm = 0.0f;
+            float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2)
-                    dsm = __builtin_fmaxf(dsm, __builtin_fmaxf(__builtin_fabsf(ds[kb][r]), __builtin_fabsf(ds[kb][r + 1])));
-            dsm = wave_max64(dsm);
+            for (int r = 0; r < 16; r += 2) {
+                m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
+                m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
+            }
+            const float dsm = wave_max64(max3f(m0, m1, m1));
             if (lane == 0) sm.red[wave] = dsm;
         }
         __syncthreads();

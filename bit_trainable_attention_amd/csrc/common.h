@@ -89,6 +89,21 @@ __device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// max(a, b, c) and max(a, |b|, |c|) as one v_max3_f32.  fmaxf in IEEE mode
+// makes the compiler quiet every operand it cannot prove canonical (one extra
+// v_max_f32 per value); the operands here are arithmetic results, never
+// signaling NaNs, so the raw instruction gives the same maximum.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float max_abs2f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
