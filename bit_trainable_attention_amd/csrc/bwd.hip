@@ -59,6 +59,20 @@ __device__ __forceinline__ int pack_codes(float x0, float x1, float x2, float x3
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+// Global -> LDS copies that bypass the registers (global_load_lds): every
+// lane of the wave moves 16 (4) bytes from its own global address to
+// lds_wave_base + 16 (4) * lane.  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+// Wait for this wave's outstanding vector-memory loads (LDS DMA included).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Workgroup -> (head, group) as in the forward: the groups of a head share an
 // XCD when the head count allows.  first_small selects the order of groups
 // within a head (smallest index first for the key-block kernel, whose causal
@@ -374,6 +388,7 @@ struct DqSmem {
     v4i k_t[2][256];     // K transposed codes (A operand of K^T dS^T)
     v8h v16[2][512];     // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
     float bias[2][64];   // Q-smoothing key bias (log2 domain)
+    float sk[2][4];      // [0]: K block scale
     float red[4];        // partial dS tile maxima, per wave
 };
 
@@ -423,7 +438,7 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
 }
 
 template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
@@ -456,40 +471,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
 
     const v4i* krg = (const v4i*)(a.k_r + bt * 4096);
     const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
-    v4i s_kr, s_kt, s_v0, s_v1;
-    float4 s_b;
-    auto fetch = [&](int t) {
-        s_kr = krg[(size_t)t * 256 + tid];
-        s_kt = ktg[(size_t)t * 256 + tid];
+    // key block t -> LDS buffer b by DMA; LDS slot s of the FP16 V tile
+    // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
+    auto fetch = [&](int t, int b) {
+        dma16_to_lds(krg + (size_t)t * 256 + tid, &sm.k_r[b][64 * wave]);
+        dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.k_t[b][64 * wave]);
         const v4i* vs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
-        s_v0 = vs[tid];
-        s_v1 = vs[tid + 256];
-        if (SMOOTHQ && tid < 16) s_b = ((const float4*)(a.bias + rowbase + t * BLK))[tid];
-    };
-    auto stage = [&](int b) {
-        sm.k_r[b][tid] = s_kr;
-        sm.k_t[b][tid] = s_kt;
-        const int c0 = tid, c1 = tid + 256;
-        ((v4i*)sm.v16[b])[swz(c0 / 8, c0 % 8)] = s_v0;
-        ((v4i*)sm.v16[b])[swz(c1 / 8, c1 % 8)] = s_v1;
-        if (SMOOTHQ && tid < 16) ((float4*)sm.bias[b])[tid] = s_b;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int s = 256 * j + tid, row = s / 8;
+            dma16_to_lds(vs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+        }
+        if (SMOOTHQ && wave == 0 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
+        if (wave == 1 && lane == 0) dma4_to_lds(a.sk + bt + t, &sm.sk[b][0]);
     };
 
     v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
     v16f nd;                         // -Delta of this lane's query: accumulator input of V dO^T
 #pragma unroll
     for (int r = 0; r < 16; ++r) nd[r] = dlq;
-    fetch(0);
-    stage(0);
+    fetch(0, 0);
+    wait_vmem();
     __syncthreads();
     const bool ragged = (a.N & (BLK - 1)) != 0;
     for (int t = 0; t <= t_last_wg; ++t) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
-        if (more) fetch(t + 1);
         const bool active = live && (!CAUSAL || t <= qblk);
         const bool masked = (CAUSAL && t == qblk) || (ragged && t == T - 1);
-        const float sK = a.sk[bt + t];
+        const float sK = sm.sk[buf][0];
         float ds[2][16];             // [kb]: lane = query, regs = keys
         uint8_t* dp = (DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t) ? a.dump : nullptr;
         if (active) {
@@ -512,6 +522,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
             const float dsm = wave_max64(max3f(m0, m1, m1));
             if (lane == 0) sm.red[wave] = dsm;
         }
+        // the next key block goes to the other buffer by DMA; its latency is
+        // covered by the other workgroups on the CU (three per CU)
+        if (more) fetch(t + 1, buf ^ 1);
+        wait_vmem();
         __syncthreads();
         if (active) {
             float sdS, invdS;
@@ -546,7 +560,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
             }
         }
-        if (more) stage(buf ^ 1);
         __syncthreads();
     }
 
