@@ -98,8 +98,8 @@ struct DkdvSmem {
     v4i q_t[2][256];     // Q transposed codes (B operand of dS^T Q)
     v4i do_t[2][256];    // dO transposed codes (B operand of P^T dO)
     v8h do16[2][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
-    float lse2[2][64];
-    float delta[2][64];
+    float lse2[2][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta of the query block
+    float qs[2][4];      // [0]: Q block scale, [1]: dO block scale
     float red[2][4];     // partial tile maxima of P [0] and dS [1], per wave
 };
 
@@ -169,50 +169,40 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     }
 
     const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
-    // staging of query block i into buffer b
+    // query block i -> LDS buffer b by DMA; LDS slot s of the FP16 dO tile
+    // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
     const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
     const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
     const v4i* dtg = (const v4i*)(a.do_t + bt * 4096);
-    v4i s_qr, s_qt, s_dt, s_h0, s_h1;
-    float4 s_rv;
-    auto fetch = [&](int i) {
-        s_qr = qrg[(size_t)i * 256 + tid];
-        s_qt = qtg[(size_t)i * 256 + tid];
-        s_dt = dtg[(size_t)i * 256 + tid];
+    auto fetch = [&](int i, int b) {
+        dma16_to_lds(qrg + (size_t)i * 256 + tid, &sm.q_r[b][64 * wave]);
+        dma16_to_lds(qtg + (size_t)i * 256 + tid, &sm.q_t[b][64 * wave]);
+        dma16_to_lds(dtg + (size_t)i * 256 + tid, &sm.do_t[b][64 * wave]);
         const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
-        s_h0 = hs[tid];
-        s_h1 = hs[tid + 256];
-        if (tid < 16) s_rv = ((const float4*)(a.lse2 + rowbase + i * BLK))[tid];
-        else if (tid < 32) s_rv = ((const float4*)(a.delta + rowbase + i * BLK))[tid - 16];
-    };
-    auto stage = [&](int b) {
-        sm.q_r[b][tid] = s_qr;
-        sm.q_t[b][tid] = s_qt;
-        sm.do_t[b][tid] = s_dt;
-        {
-            const int c0 = tid, c1 = tid + 256;
-            ((v4i*)sm.do16[b])[swz(c0 / 8, c0 % 8)] = s_h0;
-            ((v4i*)sm.do16[b])[swz(c1 / 8, c1 % 8)] = s_h1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int s = 256 * j + tid, row = s / 8;
+            dma16_to_lds(hs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
         }
-        if (tid < 16) ((float4*)sm.lse2[b])[tid] = s_rv;
-        else if (tid < 32) ((float4*)sm.delta[b])[tid - 16] = s_rv;
+        if (wave == 0 && lane < 32)
+            dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
+        if (wave == 1 && lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
     };
 
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
     float gsum = 0.0f;                                          // sum_i s_dS colsum(dS codes), this half
 
-    fetch(i0);
-    stage(0);
+    fetch(i0, 0);
+    wait_vmem();
     __syncthreads();
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
     for (int i = i0; i < T; ++i) {
         const int buf = (i - i0) & 1;
         const bool more = i + 1 < T;
-        if (more) fetch(i + 1);
         const bool active = live && (!CAUSAL || i >= kvb);
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
         float p[2][16];                      // [qb]: lane = key, regs = queries
-        const float sQ = a.sq[bt + i];
+        const float sQ = sm.qs[buf][0];
         const float sc = tile_scale(sQ, sK);
         uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
         if (active) {
@@ -235,6 +225,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             const float pm = wave_max64(__uint_as_float(umax(pm0, pm1)));
             if (lane == 0) sm.red[0][wave] = pm;
         }
+        // the next query block goes to the other buffer by DMA
+        if (more) fetch(i + 1, buf ^ 1);
+        wait_vmem();
         __syncthreads();
         float dsm = 0.0f;
         if (active) {
@@ -257,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                         dp[dumpoff::C1 + (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] =
                             (uint8_t)code_bits(p[qb][r], invP);
             }
-            const float wv = sP * a.sdo[bt + i];
+            const float wv = sP * sm.qs[buf][1];
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 v16i acc = mfma_i8(pc[0], sm.do_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
@@ -278,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 v16f nd;
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 d4 = *(const float4*)&sm.delta[buf][32 * qb + 8 * r4 + 4 * h];
+                    const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
                     nd[4 * r4 + 0] = d4.x;
                     nd[4 * r4 + 1] = d4.y;
                     nd[4 * r4 + 2] = d4.z;
@@ -351,7 +344,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
         }
-        if (more) stage(buf ^ 1);
         __syncthreads();
     }
 
