@@ -89,14 +89,16 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
             }
         }
     }
-    float mx = -__builtin_inff();
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(z[kb][r], z[kb][r + 1]));
+    for (int r = 0; r < 16; r += 2) {
+        m0 = max3f(m0, z[0][r], z[0][r + 1]);
+        m1 = max3f(m1, z[1][r], z[1][r + 1]);
+    }
+    float mx = max3f(m0, m1, m1);
     {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
     // tile-row max in log2 units; the code is rne(127 * exp2(score - max))
     const float mt = SMOOTHQ ? mx : mx * sc;
