@@ -3,7 +3,9 @@
 One step = one pass of the whole path over one batch of synthetic input: the
 forward (preparation + fused attention kernel) and the backward (preparation,
 dK/dV kernel, dQ kernel), all through the library's C ABI on torch's current
-stream, with inputs already resident in HBM.  Throughput is reported as
+stream, with inputs already resident in HBM.  As in training, the backward
+reads the quantized Q and K from the forward's workspace (--no-reuse makes it
+re-quantize them; the results are bit-identical).  Throughput is reported as
 fwd+bwd TOPS = sum over (batch, head) of 14 N^2 d (4 forward + 10 backward,
 halved when causal) per step time.
 
@@ -101,6 +103,8 @@ def main():
     ap.add_argument("--workload", default="llama16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-reuse", action="store_true",
+                    help="let the backward re-quantize Q and K instead of reading the forward's workspace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size before timing (counter calibration)")
     args = ap.parse_args()
@@ -143,7 +147,7 @@ def main():
             if s.startswith("FWD"):
                 sb.fwd_stage(s, q, k, v, o, lse, ws_f, p)
             else:
-                sb.bwd_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws_b, p)
+                sb.bwd_stage(s, q, k, v, o, lse, do, dq, dk, dv, ws_b, p, fwd_ws=None if args.no_reuse else ws_f)
         if events is not None:
             events[len(stages)].record()
 
@@ -191,7 +195,8 @@ def main():
         "dtype": "i8 (dO.V^T f16)",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step},
+                   "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
+                   "bwd_reuses_fwd_quantization": not args.no_reuse},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
         "roofline": roof,

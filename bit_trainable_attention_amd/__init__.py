@@ -61,11 +61,12 @@ def load_library() -> ctypes.CDLL:
         lib.sagebwd_bwd_workspace_size.restype = _sz
         lib.sagebwd_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_fwd.restype = ctypes.c_int
-        lib.sagebwd_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_bwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
         lib.sagebwd_bwd.restype = ctypes.c_int
         lib.sagebwd_fwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.sagebwd_fwd_stage.restype = ctypes.c_int
-        lib.sagebwd_bwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.sagebwd_bwd_stage.argtypes = [_P, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                          _vp, _sz, _vp]
         lib.sagebwd_bwd_stage.restype = ctypes.c_int
         lib.sagebwd_debug_tile.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
@@ -125,7 +126,9 @@ def _workspace(nbytes, device, ws=None):
 
 
 def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None):
-    """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N])."""
+    """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N]).  Pass a
+    forward-sized uint8 ``workspace`` to keep the quantized Q and K for a
+    backward that reuses them (``bwd(..., fwd_workspace=workspace)``)."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
     p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
@@ -142,8 +145,11 @@ def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, ou
     return o, lse
 
 
-def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None):
-    """Backward.  Returns (dQ, dK, dV) bf16 [B,H,N,64]."""
+def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None,
+        fwd_workspace=None):
+    """Backward.  Returns (dQ, dK, dV) bf16 [B,H,N,64].  ``fwd_workspace``:
+    the workspace of the forward call on the same q, k, v and flags, whose
+    quantized Q and K are then reused (bit-identical results)."""
     _check_qkv(q, k, v, o, do)
     if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3]):
         raise SageBwdError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
@@ -155,8 +161,10 @@ def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, worksp
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
+    fws = fwd_workspace
     rc = lib.sagebwd_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(fws), 0 if fws is None else fws.numel() * fws.element_size(),
+                         _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(rc, "sagebwd_bwd")
     return dq, dk, dv
 
@@ -170,11 +178,14 @@ def fwd_stage(stage, q, k, v, o, lse, ws, params: Params):
     _check(rc, f"sagebwd_fwd_stage({stage})")
 
 
-def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params):
-    """Run one backward stage (see STAGES) on caller-owned buffers."""
+def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params, fwd_ws=None):
+    """Run one backward stage (see STAGES) on caller-owned buffers; fwd_ws as
+    in bwd()."""
     rc = load_library().sagebwd_bwd_stage(ctypes.byref(params), STAGES[stage] if isinstance(stage, str) else stage,
                                           _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                                          _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream())
+                                          _ptr(dk), _ptr(dv), _ptr(fwd_ws),
+                                          0 if fwd_ws is None else fwd_ws.numel() * fwd_ws.element_size(),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream())
     _check(rc, f"sagebwd_bwd_stage({stage})")
 
 
@@ -229,18 +240,21 @@ def ws_region(params: Params, region) -> tuple:
 
 
 class SageBwdAttention(torch.autograd.Function):
-    """Autograd wrapper: forward and backward both run the HIP library."""
+    """Autograd wrapper: forward and backward both run the HIP library; the
+    backward reuses the forward's quantized Q and K (its workspace is kept)."""
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k)
-        ctx.save_for_backward(q, k, v, o, lse)
+        B, H, N, D = q.shape
+        ws = torch.empty(workspace_size(B, H, N, causal, smooth_q, smooth_k), dtype=torch.uint8, device=q.device)
+        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k, workspace=ws)
+        ctx.save_for_backward(q, k, v, o, lse, ws)
         ctx.flags = (causal, smooth_q, smooth_k)
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags)
+        q, k, v, o, lse, ws = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags, fwd_workspace=ws)
         return dq, dk, dv, None, None, None

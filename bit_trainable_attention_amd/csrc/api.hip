@@ -45,8 +45,8 @@ Layout make_layout(const sagebwd_params& p, Pass pass) {
     sz[R_Q_R] = BH * T * 4096;
     sz[R_K_R] = BH * T * 4096;
     sz[R_V_T] = BH * T * 4096;
-    sz[R_Q_T] = bwd ? BH * T * 4096 : 0;
-    sz[R_K_T] = bwd ? BH * T * 4096 : 0;
+    sz[R_Q_T] = BH * T * 4096;     // the forward writes these too, for a backward that reuses them
+    sz[R_K_T] = BH * T * 4096;
     sz[R_DO_T] = bwd ? BH * T * 4096 : 0;
     sz[R_S_Q] = BH * T * 4;
     sz[R_S_K] = BH * T * 4;
@@ -142,14 +142,22 @@ void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, co
     launch_quantize(a, BH, want_vt ? 3 : 2, st);
 }
 
-void run_bwd_pre(const sagebwd_params& p, const Layout& L, const void* V, const void* O, const float* LSE,
-                 const void* dO, void* ws, hipStream_t st) {
+// Where the backward reads the quantized Q and K (means, codes in both
+// layouts, scales, LSE correction, Q-smoothing bias): its own workspace after
+// re-quantizing, or the workspace of the forward that produced them.
+struct QkSource {
+    void* ws;
+    Layout L;
+};
+
+void run_bwd_pre(const sagebwd_params& p, const Layout& L, const QkSource& qk, const void* V, const void* O,
+                 const float* LSE, const void* dO, void* ws, hipStream_t st) {
     BwdPreArgs b{};
     b.dout = (const uint16_t*)dO;
     b.o = (const uint16_t*)O;
     b.v = (const uint16_t*)V;
     b.lse = LSE;
-    b.corr = region<float>(ws, L, R_CORR);
+    b.corr = region<float>(qk.ws, qk.L, R_CORR);
     b.delta = region<float>(ws, L, R_DELTA);
     b.lse2 = region<float>(ws, L, R_LSE2);
     b.do_t = region<int8_t>(ws, L, R_DO_T);
@@ -182,22 +190,23 @@ FwdArgs fwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* O, fl
     return a;
 }
 
-BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* dQ, void* dK, void* dV) {
+BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, void* ws, void* dQ, void* dK,
+                 void* dV) {
     BwdArgs a{};
-    a.q_r = region<int8_t>(ws, L, R_Q_R);
-    a.k_r = region<int8_t>(ws, L, R_K_R);
-    a.q_t = region<int8_t>(ws, L, R_Q_T);
-    a.k_t = region<int8_t>(ws, L, R_K_T);
+    a.q_r = region<int8_t>(qk.ws, qk.L, R_Q_R);
+    a.k_r = region<int8_t>(qk.ws, qk.L, R_K_R);
+    a.q_t = region<int8_t>(qk.ws, qk.L, R_Q_T);
+    a.k_t = region<int8_t>(qk.ws, qk.L, R_K_T);
     a.do_t = region<int8_t>(ws, L, R_DO_T);
-    a.sq = region<float>(ws, L, R_S_Q);
-    a.sk = region<float>(ws, L, R_S_K);
+    a.sq = region<float>(qk.ws, qk.L, R_S_Q);
+    a.sk = region<float>(qk.ws, qk.L, R_S_K);
     a.sdo = region<float>(ws, L, R_S_DO);
-    a.bias = region<float>(ws, L, R_BIAS);
+    a.bias = region<float>(qk.ws, qk.L, R_BIAS);
     a.delta = region<float>(ws, L, R_DELTA);
     a.lse2 = region<float>(ws, L, R_LSE2);
     a.do16 = region<_Float16>(ws, L, R_DO16);
     a.v16 = region<_Float16>(ws, L, R_V16);
-    a.mu_q = region<float>(ws, L, R_MU_Q);
+    a.mu_q = region<float>(qk.ws, qk.L, R_MU_Q);
     a.dq = (uint16_t*)dQ;
     a.dk = (uint16_t*)dK;
     a.dv = (uint16_t*)dV;
@@ -248,7 +257,7 @@ int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
     if (stage == SAGEBWD_STAGE_FWD_PREPARE) {
-        run_prepare_qkv(*p, L, Q, K, V, ws, true, true, false, st);
+        run_prepare_qkv(*p, L, Q, K, V, ws, true, true, true, st);
         return hip_status();
     }
     const FwdArgs a = fwd_args(*p, L, ws, O, LSE);
@@ -264,8 +273,8 @@ int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const voi
 }
 
 int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const void* K, const void* V,
-                      const void* O, const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      const void* O, const float* LSE, const void* dO, void* dQ, void* dK, void* dV,
+                      const void* fwd_ws, size_t fwd_ws_bytes, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_params(p);
     if (rc) return rc;
     if (stage != SAGEBWD_STAGE_BWD_PREPARE && stage != SAGEBWD_STAGE_BWD_DKDV && stage != SAGEBWD_STAGE_BWD_DQ)
@@ -276,23 +285,32 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
     const Layout L = make_layout(*p, PASS_BWD);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+    QkSource qk{ws, L};
+    if (fwd_ws) {
+        qk.L = make_layout(*p, PASS_FWD);
+        if ((rc = check_ws(qk.L, fwd_ws, fwd_ws_bytes))) return rc;
+        const uintptr_t f0 = (uintptr_t)fwd_ws, f1 = f0 + qk.L.total, w0 = (uintptr_t)ws, w1 = w0 + L.total;
+        if (f0 < w1 && w0 < f1) return SAGEBWD_ERR_INVALID_ARG;   // the two workspaces overlap
+        qk.ws = const_cast<void*>(fwd_ws);   // read only
+    }
     hipStream_t st = (hipStream_t)stream;
     if (stage == SAGEBWD_STAGE_BWD_PREPARE) {
-        run_prepare_qkv(*p, L, Q, K, V, ws, true, false, true, st);
-        run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+        if (!fwd_ws) run_prepare_qkv(*p, L, Q, K, V, ws, true, false, true, st);
+        run_bwd_pre(*p, L, qk, V, O, LSE, dO, ws, st);
         return hip_status();
     }
-    const BwdArgs a = bwd_args(*p, L, ws, dQ, dK, dV);
+    const BwdArgs a = bwd_args(*p, L, qk, ws, dQ, dK, dV);
     if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, st);
     else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, st);
     return hip_status();
 }
 
 int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
-                const float* LSE, const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
-                void* stream) {
+                const float* LSE, const void* dO, void* dQ, void* dK, void* dV, const void* fwd_ws,
+                size_t fwd_ws_bytes, void* ws, size_t ws_bytes, void* stream) {
     for (int stage : {SAGEBWD_STAGE_BWD_PREPARE, SAGEBWD_STAGE_BWD_DKDV, SAGEBWD_STAGE_BWD_DQ}) {
-        const int rc = sagebwd_bwd_stage(p, stage, Q, K, V, O, LSE, dO, dQ, dK, dV, ws, ws_bytes, stream);
+        const int rc = sagebwd_bwd_stage(p, stage, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes, ws,
+                                         ws_bytes, stream);
         if (rc) return rc;
     }
     return SAGEBWD_OK;
@@ -319,10 +337,11 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
         return hip_status();
     }
-    if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, ws, ws_bytes, stream)))
+    if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, nullptr, 0, ws,
+                                ws_bytes, stream)))
         return rc;
     const Layout L = make_layout(*p, PASS_BWD);
-    BwdArgs a = bwd_args(*p, L, ws, dQ, dK, dV);
+    BwdArgs a = bwd_args(*p, L, QkSource{ws, L}, ws, dQ, dK, dV);
     a.dump = (uint8_t*)dump;
     a.dump_bh = bh;
     a.dump_i = qblock;
@@ -350,7 +369,7 @@ int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
     run_prepare_qkv(*p, L, Q, K, V, ws, true, true, true, st);
-    if (with_bwd) run_bwd_pre(*p, L, V, O, LSE, dO, ws, st);
+    if (with_bwd) run_bwd_pre(*p, L, QkSource{ws, L}, V, O, LSE, dO, ws, st);
     return hip_status();
 }
 

@@ -79,12 +79,23 @@ int sagebwd_fwd(const sagebwd_params* p,
 
 /* Backward.  Reads Q, K, V, the forward's O and LSE, and dO (all as above,
  * with the same params as the forward call); writes dQ, dK, dV
- * [B,H,N,64] bf16.  It re-quantizes Q, K, V itself (bit-identical codes to
- * the forward's). */
+ * [B,H,N,64] bf16.
+ *
+ * fwd_ws (nullable): the workspace of a completed sagebwd_fwd call with the
+ * same params and the same Q, K, V, still unmodified, and its size
+ * fwd_ws_bytes (at least sagebwd_fwd_workspace_size).  The backward then
+ * reads the forward's smoothing means, Q and K codes (both operand
+ * layouts), block scales, LSE correction and Q-smoothing bias from it
+ * instead of re-quantizing; it only reads fwd_ws.  With fwd_ws NULL it
+ * re-quantizes Q, K, V into ws.  The results are bit-identical either way
+ * (the quantization is deterministic).  The library cannot check that
+ * fwd_ws holds that forward's data; any other content gives wrong results.
+ * ws is always a backward workspace (sagebwd_bwd_workspace_size bytes). */
 int sagebwd_bwd(const sagebwd_params* p,
                 const void* Q, const void* K, const void* V,
                 const void* O, const float* LSE, const void* dO,
                 void* dQ, void* dK, void* dV,
+                const void* fwd_ws, size_t fwd_ws_bytes,
                 void* ws, size_t ws_bytes, void* stream);
 
 /* Stages.  sagebwd_fwd runs FWD_PREPARE then FWD_ATTN; sagebwd_bwd runs
@@ -94,8 +105,8 @@ int sagebwd_bwd(const sagebwd_params* p,
  * inputs and workspace), and the full sequence is exactly the pass.
  *   FWD_PREPARE  smoothing means; Q, K, V block quantization
  *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
- *   BWD_PREPARE  means and quantization again; Delta, log2 LSE, dO codes,
- *                FP16 copies of dO and V
+ *   BWD_PREPARE  (without fwd_ws) means and quantization again; then
+ *                -Delta, log2 LSE, dO codes, FP16 copies of dO and V
  *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T)
  *   BWD_DQ       dQ (INT8 QK^T and dS K; FP16 dO V^T) */
 #define SAGEBWD_STAGE_FWD_PREPARE 0
@@ -111,6 +122,7 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage,
                       const void* Q, const void* K, const void* V,
                       const void* O, const float* LSE, const void* dO,
                       void* dQ, void* dK, void* dV,
+                      const void* fwd_ws, size_t fwd_ws_bytes,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */

@@ -49,9 +49,10 @@ def call_fwd(lib, p, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, nbytes=1
     return lib.sagebwd_fwd(None if p is None else ctypes.byref(p), q, k, v, o, lse, ws, nbytes, None)
 
 
-def call_bwd(lib, p, ptrs=None, lse=FAKE, ws=FAKE, nbytes=1 << 40):
+def call_bwd(lib, p, ptrs=None, lse=FAKE, ws=FAKE, nbytes=1 << 40, fwd_ws=None, fwd_nbytes=0):
     q, k, v, o, do, dq, dk, dv = ptrs or [FAKE] * 8
-    return lib.sagebwd_bwd(None if p is None else ctypes.byref(p), q, k, v, o, lse, do, dq, dk, dv, ws, nbytes, None)
+    return lib.sagebwd_bwd(None if p is None else ctypes.byref(p), q, k, v, o, lse, do, dq, dk, dv, fwd_ws, fwd_nbytes,
+                           ws, nbytes, None)
 
 
 def test_param_validation(lib):
@@ -151,10 +152,27 @@ def test_binding_rejects_cpu_tensors():
 def test_stage_validation(lib):
     p = P()
     f = lambda stage, nb=1 << 40: lib.sagebwd_fwd_stage(ctypes.byref(p), stage, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, nb, None)
-    b = lambda stage, nb=1 << 40: lib.sagebwd_bwd_stage(ctypes.byref(p), stage, *([FAKE] * 10), nb, None)
+    b = lambda stage, nb=1 << 40: lib.sagebwd_bwd_stage(ctypes.byref(p), stage, *([FAKE] * 9), None, 0, FAKE, nb, None)
     for bad in (-1, 2, 3, 4, 5):
         assert f(bad) == INVALID
     for bad in (-1, 0, 1, 5):
         assert b(bad) == INVALID
     assert f(0, nb=1) == WORKSPACE and f(1, nb=1) == WORKSPACE
     assert b(2, nb=1) == WORKSPACE and b(3, nb=1) == WORKSPACE and b(4, nb=1) == WORKSPACE
+
+
+def test_forward_workspace_validation(lib):
+    """A reused forward workspace is checked like the backward's own: aligned,
+    large enough, and not overlapping it (every case fails before any HIP
+    call)."""
+    p = P(causal=1, smooth_q=1)
+    fsz = lib.sagebwd_fwd_workspace_size(ctypes.byref(p))
+    bsz = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
+    ws = 1 << 30
+    assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=(1 << 34) + 16, fwd_nbytes=fsz) == INVALID     # misaligned
+    assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=1 << 34, fwd_nbytes=fsz - 1) == WORKSPACE
+    assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=ws, fwd_nbytes=fsz) == INVALID                  # same buffer
+    assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=ws + bsz - 256, fwd_nbytes=fsz) == INVALID      # overlaps the end
+    assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=ws - fsz + 256, fwd_nbytes=fsz) == INVALID      # overlaps the start
+    # the forward layout holds every region the backward reads from it
+    assert fsz < bsz

@@ -100,13 +100,16 @@ def test_end_to_end_parity_and_determinism(w):
     f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
     outs = []
-    for _ in range(2):
-        o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k)
-        dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k)
+    for reuse in (False, True):
+        # second pass: the backward reuses the forward's quantized Q and K
+        ws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k), dtype=torch.uint8,
+                         device="cuda") if reuse else None
+        o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, workspace=ws)
+        dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k, fwd_workspace=ws)
         torch.cuda.synchronize()
         outs.append([G.host_bits(t) for t in (o, dq, dk, dv)] + [lse.cpu().numpy().view(np.uint32)])
     for a, b in zip(*outs):
-        assert np.array_equal(a, b)        # no atomics anywhere: bitwise repeatable
+        assert np.array_equal(a, b)        # no atomics anywhere: bitwise repeatable, with or without reuse
     o_f, lse_f = _oracle_fwd(w, f32)
     o_b = _bf16(o_f)
     ref = F.bwd(f32["q"], f32["k"], f32["v"], o_b, lse_f.astype(np.float32), f32["do"], w.causal,

@@ -1,5 +1,6 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (the whole forward and backward over every head on the GPU).
+times (the whole forward and backward over every head on the GPU, the
+backward reusing the forward's quantized Q and K).
 
 The oracle cannot afford every head of these workloads, so it is run on one
 sampled head per workload: its forward over all query rows of that head (the
@@ -41,15 +42,16 @@ def test_fullsize_sampled_parity(name, smooth_q, head):
     print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head}", flush=True)
     x = W.make_inputs(w)
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
-    o, lse = sb.fwd(tq, tk, tv, w.causal, sq, w.smooth_k)
-    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k)
+    fws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, sq, w.smooth_k), dtype=torch.uint8, device="cuda")
+    o, lse = sb.fwd(tq, tk, tv, w.causal, sq, w.smooth_k, workspace=fws)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k, fwd_workspace=fws)
     torch.cuda.synchronize()
     o_g = G.host_f32(o[b, h])
     lse_g = lse[b, h].cpu().numpy()
     dq_g, dk_g, dv_g = (G.host_f32(t[b, h]) for t in (dq, dk, dv))
     for t in (o_g, lse_g, dq_g, dk_g, dv_g):
         assert np.all(np.isfinite(t))
-    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv
+    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv, fws
 
     f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
     N, T = w.N, (w.N + 63) // 64
