@@ -37,6 +37,10 @@ with its reason, in the design notes that ship with the library):
   B3  P codes          per 64x64 tile, F3 on fp32(P) (codes in [0,127]).
   B4  dV_t += s_P s_dO,i (P_code^T dO_code_i).
   B5  dP = fp16(dO) fp16(V)^T, accumulated exactly (the one 16-bit matmul).
+      With int8_dp (the all-INT8 ablation in the SageAttention3 summary's
+      table of measured effects, which keeps this product in FP16 because
+      quantizing it costs dQ accuracy): dP = s_dO,i s_V,t (dO_code_i
+      V_code_t^T) with the F3 codes of dO and V (exact integers).
   B6  dS = P * (dP - Delta) with the unquantized P.
   B7  dS codes         per 64x64 tile, F3 on fp32(dS).
   B8  dQ_i += s_dS s_K,t (dS_code K_code_t)      (smoothed K codes, no mu_k)
@@ -354,11 +358,13 @@ class BwdPrepared:
     v16: np.ndarray      # [Np, 64]
     delta: np.ndarray    # [Np]
     lsep: np.ndarray     # [Np] LSE - corr (+inf on padded rows)
+    int8_dp: bool = False
 
 
-def prepare_bwd(pp: Prepared, v, o, lse, do) -> BwdPrepared:
+def prepare_bwd(pp: Prepared, v, o, lse, do, int8_dp: bool = False) -> BwdPrepared:
     """B1 for one head.  o: forward output values (e.g. bf16), lse: float32
-    natural-log LSE in the true-score frame, do: bf16 values."""
+    natural-log LSE in the true-score frame, do: bf16 values.  int8_dp selects
+    the all-INT8 form of B5."""
     N, T = pp.N, pp.T
     Np = T * BLK
     r = pp.rounding
@@ -377,7 +383,7 @@ def prepare_bwd(pp: Prepared, v, o, lse, do) -> BwdPrepared:
     delta[:N] = np.sum(np.asarray(do, np.float64) * np.asarray(o, np.float64), axis=1)
     lsep = np.full(Np, np.inf)
     lsep[:N] = np.asarray(lse, np.float64) - pp.corr[:N]
-    return BwdPrepared(pp, doc, sdo, do16, v16, delta, lsep)
+    return BwdPrepared(pp, doc, sdo, do16, v16, delta, lsep, int8_dp)
 
 
 def bwd_tiles(bp: BwdPrepared, iblocks, tblocks, causal: bool):
@@ -392,7 +398,11 @@ def bwd_tiles(bp: BwdPrepared, iblocks, tblocks, causal: bool):
         P = np.where(keep, np.exp(S - bp.lsep[rows][:, None]), 0.0)
     Pq = P.astype(np.float32) if r else P
     cP, sP = quantize_tiles(Pq, r)
-    dP = bp.do16[rows] @ bp.v16[cols].T
+    if bp.int8_dp:
+        w = np.asarray(bp.sdo, np.float64)[rows // BLK][:, None] * np.asarray(pp.sv, np.float64)[cols // BLK][None, :]
+        dP = w * (bp.doc[rows] @ pp.vc[cols].T)
+    else:
+        dP = bp.do16[rows] @ bp.v16[cols].T
     dS = np.where(keep, P * (dP - bp.delta[rows][:, None]), 0.0)
     dSq = dS.astype(np.float32) if r else dS
     cdS, sdS = quantize_tiles(dSq, r)
@@ -462,7 +472,7 @@ def bwd_head(bp: BwdPrepared, causal: bool, qblocks=None, kblocks=None, chunk: i
 
 
 def bwd(q, k, v, o, lse, do, causal: bool, smooth_q: bool, smooth_k: bool,
-        rounding: bool = True):
+        rounding: bool = True, int8_dp: bool = False):
     """Faithful backward over [B, H, N, 64] arrays.  ``o``/``lse`` are the
     forward outputs handed to the backward (O as bf16 values, LSE float32).
     Returns (dQ, dK, dV) float64 [B,H,N,64]."""
@@ -471,7 +481,7 @@ def bwd(q, k, v, o, lse, do, causal: bool, smooth_q: bool, smooth_k: bool,
     for b in range(B):
         for h in range(H):
             pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding)
-            bp = prepare_bwd(pp, v[b, h], o[b, h], lse[b, h], do[b, h])
+            bp = prepare_bwd(pp, v[b, h], o[b, h], lse[b, h], do[b, h], int8_dp)
             dq, dk, dv = bwd_head(bp, causal)
             out[0][b, h], out[1][b, h], out[2][b, h] = dq[:N], dk[:N], dv[:N]
     return tuple(out)

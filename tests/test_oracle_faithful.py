@@ -197,15 +197,17 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("int8_dp", [False, True], ids=["fp16dp", "int8dp"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"N{c['N']}c{int(c['causal'])}q{int(c['sq'])}k{int(c['sk'])}")
-def test_rounding_free_reduces_to_exact(case):
+def test_rounding_free_reduces_to_exact(case, int8_dp):
     w = W.custom(1, 2, case["N"], case["causal"], case["sk"], case["sq"], case["dist"], seed_family=31)
     x = {k: _f32(v).astype(np.float64) for k, v in W.make_inputs(w).items()}
     o, lse = F.fwd(x["q"], x["k"], x["v"], w.causal, w.smooth_q, w.smooth_k, rounding=False)
     oe, le = exact.fwd_bh(x["q"], x["k"], x["v"], w.causal)
     assert np.max(np.abs(o - oe)) < 1e-12
     assert np.max(np.abs(lse - le)) < 1e-11
-    g = F.bwd(x["q"], x["k"], x["v"], oe, le, x["do"], w.causal, w.smooth_q, w.smooth_k, rounding=False)
+    g = F.bwd(x["q"], x["k"], x["v"], oe, le, x["do"], w.causal, w.smooth_q, w.smooth_k, rounding=False,
+              int8_dp=int8_dp)
     ge = exact.bwd_bh(x["q"], x["k"], x["v"], x["do"], w.causal)
     for a, b in zip(g, ge):
         assert np.max(np.abs(a - b)) < 1e-11 * max(1.0, np.max(np.abs(b)))
@@ -307,3 +309,52 @@ def test_accuracy_bars(name, qb, kb):
     r = _study(name, qb, kb, [(0, 0), (0, 1)])
     assert np.all(r[:, 0] >= 0.999), r
     assert np.all(r[:, 1:] >= 0.99), r
+
+
+# ------------------------------------------------------------ all-INT8 ablation
+
+def test_int8_dp_planted_scale_mistake(monkeypatch):
+    """The all-INT8 dP uses the dO scale of the query block: reversing the dO
+    block scales after quantization breaks dQ in that mode only (the FP16 dP
+    never reads them; dQ does not depend on them otherwise)."""
+    w = W.custom(1, 1, 200, True, True, True, "kbias", seed_family=33)
+    x = {k: _f32(v).astype(np.float64) for k, v in W.make_inputs(w).items()}
+    oe, le = exact.fwd_bh(x["q"], x["k"], x["v"], True)
+    ge = exact.bwd_bh(x["q"], x["k"], x["v"], x["do"], True)
+    real = F.prepare_bwd
+
+    def reversed_sdo(*a, **k):
+        bp = real(*a, **k)
+        bp.sdo = bp.sdo[::-1].copy()
+        return bp
+
+    def dq_err(int8_dp):
+        g = F.bwd(x["q"], x["k"], x["v"], oe, le, x["do"], True, True, True, rounding=False, int8_dp=int8_dp)
+        return np.max(np.abs(g[0] - ge[0]))
+
+    assert dq_err(True) < 1e-10 and dq_err(False) < 1e-10
+    monkeypatch.setattr(F, "prepare_bwd", reversed_sdo)
+    assert dq_err(True) > 1e-3
+    assert dq_err(False) < 1e-10
+
+
+@pytest.mark.parametrize("dist,causal,sq", [("qknorm", True, False), ("kbias", True, True), ("outlier", False, True),
+                                             ("normal", False, False)])
+def test_int8_dp_ablation_ordering(dist, causal, sq):
+    """The pages' ablation (SageAttention3 summary, table of measured effects
+    and "Surprising findings"): keeping dO V^T in FP16 gives a more accurate dQ
+    than quantizing it to INT8.  On these synthetic heads the same ordering
+    holds for dQ and dK against exact attention, and dV (which does not use
+    dP) is identical in both modes."""
+    w = W.custom(1, 2, 384, causal, True, sq, dist, seed_family=77)
+    x = {k: W.bf16_bits_to_f32(v) for k, v in W.make_inputs(w).items()}
+    o, lse = F.fwd(x["q"], x["k"], x["v"], causal, sq, True)
+    ob = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o.astype(np.float32)))
+    g16 = F.bwd(x["q"], x["k"], x["v"], ob, lse.astype(np.float32), x["do"], causal, sq, True)
+    g8 = F.bwd(x["q"], x["k"], x["v"], ob, lse.astype(np.float32), x["do"], causal, sq, True, int8_dp=True)
+    ge = exact.bwd_bh(*(x[n].astype(np.float64) for n in ("q", "k", "v", "do")), causal)
+    for i in (0, 1):
+        c16, c8 = M.cos_sim(g16[i], ge[i]), M.cos_sim(g8[i], ge[i])
+        print(f"  {dist} {'dQ' if i == 0 else 'dK'} cos fp16 dP {c16:.6f}  int8 dP {c8:.6f}")
+        assert c16 > c8
+    assert np.array_equal(g16[2], g8[2])
