@@ -13,7 +13,7 @@ using namespace sagebwd;
 enum Region {
     R_MU_Q = 0, R_MU_K, R_Q_R, R_K_R, R_V_T, R_Q_T, R_K_T, R_DO_T,
     R_S_Q, R_S_K, R_S_V, R_S_DO, R_CORR, R_BIAS, R_DELTA, R_LSE2, R_DO16, R_V16,
-    R_SUMS, R_COUNT
+    R_DO_R, R_V_R, R_SUMS, R_COUNT
 };
 
 struct Layout {
@@ -58,6 +58,9 @@ Layout make_layout(const sagebwd_params& p, Pass pass) {
     sz[R_LSE2] = bwd ? BH * Np * 4 : 0;
     sz[R_DO16] = bwd ? BH * Np * HD * 2 : 0;
     sz[R_V16] = bwd ? BH * Np * HD * 2 : 0;
+    const bool i8dp = bwd && p.int8_dp;            // row-operand dO and V codes for INT8 dO V^T
+    sz[R_DO_R] = i8dp ? BH * T * 4096 : 0;
+    sz[R_V_R] = i8dp ? BH * T * 4096 : 0;
     sz[R_SUMS] = BH * 2 * nchunk * HD * 8;
     size_t o = 0;
     for (int r = 0; r < R_COUNT; ++r) {
@@ -75,7 +78,7 @@ int check_params(const sagebwd_params* p) {
     if (!p) return SAGEBWD_ERR_INVALID_ARG;
     if (p->B < 1 || p->H < 1 || p->N < 1) return SAGEBWD_ERR_INVALID_ARG;
     if ((p->causal != 0 && p->causal != 1) || (p->smooth_q != 0 && p->smooth_q != 1) ||
-        (p->smooth_k != 0 && p->smooth_k != 1))
+        (p->smooth_k != 0 && p->smooth_k != 1) || (p->int8_dp != 0 && p->int8_dp != 1))
         return SAGEBWD_ERR_INVALID_ARG;
     if (p->D != HD) return SAGEBWD_ERR_UNSUPPORTED;
     if (p->N > MAX_N || (int64_t)p->B * p->H > MAX_BH) return SAGEBWD_ERR_UNSUPPORTED;
@@ -164,6 +167,9 @@ void run_bwd_pre(const sagebwd_params& p, const Layout& L, const QkSource& qk, c
     b.sdo = region<float>(ws, L, R_S_DO);
     b.do16 = region<_Float16>(ws, L, R_DO16);
     b.v16 = region<_Float16>(ws, L, R_V16);
+    b.do_r = region<int8_t>(ws, L, R_DO_R);       // null unless int8_dp
+    b.v_r = region<int8_t>(ws, L, R_V_R);
+    b.sv = b.v_r ? region<float>(ws, L, R_S_V) : nullptr;
     b.N = p.N;
     b.T = (p.N + BLK - 1) / BLK;
     launch_bwd_pre(b, p.B * p.H, st);
@@ -198,6 +204,9 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     a.q_t = region<int8_t>(qk.ws, qk.L, R_Q_T);
     a.k_t = region<int8_t>(qk.ws, qk.L, R_K_T);
     a.do_t = region<int8_t>(ws, L, R_DO_T);
+    a.do_r = region<int8_t>(ws, L, R_DO_R);
+    a.v_r = region<int8_t>(ws, L, R_V_R);
+    a.sv = a.v_r ? region<float>(ws, L, R_S_V) : nullptr;   // written by the backward's own preparation
     a.sq = region<float>(qk.ws, qk.L, R_S_Q);
     a.sk = region<float>(qk.ws, qk.L, R_S_K);
     a.sdo = region<float>(ws, L, R_S_DO);
@@ -300,8 +309,8 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         return hip_status();
     }
     const BwdArgs a = bwd_args(*p, L, qk, ws, dQ, dK, dV);
-    if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, st);
-    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, st);
+    if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
+    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
     return hip_status();
 }
 
@@ -346,8 +355,8 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
     a.dump_bh = bh;
     a.dump_i = qblock;
     a.dump_t = kblock;
-    if (kernel == 1) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
-    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
+    if (kernel == 1) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, (hipStream_t)stream, true);
+    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, (hipStream_t)stream, true);
     return hip_status();
 }
 

@@ -32,7 +32,8 @@ struct FwdArgs {
 
 struct BwdArgs {
     const int8_t *q_r, *k_r, *q_t, *k_t, *do_t;
-    const float *sq, *sk, *sdo;        // [BH][T]
+    const int8_t *do_r, *v_r;          // row-operand dO and V codes (INT8 dO V^T only)
+    const float *sq, *sk, *sdo, *sv;   // [BH][T] (sv: INT8 dO V^T only)
     const float *bias, *delta, *lse2;  // [BH][Np]
     const _Float16 *do16, *v16;        // [BH][Np][64]
     const float* mu_q;                 // [BH][64]
@@ -43,8 +44,11 @@ struct BwdArgs {
 };
 
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
+// int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st,
+                    bool dump = false);
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st,
+                  bool dump = false);
 
 template <class T>
 __device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }

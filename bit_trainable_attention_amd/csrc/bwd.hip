@@ -137,7 +137,7 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
+template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     __shared__ DkdvSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -151,26 +151,34 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
 
-    // persistent operands of this wave's 32 keys
-    v4i kop[2] = {v4i{}, v4i{}};
+    // persistent operands of this wave's 32 keys: K codes, and V in FP16 (or,
+    // for the all-INT8 dO V^T, V codes and the V block scale)
+    v4i kop[2] = {v4i{}, v4i{}}, vop[2] = {v4i{}, v4i{}};
     v8h vh[4];
-    float kbias = 0.0f, sK = 0.0f;
+    float kbias = 0.0f, sK = 0.0f, sV = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) vh[ks] = v8h{};
     if (live) {
         const v4i* src = (const v4i*)(a.k_r + (bt + kvb) * 4096);
         kop[0] = src[(kh * 2 + 0) * 64 + lane];
         kop[1] = src[(kh * 2 + 1) * 64 + lane];
+        if (INT8DP) {
+            const v4i* vs = (const v4i*)(a.v_r + (bt + kvb) * 4096);
+            vop[0] = vs[(kh * 2 + 0) * 64 + lane];
+            vop[1] = vs[(kh * 2 + 1) * 64 + lane];
+            sV = a.sv[bt + kvb];
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) vh[ks] = *(const v8h*)(a.v16 + (rowbase + key) * HD + 16 * ks + 8 * h);
+            for (int ks = 0; ks < 4; ++ks) vh[ks] = *(const v8h*)(a.v16 + (rowbase + key) * HD + 16 * ks + 8 * h);
+        }
         if (SMOOTHQ) kbias = a.bias[rowbase + key];
         sK = a.sk[bt + kvb];
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) vh[ks] = v8h{};
     }
 
     const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
     // query block i -> LDS buffer b by DMA; LDS slot s of the FP16 dO tile
     // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
+    // (the all-INT8 dO V^T stages the dO row-operand codes there instead)
     const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
     const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
     const v4i* dtg = (const v4i*)(a.do_t + bt * 4096);
@@ -178,11 +186,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         dma16_to_lds(qrg + (size_t)i * 256 + tid, &sm.q_r[b][64 * wave]);
         dma16_to_lds(qtg + (size_t)i * 256 + tid, &sm.q_t[b][64 * wave]);
         dma16_to_lds(dtg + (size_t)i * 256 + tid, &sm.do_t[b][64 * wave]);
-        const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
+        if (INT8DP) {
+            dma16_to_lds((const v4i*)(a.do_r + bt * 4096) + (size_t)i * 256 + tid, (v4i*)sm.do16[b] + 64 * wave);
+        } else {
+            const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int s = 256 * j + tid, row = s / 8;
-            dma16_to_lds(hs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
+            for (int j = 0; j < 2; ++j) {
+                const int s = 256 * j + tid, row = s / 8;
+                dma16_to_lds(hs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
+            }
         }
         if (wave == 0 && lane < 32)
             dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
@@ -277,12 +289,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     nd[4 * r4 + 2] = d4.z;
                     nd[4 * r4 + 3] = d4.w;
                 }
-                v16f dp = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
-                dp = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dp);
-                dp = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dp);
-                dp = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dp);
+                v16f dpd;
+                if (INT8DP) {
+                    // dP - Delta = s_dO s_V (dO codes V codes^T) + (-Delta)
+                    const v4i* dor = (const v4i*)sm.do16[buf];
+                    v16i ai = mfma_i8(dor[(qb * 2 + 0) * 64 + lane], vop[0], v16i{});
+                    ai = mfma_i8(dor[(qb * 2 + 1) * 64 + lane], vop[1], ai);
+                    const float wdp = sm.qs[buf][1] * sV;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dp[r];
+                    for (int r = 0; r < 16; ++r) dpd[r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
+                } else {
+                    dpd = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
+                    dpd = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dpd);
+                    dpd = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dpd);
+                    dpd = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dpd);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpd[r];
             }
             {
                 float m0 = 0.0f, m1 = 0.0f;
@@ -380,14 +403,15 @@ struct DqSmem {
     v4i k_t[2][256];     // K transposed codes (A operand of K^T dS^T)
     v8h v16[2][512];     // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
     float bias[2][64];   // Q-smoothing key bias (log2 domain)
-    float sk[2][4];      // [0]: K block scale
+    float sk[2][4];      // [0]: K block scale, [1]: V block scale (all-INT8 dO V^T)
     float red[4];        // partial dS tile maxima, per wave
 };
 
 // dS for one 32-query x 64-key half tile in the S^T layout (lane = query,
 // registers = keys); same float32 operations as the key-block kernel.
-template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool MASK>
 __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i (&qop)[2], const v8h (&doh)[4],
+                                           const v4i (&doop)[2], float wdp,
                                            float sc, float lq, const v16f& nd, int t, int q, int N, int lane, int h,
                                            float (&ds)[2][16], uint8_t* dp = nullptr) {
     const int l32 = lane % 32;
@@ -401,10 +425,20 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
                 dump_at<int>(dp, dumpoff::A)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[r];
         }
         const int row = 32 * kb + l32;
-        v16f dp = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], nd);
-        dp = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dp);
-        dp = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dp);
-        dp = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dp);
+        v16f dpd;
+        if (INT8DP) {
+            // (dP - Delta)^T = s_dO s_V (V codes dO codes^T) + (-Delta)
+            const v4i* vr = (const v4i*)sm.v16[buf];
+            v16i ai = mfma_i8(vr[(kb * 2 + 0) * 64 + lane], doop[0], v16i{});
+            ai = mfma_i8(vr[(kb * 2 + 1) * 64 + lane], doop[1], ai);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpd[r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
+        } else {
+            dpd = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], nd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dpd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dpd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dpd);
+        }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -423,13 +457,13 @@ __device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i 
                     const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
                     if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
                 }
-                ds[kb][r] = pv * dp[r];
+                ds[kb][r] = pv * dpd[r];
             }
         }
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
+template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool DUMP>
 __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -444,38 +478,52 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
 
-    v4i qop[2] = {v4i{}, v4i{}};
+    // persistent operands of this wave's 32 queries: Q codes, and dO in FP16
+    // (or, for the all-INT8 dO V^T, dO codes and the dO block scale)
+    v4i qop[2] = {v4i{}, v4i{}}, doop[2] = {v4i{}, v4i{}};
     v8h doh[4];
-    float lq = 0.0f, dlq = 0.0f, sQ = 0.0f;
+    float lq = 0.0f, dlq = 0.0f, sQ = 0.0f, sDO = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) doh[ks] = v8h{};
     if (live) {
         const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
         qop[0] = src[(qh * 2 + 0) * 64 + lane];
         qop[1] = src[(qh * 2 + 1) * 64 + lane];
+        if (INT8DP) {
+            const v4i* ds = (const v4i*)(a.do_r + (bt + qblk) * 4096);
+            doop[0] = ds[(qh * 2 + 0) * 64 + lane];
+            doop[1] = ds[(qh * 2 + 1) * 64 + lane];
+            sDO = a.sdo[bt + qblk];
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) doh[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+            for (int ks = 0; ks < 4; ++ks) doh[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+        }
         lq = a.lse2[rowbase + q];
         dlq = a.delta[rowbase + q];
         sQ = a.sq[bt + qblk];
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) doh[ks] = v8h{};
     }
 
     const v4i* krg = (const v4i*)(a.k_r + bt * 4096);
     const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
     // key block t -> LDS buffer b by DMA; LDS slot s of the FP16 V tile
     // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
+    // (the all-INT8 dO V^T stages the V row-operand codes there instead, and
+    // the V block scale next to the K block scale)
     auto fetch = [&](int t, int b) {
         dma16_to_lds(krg + (size_t)t * 256 + tid, &sm.k_r[b][64 * wave]);
         dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.k_t[b][64 * wave]);
-        const v4i* vs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
+        if (INT8DP) {
+            dma16_to_lds((const v4i*)(a.v_r + bt * 4096) + (size_t)t * 256 + tid, (v4i*)sm.v16[b] + 64 * wave);
+        } else {
+            const v4i* vs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int s = 256 * j + tid, row = s / 8;
-            dma16_to_lds(vs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+            for (int j = 0; j < 2; ++j) {
+                const int s = 256 * j + tid, row = s / 8;
+                dma16_to_lds(vs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+            }
         }
         if (SMOOTHQ && wave == 0 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
-        if (wave == 1 && lane == 0) dma4_to_lds(a.sk + bt + t, &sm.sk[b][0]);
+        if (wave == 1 && lane < (INT8DP ? 2 : 1)) dma4_to_lds((lane == 0 ? a.sk : a.sv) + bt + t, &sm.sk[b][0]);
     };
 
     v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
@@ -496,8 +544,13 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
         uint8_t* dp = (DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t) ? a.dump : nullptr;
         if (active) {
             const float sc = tile_scale(sQ, sK);
-            if (masked) dq_dscores<CAUSAL, SMOOTHQ, true>(sm, buf, qop, doh, sc, lq, nd, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
-            else dq_dscores<CAUSAL, SMOOTHQ, false>(sm, buf, qop, doh, sc, lq, nd, t, q, a.N, lane, h, ds, DUMP ? dp : nullptr);
+            const float wdp = INT8DP ? sDO * sm.sk[buf][1] : 0.0f;   // s_dO s_V, as in the key-block kernel
+            if (masked)
+                dq_dscores<CAUSAL, SMOOTHQ, INT8DP, true>(sm, buf, qop, doh, doop, wdp, sc, lq, nd, t, q, a.N, lane, h,
+                                                          ds, DUMP ? dp : nullptr);
+            else
+                dq_dscores<CAUSAL, SMOOTHQ, INT8DP, false>(sm, buf, qop, doh, doop, wdp, sc, lq, nd, t, q, a.N, lane,
+                                                           h, ds, DUMP ? dp : nullptr);
             if (DUMP && dp) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -571,32 +624,34 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     }
 }
 
-#define SAGEBWD_LAUNCH_BWD(KERNEL)                                                                 \
-    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);                                              \
-    if (causal) {                                                                                  \
-        if (smooth_q) {                                                                            \
-            if (dump) hipLaunchKernelGGL((KERNEL<true, true, true>), grid, block, 0, st, a);       \
-            else hipLaunchKernelGGL((KERNEL<true, true, false>), grid, block, 0, st, a);           \
-        } else {                                                                                   \
-            if (dump) hipLaunchKernelGGL((KERNEL<true, false, true>), grid, block, 0, st, a);      \
-            else hipLaunchKernelGGL((KERNEL<true, false, false>), grid, block, 0, st, a);          \
-        }                                                                                          \
-    } else {                                                                                       \
-        if (smooth_q) {                                                                            \
-            if (dump) hipLaunchKernelGGL((KERNEL<false, true, true>), grid, block, 0, st, a);      \
-            else hipLaunchKernelGGL((KERNEL<false, true, false>), grid, block, 0, st, a);          \
-        } else {                                                                                   \
-            if (dump) hipLaunchKernelGGL((KERNEL<false, false, true>), grid, block, 0, st, a);     \
-            else hipLaunchKernelGGL((KERNEL<false, false, false>), grid, block, 0, st, a);         \
-        }                                                                                          \
-    }                                                                                              \
+// Instantiation by (causal, Q-smoothing, all-INT8 dO V^T, tile dump).
+#define SAGEBWD_LAUNCH_BWD(KERNEL)                                                                   \
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);                                                \
+    switch ((causal ? 8 : 0) | (smooth_q ? 4 : 0) | (int8_dp ? 2 : 0) | (dump ? 1 : 0)) {            \
+        case 0: hipLaunchKernelGGL((KERNEL<false, false, false, false>), grid, block, 0, st, a); break; \
+        case 1: hipLaunchKernelGGL((KERNEL<false, false, false, true>), grid, block, 0, st, a); break;  \
+        case 2: hipLaunchKernelGGL((KERNEL<false, false, true, false>), grid, block, 0, st, a); break;  \
+        case 3: hipLaunchKernelGGL((KERNEL<false, false, true, true>), grid, block, 0, st, a); break;   \
+        case 4: hipLaunchKernelGGL((KERNEL<false, true, false, false>), grid, block, 0, st, a); break;  \
+        case 5: hipLaunchKernelGGL((KERNEL<false, true, false, true>), grid, block, 0, st, a); break;   \
+        case 6: hipLaunchKernelGGL((KERNEL<false, true, true, false>), grid, block, 0, st, a); break;   \
+        case 7: hipLaunchKernelGGL((KERNEL<false, true, true, true>), grid, block, 0, st, a); break;    \
+        case 8: hipLaunchKernelGGL((KERNEL<true, false, false, false>), grid, block, 0, st, a); break;  \
+        case 9: hipLaunchKernelGGL((KERNEL<true, false, false, true>), grid, block, 0, st, a); break;   \
+        case 10: hipLaunchKernelGGL((KERNEL<true, false, true, false>), grid, block, 0, st, a); break;  \
+        case 11: hipLaunchKernelGGL((KERNEL<true, false, true, true>), grid, block, 0, st, a); break;   \
+        case 12: hipLaunchKernelGGL((KERNEL<true, true, false, false>), grid, block, 0, st, a); break;  \
+        case 13: hipLaunchKernelGGL((KERNEL<true, true, false, true>), grid, block, 0, st, a); break;   \
+        case 14: hipLaunchKernelGGL((KERNEL<true, true, true, false>), grid, block, 0, st, a); break;   \
+        default: hipLaunchKernelGGL((KERNEL<true, true, true, true>), grid, block, 0, st, a); break;    \
+    }                                                                                                \
     return 0;
 
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st, bool dump) {
     SAGEBWD_LAUNCH_BWD(k_bwd_dkdv)
 }
 
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st, bool dump) {
     SAGEBWD_LAUNCH_BWD(k_bwd_dq)
 }
 #undef SAGEBWD_LAUNCH_BWD

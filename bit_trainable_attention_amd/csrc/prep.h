@@ -33,6 +33,8 @@ struct BwdPreArgs {
     float *delta, *lse2;               // [BH][Np]: -rowsum(dO*O), log2-domain LSE
     int8_t* do_t;                      // transposed operand layout
     float* sdo;                        // [BH][T]
+    int8_t *do_r, *v_r;                // row-operand dO and V codes, or null (INT8 dO V^T only)
+    float* sv;                         // [BH][T] V block scales, with v_r
     _Float16 *do16, *v16;              // [BH][Np][64]
     int N, T;
 };

@@ -174,7 +174,9 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
 // One workgroup per 64-token block: -Delta = -rowsum(dO*O) (fp32), the
 // log2-domain LSE of the smoothed scores, dO codes (transposed operand
 // layout) and scale, FP16 copies of dO and V.  Rows past N are zeroed (their
-// LSE is +inf so every P of such a row is 0).
+// LSE is +inf so every P of such a row is 0).  For the all-INT8 ablation also
+// the dO codes in the row-operand layout and the V codes (the same quantizer
+// as the forward's, V not centred) with their block scales.
 __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     const int t = blockIdx.x, bh = blockIdx.y;
     const int r = threadIdx.x / 4, g = threadIdx.x % 4;
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
     const uint32_t ow[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
     const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float delta = 0.0f, amax = 0.0f;
+    float delta = 0.0f, amax = 0.0f, vmax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         dov[2 * j] = bf16_to_f32(dw[j] & 0xFFFFu);
@@ -208,6 +210,7 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     for (int j = 0; j < 16; ++j) {
         delta = __builtin_fmaf(dov[j], ov[j], delta);
         amax = fmaxf(amax, fabsf(dov[j]));
+        vmax = fmaxf(vmax, fabsf(vv[j]));
     }
     delta += __shfl_xor(delta, 1, 64);
     delta += __shfl_xor(delta, 2, 64);
@@ -241,10 +244,26 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     block_scale(a_blk, s, inv);
     const size_t blk = (size_t)bh * a.T + t;
     if (threadIdx.x == 0) a.sdo[blk] = s;
+    uint32_t cw[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) codes[r][16 * g + j] = (int8_t)code_int(dov[j], inv);
+    for (int j = 0; j < 16; ++j) {
+        const int cq = code_int(dov[j], inv);
+        codes[r][16 * g + j] = (int8_t)cq;
+        cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
+    }
+    if (a.do_r) *(uint4*)(a.do_r + blk * 4096 + row_operand_offset(r, 16 * g)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     __syncthreads();
     store_transposed(codes, a.do_t + blk * 4096);
+    if (a.v_r) {
+        __shared__ float red_v[4];
+        float sv, invv;
+        block_scale(block_absmax_256(vmax, red_v), sv, invv);
+        if (threadIdx.x == 0) a.sv[blk] = sv;
+        uint32_t vw4[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) vw4[j / 4] |= (uint32_t)(uint8_t)code_int(vv[j], invv) << (8 * (j % 4));
+        *(uint4*)(a.v_r + blk * 4096 + row_operand_offset(r, 16 * g)) = make_uint4(vw4[0], vw4[1], vw4[2], vw4[3]);
+    }
 }
 
 // ---------------------------------------------------------------- launchers

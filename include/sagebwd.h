@@ -58,6 +58,11 @@ typedef struct sagebwd_params {
     int32_t causal;     /* 0 or 1 */
     int32_t smooth_q;   /* 0 or 1: subtract the per-head token mean of Q */
     int32_t smooth_k;   /* 0 or 1: subtract the per-head token mean of K */
+    int32_t int8_dp;    /* 0 or 1: backward only.  1 = the all-INT8 ablation of the
+                           SageAttention3 summary's table of measured effects:
+                           dO V^T also from per-block INT8 codes of dO and V
+                           (i32 accumulation, scaled by s_dO s_V) instead of
+                           FP16.  0 (the method) keeps it in FP16. */
 } sagebwd_params;
 
 #define SAGEBWD_OK               0
@@ -107,6 +112,7 @@ int sagebwd_bwd(const sagebwd_params* p,
  *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
  *   BWD_PREPARE  (without fwd_ws) means and quantization again; then
  *                -Delta, log2 LSE, dO codes, FP16 copies of dO and V
+ *                (int8_dp: also row-layout dO codes, V codes and scales)
  *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T)
  *   BWD_DQ       dQ (INT8 QK^T and dS K; FP16 dO V^T) */
 #define SAGEBWD_STAGE_FWD_PREPARE 0
@@ -153,7 +159,9 @@ const char* sagebwd_status_string(int status);
  *   15 LSE2   float32 [BH][Np]       (LSE - CORR) * log2(e); +inf past N
  *   16 DO16   fp16 [BH][Np][64]      dO in FP16, natural layout
  *   17 V16    fp16 [BH][Np][64]      V in FP16, natural layout
- * with T = ceil(N/64), Np = 64 T.  Within a 4096-byte block of 64 tokens x
+ *   18 DO_R   int8  [BH][T][4096]    dO codes, row operand layout (int8_dp only)
+ *   19 V_R    int8  [BH][T][4096]    V codes, row operand layout (int8_dp only)
+ * with T = ceil(N/64), Np = 64 T.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
  * 64 channels, element (token r, channel c) sits at byte
  *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16
  *   transposed operand:  ((c/32*2 + r/32)*64 + 32*((r%8)/4) + c%32)*16

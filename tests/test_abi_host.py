@@ -37,9 +37,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def P(**kw):
-    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64)
+    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0)
     d.update(kw)
-    return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"])
+    return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"], d["int8_dp"])
 
 
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -63,6 +63,8 @@ def test_param_validation(lib):
     assert call_fwd(lib, P(causal=2)) == INVALID
     assert call_fwd(lib, P(smooth_q=-1)) == INVALID
     assert call_fwd(lib, P(smooth_k=7)) == INVALID
+    assert call_fwd(lib, P(int8_dp=2)) == INVALID
+    assert call_bwd(lib, P(int8_dp=-1)) == INVALID
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED
     assert call_fwd(lib, P(N=(1 << 20) + 1)) == UNSUPPORTED
     assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED
@@ -110,29 +112,32 @@ def test_prepare_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, 10) == WORKSPACE
 
 
-def test_ws_regions_layout(lib):
+@pytest.mark.parametrize("int8_dp", [0, 1])
+def test_ws_regions_layout(lib, int8_dp):
     for N in (1, 63, 64, 65, 1000, 17776):
-        p = P(B=2, H=3, N=N)
+        p = P(B=2, H=3, N=N, int8_dp=int8_dp)
         BH, T = 6, (N + 63) // 64
         Np = 64 * T
         expect = {"MU_Q": BH * 256, "MU_K": BH * 256, "Q_R": BH * T * 4096, "K_R": BH * T * 4096,
                   "V_T": BH * T * 4096, "Q_T": BH * T * 4096, "K_T": BH * T * 4096, "DO_T": BH * T * 4096,
                   "S_Q": BH * T * 4, "S_K": BH * T * 4, "S_V": BH * T * 4, "S_DO": BH * T * 4,
                   "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "NDELTA": BH * Np * 4, "LSE2": BH * Np * 4,
-                  "DO16": BH * Np * 128, "V16": BH * Np * 128}
+                  "DO16": BH * Np * 128, "V16": BH * Np * 128,
+                  "DO_R": int8_dp * BH * T * 4096, "V_R": int8_dp * BH * T * 4096}
         spans = []
         for name, rid in sb.REGIONS.items():
             off, nb = sb.ws_region(p, rid)
             assert off % 256 == 0
             assert nb == expect[name], (name, nb)
-            spans.append((off, off + nb))
+            if nb:
+                spans.append((off, off + nb))
         spans.sort()
         for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
             assert a1 <= b0
         total = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
         assert spans[-1][1] <= total
     off, nb = ctypes.c_size_t(), ctypes.c_size_t()
-    assert lib.sagebwd_ws_region(ctypes.byref(P()), 18, ctypes.byref(off), ctypes.byref(nb)) == INVALID
+    assert lib.sagebwd_ws_region(ctypes.byref(P()), len(sb.REGIONS), ctypes.byref(off), ctypes.byref(nb)) == INVALID
     assert lib.sagebwd_ws_region(ctypes.byref(P()), -1, ctypes.byref(off), ctypes.byref(nb)) == INVALID
 
 

@@ -93,6 +93,31 @@ def test_backward_parity(w):
             assert np.linalg.norm(a) <= 1e-2 * max(np.linalg.norm(g[2]), 1e-30), name
 
 
+@pytest.mark.parametrize("w", SMALL, ids=_ids(SMALL))
+def test_backward_parity_int8_dp(w):
+    """The all-INT8 ablation (dO V^T from INT8 codes): the backward against the
+    oracle's int8_dp mode, same bars as the method's FP16 dO V^T."""
+    print(f"[bwd int8_dp] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    o_f, lse_f = _oracle_fwd(w, f32)
+    o_bits = W.f32_to_bf16_bits(o_f.astype(np.float32))
+    lse32 = lse_f.astype(np.float32)
+    dq, dk, dv = sb.bwd(G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]), G.dev(o_bits), torch.from_numpy(lse32).cuda(),
+                        G.dev(x["do"]), w.causal, w.smooth_q, w.smooth_k, int8_dp=True)
+    torch.cuda.synchronize()
+    g = [G.host_f32(t) for t in (dq, dk, dv)]
+    ref = F.bwd(f32["q"], f32["k"], f32["v"], W.bf16_bits_to_f32(o_bits), lse32, f32["do"], w.causal,
+                w.smooth_q, w.smooth_k, int8_dp=True)
+    ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal)
+    for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
+        assert np.all(np.isfinite(a)), name
+        print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
+        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
+        if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+
+
 @pytest.mark.parametrize("w", SMALL[:4], ids=_ids(SMALL[:4]))
 def test_end_to_end_parity_and_determinism(w):
     print(f"[e2e] {w.name}", flush=True)

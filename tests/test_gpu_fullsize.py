@@ -20,12 +20,13 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    ("tiny", None, (0, 1)),
-    ("pretrain", None, (7, 15)),
-    ("llama8k", None, (0, 17)),
-    ("llama16k", None, (0, 29)),
-    ("video", None, (1, 3)),
-    ("video", False, (0, 11)),          # the same layer with Q-smoothing off
+    ("tiny", None, (0, 1), False),
+    ("pretrain", None, (7, 15), False),
+    ("llama8k", None, (0, 17), False),
+    ("llama16k", None, (0, 29), False),
+    ("video", None, (1, 3), False),
+    ("video", False, (0, 11), False),   # the same layer with Q-smoothing off
+    ("llama8k", None, (0, 17), True),   # the all-INT8 dO V^T ablation, same head as above
 ]
 
 
@@ -33,18 +34,20 @@ def _blocks(T):
     return sorted({0, T // 2, T - 1})
 
 
-@pytest.mark.parametrize("name,smooth_q,head", CASES,
-                         ids=[f"{c[0]}{'' if c[1] is None else '_q' + str(int(c[1]))}" for c in CASES])
-def test_fullsize_sampled_parity(name, smooth_q, head):
+@pytest.mark.parametrize("name,smooth_q,head,int8_dp", CASES,
+                         ids=[f"{c[0]}{'' if c[1] is None else '_q' + str(int(c[1]))}{'_int8dp' if c[3] else ''}"
+                              for c in CASES])
+def test_fullsize_sampled_parity(name, smooth_q, head, int8_dp):
     w = W.WORKLOADS[name]
     sq = w.smooth_q if smooth_q is None else smooth_q
     b, h = head
-    print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head}", flush=True)
+    print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head} int8_dp={int8_dp}",
+          flush=True)
     x = W.make_inputs(w)
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
     fws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, sq, w.smooth_k), dtype=torch.uint8, device="cuda")
     o, lse = sb.fwd(tq, tk, tv, w.causal, sq, w.smooth_k, workspace=fws)
-    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k, fwd_workspace=fws)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k, fwd_workspace=fws, int8_dp=int8_dp)
     torch.cuda.synchronize()
     o_g = G.host_f32(o[b, h])
     lse_g = lse[b, h].cpu().numpy()
@@ -65,7 +68,7 @@ def test_fullsize_sampled_parity(name, smooth_q, head):
     assert np.max(np.abs(lse_g - lse_f)) <= 2e-3
     # end to end: the oracle's backward takes the oracle's O (bf16) and LSE
     o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
-    bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"])
+    bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"], int8_dp)
     dq_f, dk_f, dv_f = F.bwd_head(bp, w.causal, blocks, blocks)
     sel = np.concatenate([np.arange(j * 64, j * 64 + min(64, N - i * 64)) for j, i in enumerate(blocks)])
     errs = {"dQ": M.rel_l2(dq_g[rows], dq_f[sel]), "dK": M.rel_l2(dk_g[rows], dk_f[sel]),

@@ -26,8 +26,9 @@ CASES = [
 ]
 
 
-def _run(w, heads):
-    print(f"[prepare] {w.name} B{w.B} H{w.H} N{w.N} causal={w.causal} sq={w.smooth_q} sk={w.smooth_k}", flush=True)
+def _run(w, heads, int8_dp=False):
+    print(f"[prepare] {w.name} B{w.B} H{w.H} N{w.N} causal={w.causal} sq={w.smooth_q} sk={w.smooth_k} "
+          f"int8_dp={int8_dp}", flush=True)
     x = W.make_inputs(w)
     r = np.random.default_rng(5)
     o_bits = W.f32_to_bf16_bits(r.standard_normal(x["q"].shape).astype(np.float32))
@@ -35,10 +36,10 @@ def _run(w, heads):
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
     to = G.dev(o_bits)
     tlse = torch.from_numpy(lse).cuda()
-    ws = sb.prepare(tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k)
+    ws = sb.prepare(tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp)
     torch.cuda.synchronize()
     wsh = ws.cpu().numpy()
-    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k)
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp)
     BH, T = w.B * w.H, (w.N + 63) // 64
     Np = 64 * T
     got = {
@@ -56,6 +57,9 @@ def _run(w, heads):
         "do16": G.region(wsh, p, "DO16", np.float16).reshape(BH, Np, 64),
         "v16": G.region(wsh, p, "V16", np.float16).reshape(BH, Np, 64),
     }
+    if int8_dp:   # row-operand dO and V codes of the all-INT8 dO V^T
+        got["do_r"] = G.decode_codes(wsh, p, "DO_R", "row", BH, T)
+        got["v_r"] = G.decode_codes(wsh, p, "V_R", "row", BH, T)
     if heads is None:
         heads = [(b, h) for b in range(w.B) for h in range(w.H)]
     f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
@@ -71,7 +75,7 @@ def _run(w, heads):
         assert np.array_equal(got["mu_q"][i].view(np.uint32), np.asarray(pp.mu_q, np.float32).view(np.uint32))
         assert np.array_equal(got["mu_k"][i].view(np.uint32), np.asarray(pp.mu_k, np.float32).view(np.uint32))
         for name, ref in (("q_r", pp.qc), ("q_t", pp.qc), ("k_r", pp.kc), ("k_t", pp.kc), ("v_t", pp.vc),
-                          ("do_t", bp.doc)):
+                          ("do_t", bp.doc)) + ((("do_r", bp.doc), ("v_r", pp.vc)) if int8_dp else ()):
             assert np.array_equal(got[name][i].astype(np.int64), ref.astype(np.int64)), name
         for name, ref in (("sq", pp.sq), ("sk", pp.sk), ("sv", pp.sv), ("sdo", bp.sdo)):
             assert np.array_equal(got[name][i].view(np.uint32), np.asarray(ref, np.float32).view(np.uint32)), name
@@ -97,6 +101,15 @@ def _run(w, heads):
 def test_prepare_bitexact(name, w, heads):
     G.assert_perms_are_bijections()
     _run(w if w is not None else W.WORKLOADS[name], heads)
+
+
+@pytest.mark.parametrize("name,w,heads", [c for c in CASES if c[0] in ("ragged_outlier", "one_token", "llama8k")],
+                         ids=["ragged_outlier", "one_token", "llama8k"])
+def test_prepare_bitexact_int8_dp(name, w, heads):
+    """The all-INT8 dO V^T preparation: dO and V codes in the row-operand
+    layout and the V block scales, bit-exact (the V scales come from the
+    backward's own preparation and must equal the forward quantizer's)."""
+    _run(w if w is not None else W.WORKLOADS[name], heads, int8_dp=True)
 
 
 def test_prepare_zero_inputs():

@@ -30,11 +30,15 @@ pytestmark = pytest.mark.gpu
 A, F1, C1, ACC1, F2, C2, ACC2, SC = 0, 16384, 32768, 36864, 53248, 69632, 73728, 90112
 
 CASES = [
-    ("tiny", W.WORKLOADS["tiny"], 1, [(0, 0), (1, 1), (0, 1), (1, 0)]),
-    ("ragged_causal", W.custom(1, 2, 200, True, True, True, "kbias", 71), 1, [(3, 3), (3, 0), (2, 1)]),
-    ("pretrain", W.WORKLOADS["pretrain"], 100, [(5, 5), (31, 0), (17, 16)]),
-    ("video", W.WORKLOADS["video"], 33, [(277, 277), (0, 277), (277, 0), (150, 3)]),
-    ("llama16k", W.WORKLOADS["llama16k"], 5, [(255, 255), (255, 0), (100, 99)]),
+    ("tiny", W.WORKLOADS["tiny"], 1, [(0, 0), (1, 1), (0, 1), (1, 0)], False),
+    ("ragged_causal", W.custom(1, 2, 200, True, True, True, "kbias", 71), 1, [(3, 3), (3, 0), (2, 1)], False),
+    ("pretrain", W.WORKLOADS["pretrain"], 100, [(5, 5), (31, 0), (17, 16)], False),
+    ("video", W.WORKLOADS["video"], 33, [(277, 277), (0, 277), (277, 0), (150, 3)], False),
+    ("llama16k", W.WORKLOADS["llama16k"], 5, [(255, 255), (255, 0), (100, 99)], False),
+    # the all-INT8 ablation: dO V^T from INT8 codes (the dS tile must still be
+    # bitwise the same in both backward kernels)
+    ("ragged_causal_int8dp", W.custom(1, 2, 200, True, True, True, "kbias", 71), 1, [(3, 3), (3, 0), (2, 1)], True),
+    ("video_int8dp", W.WORKLOADS["video"], 33, [(277, 277), (150, 3)], True),
 ]
 
 
@@ -42,8 +46,8 @@ def _blk(d, off, dtype):
     return np.frombuffer(d, dtype=dtype, count=4096, offset=off).reshape(64, 64)
 
 
-@pytest.mark.parametrize("name,w,bh,tiles", CASES, ids=[c[0] for c in CASES])
-def test_tile_replay_bitexact(name, w, bh, tiles):
+@pytest.mark.parametrize("name,w,bh,tiles,int8_dp", CASES, ids=[c[0] for c in CASES])
+def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
     print(f"[replay] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} head {bh} tiles {tiles}", flush=True)
     b, h = divmod(bh, w.H)
     x = W.make_inputs(w)
@@ -61,7 +65,7 @@ def test_tile_replay_bitexact(name, w, bh, tiles):
     to = G.dev(W.f32_to_bf16_bits(o_all))
     tlse = torch.from_numpy(lse_all).cuda()
     o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_all[b, h]))
-    bp = F.prepare_bwd(pp, f["v"], o_b, lse_all[b, h], f["do"])
+    bp = F.prepare_bwd(pp, f["v"], o_b, lse_all[b, h], f["do"], int8_dp)
     fresh_total, fresh_diff = 0, 0
     for (i, t) in tiles:
         rows = slice(64 * i, 64 * i + 64)
@@ -78,7 +82,8 @@ def test_tile_replay_bitexact(name, w, bh, tiles):
         assert np.array_equal(_blk(d, ACC1, np.int32).astype(np.int64),
                               (codes.astype(np.float64) @ pp.vc[cols]).astype(np.int64)), ("fwd PV", i, t)
         # ---- dK/dV kernel
-        d1 = sb.debug_tile("dkdv", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k).numpy().tobytes()
+        d1 = sb.debug_tile("dkdv", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
+                           int8_dp).numpy().tobytes()
         assert np.array_equal(_blk(d1, A, np.int32), a_ref.astype(np.int32)), ("dkdv A", i, t)
         P = _blk(d1, F1, np.float32)
         sP, invP = F.block_scale(np.max(np.abs(P)))
@@ -96,7 +101,8 @@ def test_tile_replay_bitexact(name, w, bh, tiles):
         assert np.array_equal(_blk(d1, ACC2, np.int32).astype(np.int64),
                               (cdS.T @ pp.qc[rows]).astype(np.int64)), ("dS^T Q", i, t)
         # ---- dQ kernel: the same dS tile, bit for bit
-        d2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k).numpy().tobytes()
+        d2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
+                           int8_dp).numpy().tobytes()
         assert np.array_equal(_blk(d2, A, np.int32), a_ref.astype(np.int32)), ("dq A", i, t)
         assert np.array_equal(_blk(d2, F1, np.float32).view(np.uint32), dS.view(np.uint32)), ("dq dS bits", i, t)
         assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32)
