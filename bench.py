@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--workload", default="llama16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--int8-dp", action="store_true",
+                    help="time the all-INT8 ablation (dO V^T from INT8 codes) instead of the method's FP16 dO V^T")
     ap.add_argument("--no-reuse", action="store_true",
                     help="let the backward re-quantize Q and K instead of reading the forward's workspace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -129,7 +131,7 @@ def main():
 
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     del x
-    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k)
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp)
     lib = sb.load_library()
     import ctypes
     ws_f = torch.empty(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
@@ -179,7 +181,7 @@ def main():
     dom = max(KERNEL_UNITS, key=lambda s: stage_ms[s])
     ach = KERNEL_UNITS[dom] * unit / (stage_ms[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": load_traffic(dom, w.name),
+            "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None if args.int8_dp else load_traffic(dom, w.name),
             "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {
         "metric": METRIC,
@@ -192,11 +194,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8 (dO.V^T f16)",
+        "dtype": "i8" if args.int8_dp else "i8 (dO.V^T f16)",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
-                   "bwd_reuses_fwd_quantization": not args.no_reuse},
+                   "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp)},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
         "roofline": roof,
