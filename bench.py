@@ -200,6 +200,9 @@ def main():
                    "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
                    "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp)},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
+        # 12 of the 14 N^2 d units are INT8 and 2 (dO V^T, fwd-side none) FP16 at half the INT8 rate,
+        # so the MFMA floor of the mix is 14/16 of the INT8 peak
+        "frac_blended_mfma_peak": round(tops / (INT8_PEAK_TOPS * 14.0 / 16.0), 4),
         "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
         "roofline": roof,
     }
