@@ -89,7 +89,7 @@ def test_quantizer_matches_exact_rationals():
     r127 = _f32_round(Fraction(1, 127))
     r = np.random.default_rng(7)
     n_checked = 0
-    for trial in range(400):
+    for trial in range(2000):
         scale = float(np.exp(r.uniform(-12, 6)))
         x = (r.standard_normal(512) * scale).astype(np.float32)
         a = np.max(np.abs(x))
@@ -104,7 +104,7 @@ def test_quantizer_matches_exact_rationals():
         for xi, ci in zip(x.tolist(), codes.tolist()):
             assert ci == max(-127, min(127, _rne(Fraction(xi) * inv_ref)))
             n_checked += 1
-    assert n_checked == 400 * 512
+    assert n_checked == 2000 * 512        # 1 024 000 values
 
 
 def test_quantizer_hand_cases():
