@@ -11,12 +11,38 @@ on"):
     dV = P^T dO,  dP = dO V^T,  Delta_i = sum_c dO_ic O_ic,
     dS = P * (dP - Delta),  dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
 
+With ``qk_norm`` the attention runs on QK-normalized queries and keys (the
+SageBwd abstract, insight (i), calls QK-norm necessary for stable training at
+many tokens per step): every token row of Q and of K is divided by its root
+mean square, x_n = x / sqrt(mean_c x^2 + 1e-6) (unit gain), and the gradients
+are carried back through it: with r = 1/sqrt(mean_c x^2 + 1e-6),
+dx = r (dx_n - x_n mean_c(dx_n x_n)).
+
 All functions take one head: arrays of shape [N, d], any float dtype (cast to
 float64).  ``*_bh`` wrappers loop over [B, H, N, d].
 """
 from __future__ import annotations
 
 import numpy as np
+
+
+QK_NORM_EPS = 1e-6
+
+
+def qk_norm(x):
+    """Row-wise QK-norm of one head: (x_n, r) with r = 1/sqrt(mean_c x^2 + eps)
+    and x_n = x r."""
+    x = np.asarray(x, np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + QK_NORM_EPS)
+    return x * r[:, None], r
+
+
+def qk_norm_bwd(dxn, xn, r):
+    """Gradient through qk_norm: dx = r (dx_n - x_n mean_c(dx_n x_n)).  From
+    dx_n_i/dx_j = r delta_ij - r^3 x_i x_j / d."""
+    dxn = np.asarray(dxn, np.float64)
+    xn = np.asarray(xn, np.float64)
+    return np.asarray(r, np.float64)[:, None] * (dxn - xn * np.mean(dxn * xn, axis=1, keepdims=True))
 
 
 def _mask(nq: int, nk: int, causal: bool) -> np.ndarray:
@@ -37,8 +63,10 @@ def scores(q, k, causal: bool, scale: float | None = None) -> np.ndarray:
     return np.where(_mask(q.shape[0], k.shape[0], causal), s, -np.inf)
 
 
-def fwd(q, k, v, causal: bool):
+def fwd(q, k, v, causal: bool, qk_norm: bool = False):
     """Return (O [N,d], LSE [N]) in float64 (dense softmax)."""
+    if qk_norm:
+        q, k = globals()["qk_norm"](q)[0], globals()["qk_norm"](k)[0]
     s = scores(q, k, causal)
     m = np.max(s, axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -90,9 +118,14 @@ def fwd_online(q, k, v, causal: bool, block: int = 16):
     return o, lse
 
 
-def bwd(q, k, v, do, causal: bool, o=None):
+def bwd(q, k, v, do, causal: bool, o=None, qk_norm: bool = False):
     """Return (dQ, dK, dV) in float64.  ``o`` (if given) is the forward output
     used for Delta = rowsum(dO * O); by default the exact forward output."""
+    if qk_norm:
+        qn, rq = globals()["qk_norm"](q)
+        kn, rk = globals()["qk_norm"](k)
+        dqn, dkn, dv = bwd(qn, kn, v, do, causal, o)
+        return qk_norm_bwd(dqn, qn, rq), qk_norm_bwd(dkn, kn, rk), dv
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -122,10 +155,16 @@ def dscores(q, k, v, do, causal: bool):
     return p * (dp - delta)
 
 
-def sampled(q, k, v, do, causal: bool, qrows, krows, chunk: int = 512):
+def sampled(q, k, v, do, causal: bool, qrows, krows, chunk: int = 512, qk_norm: bool = False):
     """The same quantities as ``fwd``/``bwd`` for long sequences, for a sample
     of query rows (O, LSE, dQ) and key rows (dK, dV), in row chunks so that the
     N x N matrices are never held at once.  Delta uses the exact O."""
+    if qk_norm:
+        qn, rq = globals()["qk_norm"](q)
+        kn, rk = globals()["qk_norm"](k)
+        o_s, lse_s, dq_s, dk_s, dv_s = sampled(qn, kn, v, do, causal, qrows, krows, chunk)
+        qrows, krows = np.asarray(qrows), np.asarray(krows)
+        return (o_s, lse_s, qk_norm_bwd(dq_s, qn[qrows], rq[qrows]), qk_norm_bwd(dk_s, kn[krows], rk[krows]), dv_s)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -168,22 +207,22 @@ def sampled(q, k, v, do, causal: bool, qrows, krows, chunk: int = 512):
     return o_s, lse_s, dq_s, dk_s, dv_s
 
 
-def fwd_bh(q, k, v, causal: bool):
+def fwd_bh(q, k, v, causal: bool, qk_norm: bool = False):
     B, H, N, d = q.shape
     o = np.zeros((B, H, N, d))
     lse = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = fwd(q[b, h], k[b, h], v[b, h], causal)
+            o[b, h], lse[b, h] = fwd(q[b, h], k[b, h], v[b, h], causal, qk_norm)
     return o, lse
 
 
-def bwd_bh(q, k, v, do, causal: bool, o=None):
+def bwd_bh(q, k, v, do, causal: bool, o=None, qk_norm: bool = False):
     B, H, N, d = q.shape
     out = [np.zeros((B, H, N, d)) for _ in range(3)]
     for b in range(B):
         for h in range(H):
-            r = bwd(q[b, h], k[b, h], v[b, h], do[b, h], causal, None if o is None else o[b, h])
+            r = bwd(q[b, h], k[b, h], v[b, h], do[b, h], causal, None if o is None else o[b, h], qk_norm)
             for x, y in zip(out, r):
                 x[b, h] = y
     return tuple(out)

@@ -7,6 +7,11 @@ the quantization granularity nor the arithmetic of the quantizers, so this
 module writes out one precise reading of every step (each reading is listed,
 with its reason, in the design notes that ship with the library):
 
+  F0  QK-norm (option; SageBwd abstract, insight (i): necessary for stable
+      training at many tokens per step): per token row of Q and of K,
+      r = fp32(1 / sqrt(exact_sum(x^2) / 64 + 1e-6)) (float64 steps), and the
+      normalized row x_n = bf16(fp32(x r)), the tensor a separate norm would
+      hand to attention; every later step reads x_n in place of x.
   F1  smoothing means  mu = fp32( exact_sum(x over the N valid tokens) / N )
       per (batch, head, channel), for K when smooth_k and for Q when smooth_q
       (SageBwd abstract, insight (iv): K-smoothing, optional Q-smoothing).
@@ -46,6 +51,8 @@ with its reason, in the design notes that ship with the library):
   B8  dQ_i += s_dS s_K,t (dS_code K_code_t)      (smoothed K codes, no mu_k)
   B9  dK_t += s_dS s_Q,i (dS_code^T Q_code_i) + [smooth_q] s_dS colsum(dS_code) mu_q
   B10 dQ, dK scaled by 1/8 = 1/sqrt(64).
+  B11 with F0: the gradient through the norm, dx = r (dx_n - x_n mean_c(dx_n x_n))
+      with the x_n and r of F0.
 
 With ``rounding=False`` every rounding step is removed (codes are x~/s
 unrounded, no float32 or float16 rounding, P~/P/dS unquantized); the result
@@ -68,6 +75,39 @@ SCALE = 1.0 / 8.0        # 1/sqrt(64), exact
 A_MIN = 2.0 ** -100      # absmax below this -> an all-zero block
 _F127 = np.float32(127.0)
 _R127 = np.float32(1.0) / _F127          # correctly rounded float32 of 1/127
+
+
+# ---------------------------------------------------------------- F0
+
+QK_NORM_EPS = 1e-6
+
+
+def bf16_rne(x) -> np.ndarray:
+    """Round float32 values to bfloat16 (round half to even); float32 result."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def qk_norm_rows(x, rounding: bool = True):
+    """F0 for one head: (x_n, r).  The sum of squares is exact (fsum of exact
+    float64 squares of the bf16 inputs); r = 1/sqrt(sum/64 + 1e-6) in float64
+    rounded once to float32; x_n = bf16(fp32(x * r)).  Without rounding:
+    x_n = x r in float64."""
+    x64 = np.asarray(x, np.float64)
+    ss = np.array([math.fsum((row * row).tolist()) for row in x64])
+    r64 = 1.0 / np.sqrt(ss / 64.0 + QK_NORM_EPS)
+    if not rounding:
+        return x64 * r64[:, None], r64
+    r = r64.astype(np.float32)
+    return bf16_rne(np.asarray(x, np.float32) * r[:, None]), r
+
+
+def qk_norm_grad(dxn, xn, r) -> np.ndarray:
+    """B11: dx = r (dx_n - x_n mean_c(dx_n x_n)), rows of one head."""
+    dxn = np.asarray(dxn, np.float64)
+    xn = np.asarray(xn, np.float64)
+    return np.asarray(r, np.float64)[:, None] * (dxn - xn * np.mean(dxn * xn, axis=1, keepdims=True))
 
 
 # ---------------------------------------------------------------- F1, F3
@@ -174,15 +214,23 @@ class Prepared:
     sv: np.ndarray
     b: np.ndarray        # [Np] per-key bias (F4), 0 for padded keys
     corr: np.ndarray     # [Np] (q_raw . mu_k) / 8, 0 for padded rows
-    q_raw: np.ndarray    # [N, 64] float64 input values
+    q_raw: np.ndarray    # [N, 64] float64 query values the scores use (x_n with F0)
     rounding: bool
+    k_in: np.ndarray = None   # [N, 64] float64 key values the scores use (x_n with F0)
+    rq: np.ndarray = None     # [N] F0 factors (None without QK-norm)
+    rk: np.ndarray = None
 
 
-def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True) -> Prepared:
-    """F1-F4 for one head.  q, k, v: [N, 64] arrays holding bf16 values."""
-    q = np.asarray(q, np.float32)
-    k = np.asarray(k, np.float32)
-    v = np.asarray(v, np.float32)
+def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_norm: bool = False) -> Prepared:
+    """F0-F4 for one head.  q, k, v: [N, 64] arrays holding bf16 values."""
+    dt = np.float32 if rounding else np.float64
+    rq = rk = None
+    if qk_norm:
+        q, rq = qk_norm_rows(q, rounding)
+        k, rk = qk_norm_rows(k, rounding)
+    q = np.asarray(q, dt)
+    k = np.asarray(k, dt)
+    v = np.asarray(v, dt)
     N = q.shape[0]
     T = (N + BLK - 1) // BLK
     Np = T * BLK
@@ -212,7 +260,7 @@ def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True) -> P
     corr = np.zeros(Np)
     corr[:N] = (np.asarray(q, np.float64) @ np.asarray(mu_k, np.float64)) * SCALE
     return Prepared(N, T, mu_q, mu_k, qc, kc, vc, sq, sk, sv, b, corr,
-                    np.asarray(q, np.float64), rounding)
+                    np.asarray(q, np.float64), rounding, np.asarray(k, np.float64), rq, rk)
 
 
 def _score_block(pp: Prepared, rows: np.ndarray, cols: np.ndarray, causal: bool):
@@ -333,7 +381,7 @@ def fwd_head_loop(pp: Prepared, causal: bool, reading: str = "B"):
 
 
 def fwd(q, k, v, causal: bool, smooth_q: bool, smooth_k: bool, rounding: bool = True,
-        reading: str = "B"):
+        reading: str = "B", qk_norm: bool = False):
     """Faithful forward over [B, H, N, 64] arrays of bf16 values.
     Returns (O float64 [B,H,N,64], LSE float64 [B,H,N])."""
     B, H, N, _ = q.shape
@@ -341,7 +389,7 @@ def fwd(q, k, v, causal: bool, smooth_q: bool, smooth_k: bool, rounding: bool = 
     lse = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
-            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding)
+            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding, qk_norm)
             ob, lb = fwd_head(pp, causal, reading=reading)
             o[b, h], lse[b, h] = ob[:N], lb[:N]
     return o, lse
@@ -471,17 +519,29 @@ def bwd_head(bp: BwdPrepared, causal: bool, qblocks=None, kblocks=None, chunk: i
     return dq, dk, dv
 
 
+def norm_grads(pp: Prepared, dq, dk, qrows=None, krows=None):
+    """B11 applied to dQ rows ``qrows`` and dK rows ``krows`` (default: the
+    first len(dq) / len(dk) tokens); identity without F0."""
+    if pp.rq is None:
+        return dq, dk
+    qrows = np.arange(len(dq)) if qrows is None else np.asarray(qrows)
+    krows = np.arange(len(dk)) if krows is None else np.asarray(krows)
+    return (qk_norm_grad(dq, pp.q_raw[qrows], pp.rq[qrows]), qk_norm_grad(dk, pp.k_in[krows], pp.rk[krows]))
+
+
 def bwd(q, k, v, o, lse, do, causal: bool, smooth_q: bool, smooth_k: bool,
-        rounding: bool = True, int8_dp: bool = False):
+        rounding: bool = True, int8_dp: bool = False, qk_norm: bool = False):
     """Faithful backward over [B, H, N, 64] arrays.  ``o``/``lse`` are the
     forward outputs handed to the backward (O as bf16 values, LSE float32).
-    Returns (dQ, dK, dV) float64 [B,H,N,64]."""
+    Returns (dQ, dK, dV) float64 [B,H,N,64], the gradients of the raw Q, K
+    (through the norm with qk_norm) and V."""
     B, H, N, _ = q.shape
     out = [np.zeros((B, H, N, D)) for _ in range(3)]
     for b in range(B):
         for h in range(H):
-            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding)
+            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding, qk_norm)
             bp = prepare_bwd(pp, v[b, h], o[b, h], lse[b, h], do[b, h], int8_dp)
             dq, dk, dv = bwd_head(bp, causal)
-            out[0][b, h], out[1][b, h], out[2][b, h] = dq[:N], dk[:N], dv[:N]
+            dq, dk = norm_grads(pp, dq[:N], dk[:N])
+            out[0][b, h], out[1][b, h], out[2][b, h] = dq, dk, dv[:N]
     return tuple(out)

@@ -47,16 +47,21 @@ def test_closed_forms(causal):
         assert abs(lse[0] - q[0] @ k[0] / np.sqrt(d)) < 1e-13
 
 
+@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n,d", [(5, 4), (8, 8), (13, 4)])
-def test_finite_differences(causal, n, d):
-    """Central differences of L = sum(dO * O) against the analytic backward."""
+def test_finite_differences(causal, n, d, qk_norm):
+    """Central differences of L = sum(dO * O) against the analytic backward
+    (with QK-norm: through the row normalization of Q and K)."""
     q, k, v, do = _rand(n, d, 100 + n + d)
-    dq, dk, dv = exact.bwd(q, k, v, do, causal)
+    if qk_norm:   # rows of different sizes, so the norm is not a no-op
+        q = q * np.linspace(0.3, 3.0, n)[:, None]
+        k = k * np.linspace(2.0, 0.5, n)[:, None]
+    dq, dk, dv = exact.bwd(q, k, v, do, causal, qk_norm=qk_norm)
     h = 1e-6
 
     def loss(q_, k_, v_):
-        return float(np.sum(do * exact.fwd(q_, k_, v_, causal)[0]))
+        return float(np.sum(do * exact.fwd(q_, k_, v_, causal, qk_norm)[0]))
 
     for which, grad in ((0, dq), (1, dk), (2, dv)):
         num = np.zeros((n, d))
@@ -116,6 +121,58 @@ def test_sampled_matches_dense(causal):
     qr = np.array([0, 5, 299, 150])
     kr = np.array([1, 2, 250, 299])
     os_, ls, dq, dk, dv = exact.sampled(q, k, v, do, causal, qr, kr, chunk=64)
+    assert np.max(np.abs(os_ - o[qr])) < 1e-13
+    assert np.max(np.abs(ls - lse[qr])) < 1e-13
+    assert np.max(np.abs(dq - g[0][qr])) < 1e-13
+    assert np.max(np.abs(dk - g[1][kr])) < 1e-13
+    assert np.max(np.abs(dv - g[2][kr])) < 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_qk_norm_matches_torch_autograd(causal):
+    """QK-norm forward and its gradient against torch autograd of the same
+    composition written directly (row RMS norm, eps 1e-6, then attention)."""
+    n, d = 40, 64
+    q, k, v, do = _rand(n, d, 23)
+    q = q * np.linspace(0.2, 4.0, n)[:, None]
+    o, _ = exact.fwd(q, k, v, causal, qk_norm=True)
+    dq, dk, dv = exact.bwd(q, k, v, do, causal, qk_norm=True)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    nq = tq / torch.sqrt((tq * tq).mean(dim=1, keepdim=True) + 1e-6)
+    nk = tk / torch.sqrt((tk * tk).mean(dim=1, keepdim=True) + 1e-6)
+    to = torch.nn.functional.scaled_dot_product_attention(nq[None, None], nk[None, None], tv[None, None],
+                                                          is_causal=causal)[0, 0]
+    to.backward(torch.tensor(do))
+    assert np.max(np.abs(o - to.detach().numpy())) < 1e-12
+    for a, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.max(np.abs(a - t.grad.numpy())) < 1e-11
+
+
+def test_qk_norm_radial_gradient_and_scale_invariance():
+    """Scaling a row of Q or K leaves the normalized row unchanged (up to the
+    1e-6 epsilon), so O barely moves and the gradient has no component along
+    the row itself: |sum_c dQ_ic Q_ic| is at the epsilon level."""
+    n, d = 30, 64
+    q, k, v, do = _rand(n, d, 24)
+    o1, _ = exact.fwd(q, k, v, True, qk_norm=True)
+    c = np.linspace(0.5, 5.0, n)[:, None]
+    o2, _ = exact.fwd(q * c, k / c, v, True, qk_norm=True)
+    assert np.max(np.abs(o1 - o2)) < 1e-5
+    dq, dk, _ = exact.bwd(q, k, v, do, True, qk_norm=True)
+    for g, x in ((dq, q), (dk, k)):
+        radial = np.abs(np.sum(g * x, axis=1))
+        assert np.all(radial <= 1e-5 * np.linalg.norm(g, axis=1) * np.linalg.norm(x, axis=1) + 1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_matches_dense_qk_norm(causal):
+    q, k, v, do = _rand(300, 64, 42)
+    q = q * np.linspace(0.5, 2.0, 300)[:, None]
+    o, lse = exact.fwd(q, k, v, causal, qk_norm=True)
+    g = exact.bwd(q, k, v, do, causal, qk_norm=True)
+    qr = np.array([0, 5, 299, 150])
+    kr = np.array([1, 2, 250, 299])
+    os_, ls, dq, dk, dv = exact.sampled(q, k, v, do, causal, qr, kr, chunk=64, qk_norm=True)
     assert np.max(np.abs(os_ - o[qr])) < 1e-13
     assert np.max(np.abs(ls - lse[qr])) < 1e-13
     assert np.max(np.abs(dq - g[0][qr])) < 1e-13

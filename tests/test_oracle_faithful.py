@@ -2,6 +2,7 @@
 integer products, an exact-rational re-derivation of the quantizer, hand-derived
 quantizer cases, the rounding-free reduction to exact attention, a literal
 online tile loop, and the exactness of the smoothing-mean sums."""
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -358,3 +359,79 @@ def test_int8_dp_ablation_ordering(dist, causal, sq):
         print(f"  {dist} {'dQ' if i == 0 else 'dK'} cos fp16 dP {c16:.6f}  int8 dP {c8:.6f}")
         assert c16 > c8
     assert np.array_equal(g16[2], g8[2])
+
+
+# ------------------------------------------------------------ QK-norm (F0, B11)
+
+def _qk_rows(n, seed, scale_lo=0.05, scale_hi=20.0):
+    """bf16 rows of very different sizes, so the norm is far from a no-op."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((n, 64)) * np.exp(r.uniform(np.log(scale_lo), np.log(scale_hi), n))[:, None]
+    return F.bf16_rne(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("causal,sq,sk", [(True, True, True), (False, False, True), (True, False, False)])
+def test_rounding_free_reduces_to_exact_qk_norm(causal, sq, sk):
+    """F0 and B11 without rounding: faithful = exact attention on QK-normalized
+    inputs, gradients carried back through the norm."""
+    n = 150
+    q, k = _qk_rows(n, 61)[None, None], _qk_rows(n, 62)[None, None]
+    r = np.random.default_rng(63)
+    v, do = (F.bf16_rne(r.standard_normal((1, 1, n, 64)).astype(np.float32)) for _ in range(2))
+    x = {"q": q.astype(np.float64), "k": k.astype(np.float64), "v": v.astype(np.float64), "do": do.astype(np.float64)}
+    o, lse = F.fwd(x["q"], x["k"], x["v"], causal, sq, sk, rounding=False, qk_norm=True)
+    oe, le = exact.fwd_bh(x["q"], x["k"], x["v"], causal, qk_norm=True)
+    assert np.max(np.abs(o - oe)) < 1e-12 and np.max(np.abs(lse - le)) < 1e-11
+    g = F.bwd(x["q"], x["k"], x["v"], oe, le, x["do"], causal, sq, sk, rounding=False, qk_norm=True)
+    ge = exact.bwd_bh(x["q"], x["k"], x["v"], x["do"], causal, qk_norm=True)
+    for a, b in zip(g, ge):
+        assert np.max(np.abs(a - b)) < 1e-11 * max(1.0, np.max(np.abs(b)))
+
+
+def test_qk_norm_step_against_high_precision():
+    """F0 with rounding: r is within one float32 ulp of 1/sqrt(mean x^2 + 1e-6)
+    computed with 50 significant digits; x_n is within half a bf16 ulp (plus
+    the float32 product's error) of x r; normalized rows have mean square 1 to
+    bf16 precision; and the float64 sum of squares is order-free on these
+    rows (the GPU forms it in another order)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    x = _qk_rows(500, 64, 1e-3, 1e3)
+    xn, r = F.qk_norm_rows(x)
+    for i in range(x.shape[0]):
+        row = [Decimal(float(t)) for t in x[i]]
+        ref = 1 / (sum(t * t for t in row) / 64 + Decimal("0.000001")).sqrt()
+        rf = float(ref)
+        assert abs(float(r[i]) - rf) <= np.spacing(np.float32(rf))
+        assert np.sum(x[i].astype(np.float64) ** 2) == math.fsum((x[i].astype(np.float64) ** 2).tolist())
+    exact_xn = x.astype(np.float64) * r.astype(np.float64)[:, None]
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact_xn), 1e-30))) - 7)
+    assert np.all(np.abs(xn - exact_xn) <= 0.5 * ulp * (1 + 2 ** -16))
+    ms = np.mean(xn.astype(np.float64) ** 2, axis=1)
+    m = np.mean(x.astype(np.float64) ** 2, axis=1)
+    assert np.all(np.abs(ms - m / (m + 1e-6)) < 2 ** -6)      # 1 unless the row is as small as eps
+
+
+def test_qk_norm_planted_mistakes(monkeypatch):
+    """A wrong epsilon in F0 or a sign slip in B11 breaks the rounding-free
+    reduction."""
+    n = 96
+    q, k = _qk_rows(n, 65, 1e-3, 1e-1)[None, None], _qk_rows(n, 66)[None, None]   # tiny rows: eps matters
+    r = np.random.default_rng(67)
+    v, do = (r.standard_normal((1, 1, n, 64)) for _ in range(2))
+    x = {"q": q.astype(np.float64), "k": k.astype(np.float64), "v": v, "do": do}
+    oe, le = exact.fwd_bh(x["q"], x["k"], x["v"], True, qk_norm=True)
+    ge = exact.bwd_bh(x["q"], x["k"], x["v"], x["do"], True, qk_norm=True)
+
+    def err():
+        o, _ = F.fwd(x["q"], x["k"], x["v"], True, True, True, rounding=False, qk_norm=True)
+        g = F.bwd(x["q"], x["k"], x["v"], oe, le, x["do"], True, True, True, rounding=False, qk_norm=True)
+        return max(np.max(np.abs(o - oe)), max(np.max(np.abs(a - b)) / np.max(np.abs(b)) for a, b in zip(g, ge)))
+
+    assert err() < 1e-10
+    monkeypatch.setattr(F, "QK_NORM_EPS", 1e-5)
+    assert err() > 1e-6
+    monkeypatch.setattr(F, "QK_NORM_EPS", 1e-6)
+    monkeypatch.setattr(F, "qk_norm_grad", lambda dxn, xn, rr: np.asarray(rr, np.float64)[:, None] * (
+        dxn + xn * np.mean(dxn * xn, axis=1, keepdims=True)))      # + where the gradient has -
+    assert err() > 1e-3
