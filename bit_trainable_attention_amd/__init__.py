@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libsagebwd.so")
 
 REGIONS = {"MU_Q": 0, "MU_K": 1, "Q_R": 2, "K_R": 3, "V_T": 4, "Q_T": 5, "K_T": 6, "DO_T": 7,
            "S_Q": 8, "S_K": 9, "S_V": 10, "S_DO": 11, "CORR": 12, "BIAS": 13, "NDELTA": 14,
-           "LSE2": 15, "DO16": 16, "V16": 17, "DO_R": 18, "V_R": 19}
+           "LSE2": 15, "DO16": 16, "V16": 17, "DO_R": 18, "V_R": 19, "RQ": 20, "RK": 21}
 
 
 STAGES = {"FWD_PREPARE": 0, "FWD_ATTN": 1, "BWD_PREPARE": 2, "BWD_DKDV": 3, "BWD_DQ": 4}
@@ -40,7 +40,7 @@ class SageBwdError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32), ("smooth_k", ctypes.c_int32),
-                ("int8_dp", ctypes.c_int32)]
+                ("int8_dp", ctypes.c_int32), ("qk_norm", ctypes.c_int32)]
 
 
 _lib = None
@@ -82,10 +82,11 @@ def load_library() -> ctypes.CDLL:
     return _lib
 
 
-def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False) -> Params:
-    """int8_dp: the all-INT8 ablation (dO V^T from INT8 codes); backward only."""
+def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False, qk_norm=False) -> Params:
+    """int8_dp: the all-INT8 ablation (dO V^T from INT8 codes); backward only.
+    qk_norm: QK-norm fused in (same value for forward and backward)."""
     return Params(int(B), int(H), int(N), int(D), int(bool(causal)), int(bool(smooth_q)), int(bool(smooth_k)),
-                  int(bool(int8_dp)))
+                  int(bool(int8_dp)), int(bool(qk_norm)))
 
 
 def _check(rc: int, what: str):
@@ -111,8 +112,9 @@ def _check_qkv(*ts):
             raise SageBwdError(f"shape mismatch: {tuple(t.shape)} vs {tuple(ref.shape)}")
 
 
-def workspace_size(B, H, N, causal=False, smooth_q=False, smooth_k=True, backward=False, int8_dp=False) -> int:
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp)
+def workspace_size(B, H, N, causal=False, smooth_q=False, smooth_k=True, backward=False, int8_dp=False,
+                   qk_norm=False) -> int:
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp, qk_norm=qk_norm)
     lib = load_library()
     n = (lib.sagebwd_bwd_workspace_size if backward else lib.sagebwd_fwd_workspace_size)(ctypes.byref(p))
     if n == 0:
@@ -128,13 +130,13 @@ def _workspace(nbytes, device, ws=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None):
+def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None, qk_norm=False):
     """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N]).  Pass a
     forward-sized uint8 ``workspace`` to keep the quantized Q and K for a
     backward that reuses them (``bwd(..., fwd_workspace=workspace)``)."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, qk_norm=qk_norm)
     lib = load_library()
     ws = _workspace(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     if out is None:
@@ -149,7 +151,7 @@ def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, ou
 
 
 def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None,
-        fwd_workspace=None, int8_dp=False):
+        fwd_workspace=None, int8_dp=False, qk_norm=False):
     """Backward.  Returns (dQ, dK, dV) bf16 [B,H,N,64].  ``fwd_workspace``:
     the workspace of the forward call on the same q, k, v and flags, whose
     quantized Q and K are then reused (bit-identical results).  ``int8_dp``:
@@ -158,7 +160,7 @@ def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, worksp
     if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3]):
         raise SageBwdError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
     lib = load_library()
     ws = _workspace(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     if out is None:
@@ -193,12 +195,13 @@ def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params, fwd_ws
     _check(rc, f"sagebwd_bwd_stage({stage})")
 
 
-def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True, int8_dp=False):
+def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True, int8_dp=False,
+            qk_norm=False):
     """Run only the preparation kernels into a fresh backward-sized workspace
     (uint8 tensor) for inspection; see ws_region for the layout."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
     lib = load_library()
     nbytes = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
@@ -213,14 +216,14 @@ DEBUG_KERNELS = {"fwd": 0, "dkdv": 1, "dq": 2}
 
 
 def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=False, smooth_q=False,
-               smooth_k=True, int8_dp=False):
+               smooth_k=True, int8_dp=False, qk_norm=False):
     """Run one attention kernel's debug instantiation and return the raw
     SAGEBWD_DUMP_BYTES dump of tile (bh, qblock, kblock) as a CPU uint8
     tensor (see include/sagebwd.h for the layout).  kernel: "fwd" writes into
     o and lse; "dkdv" and "dq" read o, lse and do."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
     lib = load_library()
     ws = torch.empty(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=q.device)
     dump = torch.zeros(DUMP_BYTES, dtype=torch.uint8, device=q.device)
@@ -248,17 +251,19 @@ class SageBwdAttention(torch.autograd.Function):
     backward reuses the forward's quantized Q and K (its workspace is kept)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True):
+    def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True, qk_norm=False):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         B, H, N, D = q.shape
-        ws = torch.empty(workspace_size(B, H, N, causal, smooth_q, smooth_k), dtype=torch.uint8, device=q.device)
-        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k, workspace=ws)
+        ws = torch.empty(workspace_size(B, H, N, causal, smooth_q, smooth_k, qk_norm=qk_norm), dtype=torch.uint8,
+                         device=q.device)
+        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k, workspace=ws, qk_norm=qk_norm)
         ctx.save_for_backward(q, k, v, o, lse, ws)
         ctx.flags = (causal, smooth_q, smooth_k)
+        ctx.qk_norm = qk_norm
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, ws = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags, fwd_workspace=ws)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags, fwd_workspace=ws, qk_norm=ctx.qk_norm)
+        return dq, dk, dv, None, None, None, None

@@ -13,7 +13,7 @@ using namespace sagebwd;
 enum Region {
     R_MU_Q = 0, R_MU_K, R_Q_R, R_K_R, R_V_T, R_Q_T, R_K_T, R_DO_T,
     R_S_Q, R_S_K, R_S_V, R_S_DO, R_CORR, R_BIAS, R_DELTA, R_LSE2, R_DO16, R_V16,
-    R_DO_R, R_V_R, R_SUMS, R_COUNT
+    R_DO_R, R_V_R, R_RQ, R_RK, R_SUMS, R_COUNT
 };
 
 struct Layout {
@@ -61,6 +61,8 @@ Layout make_layout(const sagebwd_params& p, Pass pass) {
     const bool i8dp = bwd && p.int8_dp;            // row-operand dO and V codes for INT8 dO V^T
     sz[R_DO_R] = i8dp ? BH * T * 4096 : 0;
     sz[R_V_R] = i8dp ? BH * T * 4096 : 0;
+    sz[R_RQ] = p.qk_norm ? BH * Np * 4 : 0;         // QK-norm factors of Q and K tokens
+    sz[R_RK] = p.qk_norm ? BH * Np * 4 : 0;
     sz[R_SUMS] = BH * 2 * nchunk * HD * 8;
     size_t o = 0;
     for (int r = 0; r < R_COUNT; ++r) {
@@ -78,7 +80,8 @@ int check_params(const sagebwd_params* p) {
     if (!p) return SAGEBWD_ERR_INVALID_ARG;
     if (p->B < 1 || p->H < 1 || p->N < 1) return SAGEBWD_ERR_INVALID_ARG;
     if ((p->causal != 0 && p->causal != 1) || (p->smooth_q != 0 && p->smooth_q != 1) ||
-        (p->smooth_k != 0 && p->smooth_k != 1) || (p->int8_dp != 0 && p->int8_dp != 1))
+        (p->smooth_k != 0 && p->smooth_k != 1) || (p->int8_dp != 0 && p->int8_dp != 1) ||
+        (p->qk_norm != 0 && p->qk_norm != 1))
         return SAGEBWD_ERR_INVALID_ARG;
     if (p->D != HD) return SAGEBWD_ERR_UNSUPPORTED;
     if (p->N > MAX_N || (int64_t)p->B * p->H > MAX_BH) return SAGEBWD_ERR_UNSUPPORTED;
@@ -109,9 +112,14 @@ void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, co
                      void* ws, bool want_row, bool want_vt, bool want_qkt, hipStream_t st) {
     const int BH = p.B * p.H;
     const int T = (p.N + BLK - 1) / BLK;
+    float* rq = region<float>(ws, L, R_RQ);     // null without QK-norm
+    float* rk = region<float>(ws, L, R_RK);
+    if (rq) launch_rownorm((const uint16_t*)Q, (const uint16_t*)K, rq, rk, p.N, T, BH, st);
     MeansArgs m{};
     m.q = (const uint16_t*)Q;
     m.k = (const uint16_t*)K;
+    m.rq = rq;
+    m.rk = rk;
     m.sums = region<double>(ws, L, R_SUMS);
     m.mu_q = region<float>(ws, L, R_MU_Q);
     m.mu_k = region<float>(ws, L, R_MU_K);
@@ -125,6 +133,8 @@ void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, co
     a.q = (const uint16_t*)Q;
     a.k = (const uint16_t*)K;
     a.v = (const uint16_t*)V;
+    a.rq = rq;
+    a.rk = rk;
     a.mu_q = m.mu_q;
     a.mu_k = m.mu_k;
     a.q_r = want_row ? region<int8_t>(ws, L, R_Q_R) : nullptr;
@@ -196,9 +206,11 @@ FwdArgs fwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* O, fl
     return a;
 }
 
-BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, void* ws, void* dQ, void* dK,
-                 void* dV) {
+BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, void* ws, const void* Q,
+                 const void* K, void* dQ, void* dK, void* dV) {
     BwdArgs a{};
+    a.q_in = (const uint16_t*)Q;
+    a.k_in = (const uint16_t*)K;
     a.q_r = region<int8_t>(qk.ws, qk.L, R_Q_R);
     a.k_r = region<int8_t>(qk.ws, qk.L, R_K_R);
     a.q_t = region<int8_t>(qk.ws, qk.L, R_Q_T);
@@ -216,6 +228,8 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     a.do16 = region<_Float16>(ws, L, R_DO16);
     a.v16 = region<_Float16>(ws, L, R_V16);
     a.mu_q = region<float>(qk.ws, qk.L, R_MU_Q);
+    a.rq = region<float>(qk.ws, qk.L, R_RQ);
+    a.rk = region<float>(qk.ws, qk.L, R_RK);
     a.dq = (uint16_t*)dQ;
     a.dk = (uint16_t*)dK;
     a.dv = (uint16_t*)dV;
@@ -308,7 +322,7 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         run_bwd_pre(*p, L, qk, V, O, LSE, dO, ws, st);
         return hip_status();
     }
-    const BwdArgs a = bwd_args(*p, L, qk, ws, dQ, dK, dV);
+    const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
     if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
     else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
     return hip_status();
@@ -350,7 +364,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
                                 ws_bytes, stream)))
         return rc;
     const Layout L = make_layout(*p, PASS_BWD);
-    BwdArgs a = bwd_args(*p, L, QkSource{ws, L}, ws, dQ, dK, dV);
+    BwdArgs a = bwd_args(*p, L, QkSource{ws, L}, ws, Q, K, dQ, dK, dV);
     a.dump = (uint8_t*)dump;
     a.dump_bh = bh;
     a.dump_i = qblock;

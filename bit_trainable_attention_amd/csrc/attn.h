@@ -37,6 +37,8 @@ struct BwdArgs {
     const float *bias, *delta, *lse2;  // [BH][Np]
     const _Float16 *do16, *v16;        // [BH][Np][64]
     const float* mu_q;                 // [BH][64]
+    const uint16_t *q_in, *k_in;       // bf16 Q, K as passed in [BH][N][64] (QK-norm gradient)
+    const float *rq, *rk;              // QK-norm factors [BH][Np], or null (no QK-norm)
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
     uint8_t* dump;                     // tile dump (debug instantiation only)

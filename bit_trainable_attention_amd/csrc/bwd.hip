@@ -36,6 +36,24 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 32 lanes of this lane's half of the wave (its pair of 16-lane
+// rows), returned in each of them with the same bits: DPP within each row,
+// then the row pair through v_permlane16_swap (both lanes add the two row
+// sums in the same order).
+__device__ __forceinline__ float half_sum32(float v) {
+    v += dppf<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dppf<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dppf<0x141>(v);   // row_half_mirror
+    v += dppf<0x140>(v);   // row_mirror
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // Maximum over the 64 lanes of a wave of non-negative floats, returned in
 // every lane.  Non-negative floats order like their bit patterns, so the
 // reduction runs on unsigned integers: DPP within each 16-lane row, then the
@@ -380,16 +398,37 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-        const int d = 32 * db + l32;
-        const float muq = SMOOTHQ ? a.mu_q[(size_t)bh * HD + d] : 0.0f;
+        const float muq = SMOOTHQ ? a.mu_q[(size_t)bh * HD + 32 * db + l32] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int kr = 8 * (r / 4) + 4 * h + (r % 4);
-            const int kk = kvb * BLK + 32 * kh + kr;
-            const float gk = SMOOTHQ ? __shfl(gfull, kr, 64) : 0.0f;
+            const float gk = SMOOTHQ ? __shfl(gfull, 8 * (r / 4) + 4 * h + (r % 4), 64) : 0.0f;
+            dk[db][r] = (SMOOTHQ ? __builtin_fmaf(gk, muq, dk[db][r]) : dk[db][r]) * 0.125f;
+        }
+    }
+    if (a.rk) {
+        // QK-norm: dK = r (dK_n - K_n mean_c(dK_n K_n)).  A key's 64 channels
+        // are two registers in each of the 32 lanes of this half.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kvb * BLK + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4);
+            const bool ok = kk < a.N;
+            const float rr = ok ? a.rk[rowbase + kk] : 0.0f;
+            const uint16_t* krow = a.k_in + ((size_t)bh * a.N + (ok ? kk : 0)) * HD;
+            const float kn0 = ok ? qk_normed(krow[l32], rr) : 0.0f;
+            const float kn1 = ok ? qk_normed(krow[32 + l32], rr) : 0.0f;
+            const float mean = half_sum32(__builtin_fmaf(dk[1][r], kn1, dk[0][r] * kn0)) * (1.0f / HD);
+            dk[0][r] = rr * __builtin_fmaf(-kn0, mean, dk[0][r]);
+            dk[1][r] = rr * __builtin_fmaf(-kn1, mean, dk[1][r]);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        const int d = 32 * db + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kvb * BLK + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4);
             if (kk < a.N) {
-                const float dkv = (SMOOTHQ ? __builtin_fmaf(gk, muq, dk[db][r]) : dk[db][r]) * 0.125f;
-                a.dk[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dkv);
+                a.dk[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dk[db][r]);
                 a.dv[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dv[db][r]);
             }
         }
@@ -608,17 +647,46 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
         __syncthreads();
     }
 
-    if (live && q < a.N) {
+    // dQ (x 1/8); with QK-norm then dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
+    // other 32 channels of this lane's query being in the other half of the wave
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[db][r] *= 0.125f;
+    const bool qok = live && q < a.N;
+    if (a.rq) {
+        const float rr = qok ? a.rq[rowbase + q] : 0.0f;
+        const uint16_t* qrow = a.q_in + ((size_t)bh * a.N + (qok ? q : 0)) * HD;
+        float qn[2][16];
+        float part = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const uint2 u = qok ? *(const uint2*)(qrow + 32 * db + 8 * r4 + 4 * h) : make_uint2(0, 0);
+                qn[db][4 * r4 + 0] = qk_normed(u.x & 0xFFFFu, rr);
+                qn[db][4 * r4 + 1] = qk_normed(u.x >> 16, rr);
+                qn[db][4 * r4 + 2] = qk_normed(u.y & 0xFFFFu, rr);
+                qn[db][4 * r4 + 3] = qk_normed(u.y >> 16, rr);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part = __builtin_fmaf(dq[db][4 * r4 + j], qn[db][4 * r4 + j], part);
+            }
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        const float mean = (__uint_as_float(s[0]) + __uint_as_float(s[1])) * (1.0f / HD);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[db][r] = rr * __builtin_fmaf(-qn[db][r], mean, dq[db][r]);
+    }
+    if (qok) {
         uint16_t* row = a.dq + ((size_t)bh * a.N + q) * HD;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d = 32 * db + 8 * r4 + 4 * h;
-                const uint32_t w0 = f32_to_bf16_rne(dq[db][4 * r4 + 0] * 0.125f) |
-                                    (f32_to_bf16_rne(dq[db][4 * r4 + 1] * 0.125f) << 16);
-                const uint32_t w1 = f32_to_bf16_rne(dq[db][4 * r4 + 2] * 0.125f) |
-                                    (f32_to_bf16_rne(dq[db][4 * r4 + 3] * 0.125f) << 16);
+                const uint32_t w0 = f32_to_bf16_rne(dq[db][4 * r4 + 0]) | (f32_to_bf16_rne(dq[db][4 * r4 + 1]) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(dq[db][4 * r4 + 2]) | (f32_to_bf16_rne(dq[db][4 * r4 + 3]) << 16);
                 *(uint2*)(row + d) = make_uint2(w0, w1);
             }
     }

@@ -49,6 +49,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// QK-norm of one bf16 element with its token's factor r: bf16(fp32(x r)),
+// returned as float32.
+__device__ __forceinline__ float qk_normed(uint32_t bits16, float r) {
+    return bf16_to_f32(f32_to_bf16_rne(bf16_to_f32(bits16) * r));
+}
+constexpr double QK_NORM_EPS = 1e-6;
+
 // Per-block scale from an absmax: s = a * fp32(1/127) (one rounded
 // multiply) and inv = 127/a (correctly rounded float32 division); blocks with
 // a < 2^-100 are all-zero.

@@ -9,6 +9,7 @@ constexpr int SUM_CHUNK = 256;   // tokens per partial column sum
 struct MeansArgs {
     const uint16_t* q;
     const uint16_t* k;
+    const float *rq, *rk;              // QK-norm factors [BH][Np], or null
     double* sums;      // [BH][2][nchunk][64]
     float* mu_q;       // [BH][64]
     float* mu_k;
@@ -17,6 +18,7 @@ struct MeansArgs {
 
 struct QuantArgs {
     const uint16_t *q, *k, *v;         // bf16 [BH][N][64]
+    const float *rq, *rk;              // QK-norm factors [BH][Np], or null
     const float *mu_q, *mu_k;          // [BH][64]
     int8_t *q_r, *k_r;                 // row operand layout (nullable)
     int8_t *q_t, *k_t, *v_t;           // transposed operand layout (nullable)
@@ -39,6 +41,7 @@ struct BwdPreArgs {
     int N, T;
 };
 
+int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, int N, int T, int BH, hipStream_t st);
 int launch_means(const MeansArgs& m, hipStream_t st);
 int launch_quantize(const QuantArgs& a, int BH, int ntensors, hipStream_t st);
 int launch_bwd_pre(const BwdPreArgs& a, int BH, hipStream_t st);

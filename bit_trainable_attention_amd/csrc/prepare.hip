@@ -12,6 +12,39 @@
 
 namespace sagebwd {
 
+// ---------------------------------------------------------------- QK-norm
+// Factor r = 1/sqrt(mean_c x^2 + 1e-6) of every token row of Q (tensor 0)
+// and K (tensor 1), in float64 and rounded once to float32 (SageBwd abstract,
+// insight (i): QK-norm); every later kernel reads x_n = bf16(fp32(x r)).  The
+// squares of bf16 values are exact in float64; the order of their sum moves
+// it by a few float64 ulps at most, far below what changes the float32 r
+// except within ~1e-16 of one of its rounding boundaries.  0 past N.
+__global__ __launch_bounds__(256) void k_rownorm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                 float* __restrict__ rq, float* __restrict__ rk, int N, int T) {
+    const int t = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+    const int r = threadIdx.x / 4, g = threadIdx.x % 4;
+    const int tok = t * BLK + r;
+    const bool valid = tok < N;
+    double ss = 0.0;
+    if (valid) {
+        const uint16_t* src = (tensor == 0 ? q : k) + ((size_t)bh * N + tok) * HD + 16 * g;
+        const uint4 u0 = *(const uint4*)src, u1 = *(const uint4*)(src + 8);
+        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const double a = bf16_to_f32(w[j] & 0xFFFFu), b = bf16_to_f32(w[j] >> 16);
+            ss = __builtin_fma(a, a, ss);
+            ss = __builtin_fma(b, b, ss);
+        }
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (g == 0) {
+        const float rr = valid ? (float)(1.0 / __builtin_sqrt(ss * (1.0 / HD) + QK_NORM_EPS)) : 0.0f;
+        (tensor == 0 ? rq : rk)[(size_t)bh * T * BLK + tok] = rr;
+    }
+}
+
 // ---------------------------------------------------------------- means
 // Partial float64 column sums of K (tensor 0) and Q (tensor 1) over chunks
 // of SUM_CHUNK tokens.  The order of additions is fixed; for bf16 inputs
@@ -19,11 +52,14 @@ namespace sagebwd {
 // so the final mean does not depend on the order at all.
 __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ q,
                                                 const uint16_t* __restrict__ k,
+                                                const float* __restrict__ rq, const float* __restrict__ rk,
                                                 double* __restrict__ sums, int N, int nchunk,
                                                 int do_q, int do_k) {
     const int chunk = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
     if ((tensor == 0 && !do_k) || (tensor == 1 && !do_q)) return;
     const uint16_t* src = (tensor == 0 ? k : q) + (size_t)bh * N * HD;
+    const float* rn = tensor == 0 ? rk : rq;      // QK-norm factors, or null
+    const size_t rbase = (size_t)bh * ((N + BLK - 1) / BLK) * BLK;
     const int g = threadIdx.x % 8;            // 8 channels per thread
     const int tr = threadIdx.x / 8;           // 32 token rows
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -33,10 +69,19 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ q,
         if (tok < N) {
             const uint4 u = *(const uint4*)(src + (size_t)tok * HD + 8 * g);
             const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+            if (rn) {
+                const float rr = rn[rbase + tok];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] += (double)bf16_to_f32(w[j] & 0xFFFFu);
-                acc[2 * j + 1] += (double)bf16_to_f32(w[j] >> 16);
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] += (double)qk_normed(w[j] & 0xFFFFu, rr);
+                    acc[2 * j + 1] += (double)qk_normed(w[j] >> 16, rr);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[2 * j] += (double)bf16_to_f32(w[j] & 0xFFFFu);
+                    acc[2 * j + 1] += (double)bf16_to_f32(w[j] >> 16);
+                }
             }
         }
     }
@@ -114,10 +159,20 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         u1 = *(const uint4*)(src + 8);
     }
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const float* rn = tensor == 0 ? a.rq : tensor == 1 ? a.rk : nullptr;   // QK-norm: x_n = bf16(fp32(x r))
+    if (rn) {
+        const float rr = valid ? rn[(size_t)bh * a.T * BLK + tok] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        raw[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-        raw[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+        for (int j = 0; j < 8; ++j) {
+            raw[2 * j] = qk_normed(w[j] & 0xFFFFu, rr);
+            raw[2 * j + 1] = qk_normed(w[j] >> 16, rr);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            raw[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+            raw[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+        }
     }
     float amax = 0.0f;
 #pragma unroll
@@ -270,11 +325,16 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
 int launch_means(const MeansArgs& m, hipStream_t st) {
     const int nchunk = (m.N + SUM_CHUNK - 1) / SUM_CHUNK;
     if (m.smooth_q || m.smooth_k) {
-        hipLaunchKernelGGL(k_colsum, dim3(nchunk, m.BH, 2), dim3(256), 0, st, m.q, m.k, m.sums, m.N, nchunk,
-                           m.smooth_q, m.smooth_k);
+        hipLaunchKernelGGL(k_colsum, dim3(nchunk, m.BH, 2), dim3(256), 0, st, m.q, m.k, m.rq, m.rk, m.sums, m.N,
+                           nchunk, m.smooth_q, m.smooth_k);
     }
     hipLaunchKernelGGL(k_means, dim3(m.BH), dim3(128), 0, st, m.sums, m.mu_q, m.mu_k, m.N, nchunk, m.smooth_q,
                        m.smooth_k);
+    return 0;
+}
+
+int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, int N, int T, int BH, hipStream_t st) {
+    hipLaunchKernelGGL(k_rownorm, dim3(T, BH, 2), dim3(256), 0, st, q, k, rq, rk, N, T);
     return 0;
 }
 

@@ -63,6 +63,16 @@ typedef struct sagebwd_params {
                            dO V^T also from per-block INT8 codes of dO and V
                            (i32 accumulation, scaled by s_dO s_V) instead of
                            FP16.  0 (the method) keeps it in FP16. */
+    int32_t qk_norm;    /* 0 or 1: QK-norm fused in (SageBwd abstract, insight
+                           (i): necessary for stable training at many tokens
+                           per step).  Every token row x of Q and of K becomes
+                           x_n = bf16(fp32(x r)), r = 1/sqrt(mean_c x^2 + 1e-6)
+                           (float64, rounded once to float32), before smoothing
+                           and quantization, so attention (and LSE) use the
+                           normalized scores; the backward returns dQ, dK
+                           with respect to the Q, K passed in, through
+                           dx = r (dx_n - x_n mean_c(dx_n x_n)).  Forward and
+                           backward must be called with the same value. */
 } sagebwd_params;
 
 #define SAGEBWD_OK               0
@@ -161,6 +171,8 @@ const char* sagebwd_status_string(int status);
  *   17 V16    fp16 [BH][Np][64]      V in FP16, natural layout
  *   18 DO_R   int8  [BH][T][4096]    dO codes, row operand layout (int8_dp only)
  *   19 V_R    int8  [BH][T][4096]    V codes, row operand layout (int8_dp only)
+ *   20 RQ     float32 [BH][Np]       QK-norm factor r of each Q token (qk_norm only; 0 past N)
+ *   21 RK     float32 [BH][Np]       likewise for K
  * with T = ceil(N/64), Np = 64 T.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
  * 64 channels, element (token r, channel c) sits at byte
  *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16

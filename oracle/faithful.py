@@ -9,9 +9,12 @@ with its reason, in the design notes that ship with the library):
 
   F0  QK-norm (option; SageBwd abstract, insight (i): necessary for stable
       training at many tokens per step): per token row of Q and of K,
-      r = fp32(1 / sqrt(exact_sum(x^2) / 64 + 1e-6)) (float64 steps), and the
-      normalized row x_n = bf16(fp32(x r)), the tensor a separate norm would
-      hand to attention; every later step reads x_n in place of x.
+      r = fp32(1 / sqrt(S / 64 + 1e-6)) (float64 steps) with S the float64
+      sum of the exact squares (here the correctly rounded one; another
+      summation order moves S by a few float64 ulps, which changes the
+      float32 r only if r lies within ~1e-16 of a float32 rounding boundary),
+      and the normalized row x_n = bf16(fp32(x r)), the tensor a separate norm
+      would hand to attention; every later step reads x_n in place of x.
   F1  smoothing means  mu = fp32( exact_sum(x over the N valid tokens) / N )
       per (batch, head, channel), for K when smooth_k and for Q when smooth_q
       (SageBwd abstract, insight (iv): K-smoothing, optional Q-smoothing).
@@ -90,10 +93,10 @@ def bf16_rne(x) -> np.ndarray:
 
 
 def qk_norm_rows(x, rounding: bool = True):
-    """F0 for one head: (x_n, r).  The sum of squares is exact (fsum of exact
-    float64 squares of the bf16 inputs); r = 1/sqrt(sum/64 + 1e-6) in float64
-    rounded once to float32; x_n = bf16(fp32(x * r)).  Without rounding:
-    x_n = x r in float64."""
+    """F0 for one head: (x_n, r).  The sum of squares is the correctly rounded
+    float64 sum (fsum) of the exact float64 squares of the bf16 inputs;
+    r = 1/sqrt(sum/64 + 1e-6) in float64 rounded once to float32;
+    x_n = bf16(fp32(x * r)).  Without rounding: x_n = x r in float64."""
     x64 = np.asarray(x, np.float64)
     ss = np.array([math.fsum((row * row).tolist()) for row in x64])
     r64 = 1.0 / np.sqrt(ss / 64.0 + QK_NORM_EPS)

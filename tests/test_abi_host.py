@@ -37,9 +37,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def P(**kw):
-    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0)
+    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0, qk_norm=0)
     d.update(kw)
-    return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"], d["int8_dp"])
+    return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"], d["int8_dp"],
+                     d["qk_norm"])
 
 
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -65,6 +66,7 @@ def test_param_validation(lib):
     assert call_fwd(lib, P(smooth_k=7)) == INVALID
     assert call_fwd(lib, P(int8_dp=2)) == INVALID
     assert call_bwd(lib, P(int8_dp=-1)) == INVALID
+    assert call_fwd(lib, P(qk_norm=3)) == INVALID
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED
     assert call_fwd(lib, P(N=(1 << 20) + 1)) == UNSUPPORTED
     assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED
@@ -112,10 +114,10 @@ def test_prepare_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, 10) == WORKSPACE
 
 
-@pytest.mark.parametrize("int8_dp", [0, 1])
-def test_ws_regions_layout(lib, int8_dp):
+@pytest.mark.parametrize("int8_dp,qk_norm", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_ws_regions_layout(lib, int8_dp, qk_norm):
     for N in (1, 63, 64, 65, 1000, 17776):
-        p = P(B=2, H=3, N=N, int8_dp=int8_dp)
+        p = P(B=2, H=3, N=N, int8_dp=int8_dp, qk_norm=qk_norm)
         BH, T = 6, (N + 63) // 64
         Np = 64 * T
         expect = {"MU_Q": BH * 256, "MU_K": BH * 256, "Q_R": BH * T * 4096, "K_R": BH * T * 4096,
@@ -123,7 +125,8 @@ def test_ws_regions_layout(lib, int8_dp):
                   "S_Q": BH * T * 4, "S_K": BH * T * 4, "S_V": BH * T * 4, "S_DO": BH * T * 4,
                   "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "NDELTA": BH * Np * 4, "LSE2": BH * Np * 4,
                   "DO16": BH * Np * 128, "V16": BH * Np * 128,
-                  "DO_R": int8_dp * BH * T * 4096, "V_R": int8_dp * BH * T * 4096}
+                  "DO_R": int8_dp * BH * T * 4096, "V_R": int8_dp * BH * T * 4096,
+                  "RQ": qk_norm * BH * Np * 4, "RK": qk_norm * BH * Np * 4}
         spans = []
         for name, rid in sb.REGIONS.items():
             off, nb = sb.ws_region(p, rid)

@@ -143,6 +143,47 @@ def test_end_to_end_parity_and_determinism(w):
         assert M.rel_l2(W.bf16_bits_to_f32(a), b) <= REL_L2
 
 
+QK_SMALL = [
+    W.custom(1, 2, 200, True, True, True, "rowscale", 91),
+    W.custom(2, 1, 129, False, True, False, "rowscale", 92),
+    W.custom(1, 1, 65, True, False, False, "rowscale", 93),
+    W.custom(1, 1, 1, True, True, True, "rowscale", 94),
+]
+
+
+@pytest.mark.parametrize("w", QK_SMALL, ids=_ids(QK_SMALL))
+def test_qk_norm_parity(w):
+    """Fused QK-norm: forward, and backward end to end (each side feeds its own
+    forward), against the faithful oracle with F0/B11 and against exact
+    attention on normalized Q, K with gradients through the norm."""
+    print(f"[qk_norm] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o), lse.cpu().numpy()
+    g = [G.host_f32(t) for t in (dq, dk, dv)]
+    o_f, lse_f = F.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    ref = F.bwd(f32["q"], f32["k"], f32["v"], _bf16(o_f), lse_f.astype(np.float32), f32["do"], w.causal,
+                w.smooth_q, w.smooth_k, qk_norm=True)
+    o_e, lse_e = exact.fwd_bh(f32["q"], f32["k"], f32["v"], w.causal, qk_norm=True)
+    ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal, qk_norm=True)
+    print(f"  O: rel-L2 vs faithful {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}")
+    assert M.rel_l2(o_g, o_f) <= REL_L2
+    assert np.max(np.abs(lse_g - lse_f)) <= LSE_ATOL
+    assert M.cos_sim(o_g, o_e) >= COS_O
+    for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
+        assert np.all(np.isfinite(a)), name
+        print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
+        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
+        if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+        else:
+            assert np.linalg.norm(a) <= 1e-2 * max(np.linalg.norm(g[2]), 1e-30), name
+
+
 def test_zero_inputs():
     z = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
     for causal in (False, True):
@@ -155,14 +196,16 @@ def test_zero_inputs():
         assert torch.allclose(lse[0, 0], torch.log(n), atol=1e-5)
 
 
-def test_autograd_wrapper():
-    w = W.custom(1, 1, 96, True, True, True, "kbias", 59)
+@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
+def test_autograd_wrapper(qk_norm):
+    w = W.custom(1, 1, 96, True, True, True, "rowscale" if qk_norm else "kbias", 59)
     x = W.make_inputs(w)
     q, k, v = (G.dev(x[n]).requires_grad_(True) for n in ("q", "k", "v"))
-    o = sb.SageBwdAttention.apply(q, k, v, True, True, True)
+    o = sb.SageBwdAttention.apply(q, k, v, True, True, True, qk_norm)
     o.backward(G.dev(x["do"]))
-    dq, dk, dv = sb.bwd(q.detach(), k.detach(), v.detach(), *sb.fwd(q.detach(), k.detach(), v.detach(), True, True, True),
-                        G.dev(x["do"]), True, True, True)
+    dq, dk, dv = sb.bwd(q.detach(), k.detach(), v.detach(),
+                        *sb.fwd(q.detach(), k.detach(), v.detach(), True, True, True, qk_norm=qk_norm),
+                        G.dev(x["do"]), True, True, True, qk_norm=qk_norm)
     torch.cuda.synchronize()
     for a, b in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
         assert torch.equal(a, b)

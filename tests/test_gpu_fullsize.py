@@ -85,3 +85,46 @@ def test_fullsize_sampled_parity(name, smooth_q, head, int8_dp):
     assert cos["O"] >= 0.999
     for k in ("dQ", "dK", "dV"):
         assert cos[k] >= 0.99, (k, cos[k])
+
+
+def test_fullsize_qk_norm_sampled_parity():
+    """The fused QK-norm at the pretraining shape (B8 H16 N2048 causal) on raw
+    rows of very different sizes: one sampled head, forward over all rows and
+    the backward's first, middle and last blocks, with gradients through the
+    norm."""
+    w = W.custom(8, 16, 2048, True, True, False, "rowscale", 95)
+    b, h = 5, 9
+    print(f"[fullsize qk_norm] B{w.B} H{w.H} N{w.N} head=({b}, {h})", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    fws = torch.empty(sb.workspace_size(w.B, w.H, w.N, True, False, True, qk_norm=True), dtype=torch.uint8,
+                      device="cuda")
+    o, lse = sb.fwd(tq, tk, tv, True, False, True, workspace=fws, qk_norm=True)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, True, False, True, fwd_workspace=fws, qk_norm=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o[b, h]), lse[b, h].cpu().numpy()
+    dq_g, dk_g, dv_g = (G.host_f32(t[b, h]) for t in (dq, dk, dv))
+    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv, fws
+    f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
+    N, T = w.N, w.N // 64
+    pp = F.prepare(f["q"], f["k"], f["v"], False, True, qk_norm=True)
+    o_f, lse_f = F.fwd_head(pp, True)
+    o_f, lse_f = o_f[:N], lse_f[:N]
+    assert M.rel_l2(o_g, o_f) <= 1e-2 and np.max(np.abs(lse_g - lse_f)) <= 2e-3
+    blocks = _blocks(T)
+    rows = np.concatenate([np.arange(i * 64, i * 64 + 64) for i in blocks])
+    o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
+    bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"])
+    dq_f, dk_f, dv_f = F.bwd_head(bp, True, blocks, blocks)
+    dq_f, dk_f = F.norm_grads(pp, dq_f, dk_f, rows, rows)
+    errs = {"dQ": M.rel_l2(dq_g[rows], dq_f), "dK": M.rel_l2(dk_g[rows], dk_f), "dV": M.rel_l2(dv_g[rows], dv_f)}
+    print("  rel-L2 vs faithful:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    for k, v in errs.items():
+        assert v <= 1e-2, (k, v)
+    oe, le, dqe, dke, dve = exact.sampled(f["q"], f["k"], f["v"], f["do"], True, rows, rows, qk_norm=True)
+    cos = {"O": M.cos_sim(o_g[rows], oe), "dQ": M.cos_sim(dq_g[rows], dqe), "dK": M.cos_sim(dk_g[rows], dke),
+           "dV": M.cos_sim(dv_g[rows], dve)}
+    print("  cos vs exact:", {k: f"{v:.6f}" for k, v in cos.items()}, flush=True)
+    assert cos["O"] >= 0.999
+    for k in ("dQ", "dK", "dV"):
+        assert cos[k] >= 0.99, (k, cos[k])

@@ -3,6 +3,8 @@ means, INT8 codes of Q, K, V, dO in both operand layouts, and block scales.
 Side outputs (correction, bias, Delta, log2 LSE) are float32 reductions whose
 order differs from the oracle's, so they are compared within float32
 rounding; the FP16 copies are compared bit for bit with IEEE conversion."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -26,9 +28,9 @@ CASES = [
 ]
 
 
-def _run(w, heads, int8_dp=False):
+def _run(w, heads, int8_dp=False, qk_norm=False):
     print(f"[prepare] {w.name} B{w.B} H{w.H} N{w.N} causal={w.causal} sq={w.smooth_q} sk={w.smooth_k} "
-          f"int8_dp={int8_dp}", flush=True)
+          f"int8_dp={int8_dp} qk_norm={qk_norm}", flush=True)
     x = W.make_inputs(w)
     r = np.random.default_rng(5)
     o_bits = W.f32_to_bf16_bits(r.standard_normal(x["q"].shape).astype(np.float32))
@@ -36,10 +38,10 @@ def _run(w, heads, int8_dp=False):
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
     to = G.dev(o_bits)
     tlse = torch.from_numpy(lse).cuda()
-    ws = sb.prepare(tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp)
+    ws = sb.prepare(tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp, qk_norm=qk_norm)
     torch.cuda.synchronize()
     wsh = ws.cpu().numpy()
-    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp)
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp, qk_norm=qk_norm)
     BH, T = w.B * w.H, (w.N + 63) // 64
     Np = 64 * T
     got = {
@@ -57,6 +59,9 @@ def _run(w, heads, int8_dp=False):
         "do16": G.region(wsh, p, "DO16", np.float16).reshape(BH, Np, 64),
         "v16": G.region(wsh, p, "V16", np.float16).reshape(BH, Np, 64),
     }
+    if qk_norm:   # QK-norm factors of every Q and K token
+        got["rq"] = G.region(wsh, p, "RQ", np.float32).reshape(BH, Np)
+        got["rk"] = G.region(wsh, p, "RK", np.float32).reshape(BH, Np)
     if int8_dp:   # row-operand dO and V codes of the all-INT8 dO V^T
         got["do_r"] = G.decode_codes(wsh, p, "DO_R", "row", BH, T)
         got["v_r"] = G.decode_codes(wsh, p, "V_R", "row", BH, T)
@@ -68,9 +73,19 @@ def _run(w, heads, int8_dp=False):
     for b, h in heads:
         i = b * w.H + h
         q, k, v, do = (f32[n][b, h] for n in ("q", "k", "v", "do"))
-        for key in ("q", "k"):
-            assert F.sum_order_free(f32[key][b, h]) or not (w.smooth_q if key == "q" else w.smooth_k)
-        pp = F.prepare(q, k, v, w.smooth_q, w.smooth_k)
+        pp = F.prepare(q, k, v, w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+        for xin, on in ((pp.q_raw, w.smooth_q), (pp.k_in, w.smooth_k)):     # the values the means are taken over
+            assert F.sum_order_free(xin.astype(np.float32)) or not on
+        if qk_norm:
+            for key, rr in (("q", pp.rq), ("k", pp.rk)):
+                # the GPU forms the float64 sum of squares in its own order; r
+                # is the same for any order on these rows (checked with two)
+                x64 = f32[key][b, h].astype(np.float64) ** 2
+                for s_other in (np.sum(x64, axis=1), np.sum(x64[:, ::-1], axis=1)):
+                    r_other = (1.0 / np.sqrt(s_other / 64.0 + 1e-6)).astype(np.float32)
+                    assert np.array_equal(r_other.view(np.uint32), rr.view(np.uint32)), key
+                assert np.array_equal(got["r" + key][i][:N].view(np.uint32), rr.view(np.uint32)), key
+                assert np.all(got["r" + key][i][N:] == 0)
         bp = F.prepare_bwd(pp, v, of32[b, h], lse[b, h], do)
         assert np.array_equal(got["mu_q"][i].view(np.uint32), np.asarray(pp.mu_q, np.float32).view(np.uint32))
         assert np.array_equal(got["mu_k"][i].view(np.uint32), np.asarray(pp.mu_k, np.float32).view(np.uint32))
@@ -101,6 +116,21 @@ def _run(w, heads, int8_dp=False):
 def test_prepare_bitexact(name, w, heads):
     G.assert_perms_are_bijections()
     _run(w if w is not None else W.WORKLOADS[name], heads)
+
+
+QK_CASES = [
+    ("ragged_causal", W.custom(1, 2, 200, True, True, True, "rowscale", 81), None),
+    ("ragged_noncausal", W.custom(2, 1, 129, False, True, False, "rowscale", 82), None),
+    ("one_token", W.custom(1, 1, 1, True, True, True, "rowscale", 83), None),
+    ("pretrain_shape", W.custom(8, 16, 2048, True, True, False, "rowscale", 84), [(0, 0), (7, 15)]),
+]
+
+
+@pytest.mark.parametrize("name,w,heads", QK_CASES, ids=[c[0] for c in QK_CASES])
+def test_prepare_bitexact_qk_norm(name, w, heads):
+    """The fused QK-norm: per-token factors r and everything derived from the
+    normalized rows (means, codes, scales, correction, bias), bit-exact."""
+    _run(w, heads, qk_norm=True)
 
 
 @pytest.mark.parametrize("name,w,heads", [c for c in CASES if c[0] in ("ragged_outlier", "one_token", "llama8k")],

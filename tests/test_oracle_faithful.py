@@ -392,8 +392,9 @@ def test_qk_norm_step_against_high_precision():
     """F0 with rounding: r is within one float32 ulp of 1/sqrt(mean x^2 + 1e-6)
     computed with 50 significant digits; x_n is within half a bf16 ulp (plus
     the float32 product's error) of x r; normalized rows have mean square 1 to
-    bf16 precision; and the float64 sum of squares is order-free on these
-    rows (the GPU forms it in another order)."""
+    bf16 precision; and r does not change when the float64 sum of squares is
+    formed in another order (the GPU's), even on rows whose exact sum does not
+    fit a float64."""
     from decimal import Decimal, getcontext
     getcontext().prec = 50
     x = _qk_rows(500, 64, 1e-3, 1e3)
@@ -403,7 +404,10 @@ def test_qk_norm_step_against_high_precision():
         ref = 1 / (sum(t * t for t in row) / 64 + Decimal("0.000001")).sqrt()
         rf = float(ref)
         assert abs(float(r[i]) - rf) <= np.spacing(np.float32(rf))
-        assert np.sum(x[i].astype(np.float64) ** 2) == math.fsum((x[i].astype(np.float64) ** 2).tolist())
+    sq = x.astype(np.float64) ** 2
+    for s_other in (np.sum(sq, axis=1), np.sum(sq[:, ::-1], axis=1), np.sum(sq.reshape(-1, 4, 16), axis=2).sum(axis=1)):
+        r_other = (1.0 / np.sqrt(s_other / 64.0 + 1e-6)).astype(np.float32)
+        assert np.array_equal(r_other.view(np.uint32), r.view(np.uint32))
     exact_xn = x.astype(np.float64) * r.astype(np.float64)[:, None]
     ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact_xn), 1e-30))) - 7)
     assert np.all(np.abs(xn - exact_xn) <= 0.5 * ulp * (1 + 2 ** -16))

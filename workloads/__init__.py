@@ -18,9 +18,14 @@ datasets and checkpoints themselves are not used. Shapes and distributions:
   video       B2 H30 N17776 non-causal  Q,K ~ N(0,1) plus +-8 on 4 random channels
                                         per (tensor, b, h); V,dO ~ N(0,1)
 
+  rowscale    (custom shapes, for the fused QK-norm) Q, K ~ N(0,1), each token
+                                        row scaled by exp(U(ln 0.05, ln 20)), i.e.
+                                        un-normalized activations; V,dO ~ N(0,1)
+
 Seeds: every (tensor, batch b, head h) has its own numpy PCG64 stream seeded by
 SeedSequence([1000*k + tensor index, b, h]) with tensor index Q 0, K 1, V 2,
-dO 3, K-bias 4, outlier channels 6, and k = 1..5 in the order above.  Draws are
+dO 3, K-bias 4, outlier channels 6, row scales 7 (K's with head 1000 + h),
+and k = 1..5 in the order above.  Draws are
 float32, rounded to bfloat16 with round-to-nearest-even; the bf16 bit patterns
 (uint16) are what both sides receive.
 """
@@ -42,7 +47,7 @@ class Workload:
     causal: bool
     smooth_k: bool
     smooth_q: bool
-    dist: str         # "normal" | "qknorm" | "kbias" | "outlier"
+    dist: str         # "normal" | "qknorm" | "kbias" | "outlier" | "rowscale"
     d: int = D
 
     @property
@@ -99,6 +104,10 @@ def make_head(w: Workload, b: int, h: int, seed_family: int | None = None) -> di
             ch = rng.choice(w.d, size=4, replace=False)
             sign = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=4)
             x[:, ch] += (np.float32(8.0) * sign)[None, :]
+    elif w.dist == "rowscale":
+        for ti, x in enumerate((q, kk)):
+            u = _gen(1000 * k + 7, b, 1000 * ti + h).uniform(np.log(0.05), np.log(20.0), (w.N, 1))
+            x *= np.exp(u).astype(np.float32)
     elif w.dist != "normal":
         raise ValueError(w.dist)
     return {n: f32_to_bf16_bits(a) for n, a in (("q", q), ("k", kk), ("v", v), ("do", do))}
