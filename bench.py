@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--int8-dp", action="store_true",
                     help="time the all-INT8 ablation (dO V^T from INT8 codes) instead of the method's FP16 dO V^T")
+    ap.add_argument("--qk-norm", action="store_true", help="fuse QK-norm into the path (normalizes the inputs' rows)")
     ap.add_argument("--no-reuse", action="store_true",
                     help="let the backward re-quantize Q and K instead of reading the forward's workspace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -131,7 +132,7 @@ def main():
 
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     del x
-    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp)
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp, qk_norm=args.qk_norm)
     lib = sb.load_library()
     import ctypes
     ws_f = torch.empty(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
@@ -181,7 +182,7 @@ def main():
     dom = max(KERNEL_UNITS, key=lambda s: stage_ms[s])
     ach = KERNEL_UNITS[dom] * unit / (stage_ms[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None if args.int8_dp else load_traffic(dom, w.name),
+            "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name),
             "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {
         "metric": METRIC,
@@ -198,7 +199,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
-                   "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp)},
+                   "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp),
+                   "qk_norm": bool(args.qk_norm)},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         # 12 of the 14 N^2 d units are INT8 and 2 (dO V^T, fwd-side none) FP16 at half the INT8 rate,
         # so the MFMA floor of the mix is 14/16 of the INT8 peak
