@@ -36,9 +36,8 @@ KERNEL_SOURCES = {
 }
 # algorithmic matmul work of each attention kernel, in units of 2*N^2*d per
 # head (times 1/2 when causal): forward QK^T + P~V; dK/dV kernel QK^T, P^T dO,
-# dO V^T, dS^T Q; dQ kernel QK^T, dO V^T, dS K (it recomputes S and dP because
-# the backward is split into two kernels that never exchange dS)
-KERNEL_UNITS = {"FWD_ATTN": 2, "BWD_DKDV": 4, "BWD_DQ": 3}
+# dO V^T, dS^T Q; dQ kernel dS K (from the dS codes the dK/dV kernel stored)
+KERNEL_UNITS = {"FWD_ATTN": 2, "BWD_DKDV": 4, "BWD_DQ": 1}
 
 
 def source_sha(stage: str) -> str:

@@ -3,6 +3,8 @@
 // contract are in include/sagebwd.h.
 #include "sagebwd.h"
 
+#include <algorithm>
+
 #include "attn.h"
 #include "prep.h"
 
@@ -13,7 +15,7 @@ using namespace sagebwd;
 enum Region {
     R_MU_Q = 0, R_MU_K, R_Q_R, R_K_R, R_V_T, R_Q_T, R_K_T, R_DO_T,
     R_S_Q, R_S_K, R_S_V, R_S_DO, R_CORR, R_BIAS, R_DELTA, R_LSE2, R_DO16, R_V16,
-    R_DO_R, R_V_R, R_RQ, R_RK, R_SUMS, R_COUNT
+    R_DO_R, R_V_R, R_RQ, R_RK, R_DS, R_DS_SCALE, R_SUMS, R_COUNT
 };
 
 struct Layout {
@@ -22,10 +24,29 @@ struct Layout {
     size_t total;
 };
 
-constexpr int32_t MAX_N = 1 << 20;
+constexpr int32_t MAX_N = 1 << 18;
 constexpr int64_t MAX_BH = 65535;
+// The backward keeps the INT8 dS codes of every tile of a group of heads
+// (4 KB per 64x64 tile) between its two attention kernels; a group holds as
+// many heads as fit in this many bytes, and at least one.
+constexpr size_t DS_CAP_BYTES = (size_t)16 << 30;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Heads per backward group and the number of groups (equal-sized but the last).
+struct Groups {
+    int heads, count;
+    size_t ntiles;   // dS tiles per head
+};
+Groups head_groups(const sagebwd_params& p) {
+    const int BH = p.B * p.H;
+    const int T = (p.N + BLK - 1) / BLK;
+    const size_t nt = ds_tiles_per_head(p.causal, T);
+    size_t hmax = DS_CAP_BYTES / (nt * 4096);
+    if (hmax < 1) hmax = 1;
+    const int count = (int)((BH + hmax - 1) / hmax);
+    return Groups{(BH + count - 1) / count, count, nt};
+}
 
 // Which regions a pass uses: the forward needs Q/K row codes and V
 // transposed codes; the backward needs Q/K in both layouts and its own
@@ -63,6 +84,9 @@ Layout make_layout(const sagebwd_params& p, Pass pass) {
     sz[R_V_R] = i8dp ? BH * T * 4096 : 0;
     sz[R_RQ] = p.qk_norm ? BH * Np * 4 : 0;         // QK-norm factors of Q and K tokens
     sz[R_RK] = p.qk_norm ? BH * Np * 4 : 0;
+    const Groups G = head_groups(p);
+    sz[R_DS] = bwd ? (size_t)G.heads * G.ntiles * 4096 : 0;     // dS codes of one head group
+    sz[R_DS_SCALE] = bwd ? (size_t)G.heads * G.ntiles * 4 : 0;
     sz[R_SUMS] = BH * 2 * nchunk * HD * 8;
     size_t o = 0;
     for (int r = 0; r < R_COUNT; ++r) {
@@ -233,6 +257,9 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     a.dq = (uint16_t*)dQ;
     a.dk = (uint16_t*)dK;
     a.dv = (uint16_t*)dV;
+    a.ds_codes = region<int8_t>(ws, L, R_DS);
+    a.ds_scale = region<float>(ws, L, R_DS_SCALE);
+    a.ntiles = head_groups(p).ntiles;
     a.N = p.N;
     a.T = (p.N + BLK - 1) / BLK;
     a.ngroups = (a.T + 1) / 2;
@@ -240,6 +267,54 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     a.dump = nullptr;
     a.dump_bh = a.dump_i = a.dump_t = -1;
     return a;
+}
+
+// The same arguments restricted to heads [bh0, bh0 + nbh): every per-head
+// pointer moves by bh0 heads, the dS buffers stay (they hold one group).
+template <class P>
+P* adv(P* ptr, size_t n) { return ptr ? ptr + n : ptr; }
+BwdArgs group_args(const BwdArgs& a, int bh0, int nbh) {
+    BwdArgs c = a;
+    const size_t T = (size_t)a.T, Np = T * BLK, codes = (size_t)bh0 * T * 4096, blocks = (size_t)bh0 * T,
+                 rows = (size_t)bh0 * Np, toks = (size_t)bh0 * a.N * HD;
+    c.q_r = adv(a.q_r, codes);
+    c.k_r = adv(a.k_r, codes);
+    c.q_t = adv(a.q_t, codes);
+    c.k_t = adv(a.k_t, codes);
+    c.do_t = adv(a.do_t, codes);
+    c.do_r = adv(a.do_r, codes);
+    c.v_r = adv(a.v_r, codes);
+    c.sq = adv(a.sq, blocks);
+    c.sk = adv(a.sk, blocks);
+    c.sdo = adv(a.sdo, blocks);
+    c.sv = adv(a.sv, blocks);
+    c.bias = adv(a.bias, rows);
+    c.delta = adv(a.delta, rows);
+    c.lse2 = adv(a.lse2, rows);
+    c.rq = adv(a.rq, rows);
+    c.rk = adv(a.rk, rows);
+    c.do16 = adv(a.do16, rows * HD);
+    c.v16 = adv(a.v16, rows * HD);
+    c.mu_q = adv(a.mu_q, (size_t)bh0 * HD);
+    c.q_in = adv(a.q_in, toks);
+    c.k_in = adv(a.k_in, toks);
+    c.dq = adv(a.dq, toks);
+    c.dk = adv(a.dk, toks);
+    c.dv = adv(a.dv, toks);
+    c.BH = nbh;
+    c.dump_bh = a.dump_bh >= 0 ? a.dump_bh - bh0 : -1;
+    return c;
+}
+
+// The two attention kernels of the backward over one head group.  kernel_dump
+// selects which of them (1: dK/dV, 2: dQ) runs its debug instantiation.
+void run_bwd_group(const sagebwd_params& p, const BwdArgs& a, int grp, int which, int kernel_dump,
+                   hipStream_t st) {
+    const Groups G = head_groups(p);
+    const int bh0 = grp * G.heads, nbh = std::min(G.heads, p.B * p.H - bh0);
+    const BwdArgs c = group_args(a, bh0, nbh);
+    if (which & 1) launch_bwd_dkdv(c, nbh, p.causal, p.smooth_q, p.int8_dp, st, kernel_dump == 1);
+    if (which & 2) launch_bwd_dq(c, nbh, p.causal, st, kernel_dump == 2);
 }
 
 }  // namespace
@@ -322,21 +397,35 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         run_bwd_pre(*p, L, qk, V, O, LSE, dO, ws, st);
         return hip_status();
     }
+    // the two attention stages hand the dS codes of all heads from one to the
+    // other, which needs a single head group
+    if (head_groups(*p).count != 1) return SAGEBWD_ERR_UNSUPPORTED;
     const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
-    if (stage == SAGEBWD_STAGE_BWD_DKDV) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
-    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, st);
+    run_bwd_group(*p, a, 0, stage == SAGEBWD_STAGE_BWD_DKDV ? 1 : 2, 0, st);
+    return hip_status();
+}
+
+// The whole backward: preparation, then for each head group the dK/dV kernel
+// followed by the dQ kernel (which reads the group's dS codes).
+static int bwd_pass(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
+             const float* LSE, const void* dO, void* dQ, void* dK, void* dV, const void* fwd_ws,
+             size_t fwd_ws_bytes, void* ws, size_t ws_bytes, hipStream_t st) {
+    int rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes,
+                               ws, ws_bytes, st);
+    if (rc) return rc;
+    const Layout L = make_layout(*p, PASS_BWD);
+    QkSource qk{ws, L};
+    if (fwd_ws) qk = QkSource{const_cast<void*>(fwd_ws), make_layout(*p, PASS_FWD)};
+    const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
+    const int groups = head_groups(*p).count;
+    for (int g = 0; g < groups; ++g) run_bwd_group(*p, a, g, 3, 0, st);
     return hip_status();
 }
 
 int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
                 const float* LSE, const void* dO, void* dQ, void* dK, void* dV, const void* fwd_ws,
                 size_t fwd_ws_bytes, void* ws, size_t ws_bytes, void* stream) {
-    for (int stage : {SAGEBWD_STAGE_BWD_PREPARE, SAGEBWD_STAGE_BWD_DKDV, SAGEBWD_STAGE_BWD_DQ}) {
-        const int rc = sagebwd_bwd_stage(p, stage, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes, ws,
-                                         ws_bytes, stream);
-        if (rc) return rc;
-    }
-    return SAGEBWD_OK;
+    return bwd_pass(p, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, int kblock, const void* Q,
@@ -369,8 +458,9 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
     a.dump_bh = bh;
     a.dump_i = qblock;
     a.dump_t = kblock;
-    if (kernel == 1) launch_bwd_dkdv(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, (hipStream_t)stream, true);
-    else launch_bwd_dq(a, p->B * p->H, p->causal, p->smooth_q, p->int8_dp, (hipStream_t)stream, true);
+    // the head group holding the dumped head: its dK/dV kernel (which the dQ
+    // kernel reads), and for kernel 2 its dQ kernel
+    run_bwd_group(*p, a, bh / head_groups(*p).heads, kernel == 1 ? 1 : 3, kernel, (hipStream_t)stream);
     return hip_status();
 }
 

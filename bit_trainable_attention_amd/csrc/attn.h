@@ -40,6 +40,9 @@ struct BwdArgs {
     const uint16_t *q_in, *k_in;       // bf16 Q, K as passed in [BH][N][64] (QK-norm gradient)
     const float *rq, *rk;              // QK-norm factors [BH][Np], or null (no QK-norm)
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
+    int8_t* ds_codes;                  // dS codes of every computed tile [BH][ntiles][4096] (see ds_tile_index)
+    float* ds_scale;                   // their block scales [BH][ntiles]
+    size_t ntiles;                     // tiles per head: T (T + 1) / 2 causal, T^2 otherwise
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
     uint8_t* dump;                     // tile dump (debug instantiation only)
     int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
@@ -49,8 +52,17 @@ int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t
 // int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16
 int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st,
                     bool dump = false);
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st,
-                  bool dump = false);
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, hipStream_t st, bool dump = false);
+
+// Position of the dS tile (query block i, key block t) among the tiles of
+// its head: query-block major, so the tiles of one query block are
+// contiguous; causal heads keep only t <= i.
+__host__ __device__ inline size_t ds_tile_index(bool causal, int i, int t, int T) {
+    return causal ? (size_t)i * (i + 1) / 2 + t : (size_t)i * T + t;
+}
+__host__ __device__ inline size_t ds_tiles_per_head(bool causal, int T) {
+    return causal ? (size_t)T * (T + 1) / 2 : (size_t)T * T;
+}
 
 template <class T>
 __device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }

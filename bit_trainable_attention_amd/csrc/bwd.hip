@@ -12,15 +12,13 @@
 //   k_bwd_dkdv  a workgroup of 4 waves owns two 64-key blocks (each wave 32
 //               keys) and walks the query blocks.  It computes S (lane = key),
 //               so P and dS codes leave the accumulator as the A operand of
-//               P^T dO and dS^T Q (contraction over queries).
-//   k_bwd_dq    a workgroup of 4 waves owns two 64-query blocks (each wave 32
-//               queries) and walks the key blocks.  It computes S^T (lane =
-//               query), so dS^T codes feed K^T dS^T directly.
+//               P^T dO and dS^T Q (contraction over queries).  It also stores
+//               every tile's dS codes and scale in the workspace.
+//   k_bwd_dq    each wave owns 32 queries and streams the stored dS codes of
+//               its query block: dQ = sum_t s_dS s_K (dS codes K codes), with
+//               no recomputation of S, P or dS.
 // A 64x64 quantization tile of P or dS is held by a pair of waves, which
-// exchange their partial maxima through LDS.  Both kernels evaluate P and dS
-// with the same float32 operations on bit-identical operands (the FP16 MFMA
-// gives the same bits for dO V^T and V dO^T), so each dS tile, its scale and
-// its codes are identical in the two kernels.  The streamed operand tiles go
+// exchange their partial maxima through LDS.  The streamed operand tiles go
 // through double-buffered LDS, fetched one step ahead; FP16 rows are stored
 // with their 16-byte chunks XOR-swizzled by row so column reads do not
 // collide on LDS banks.
@@ -90,6 +88,14 @@ __device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_wave_base) 
 }
 // Wait for this wave's outstanding vector-memory loads (LDS DMA included).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then s_barrier (a compiler memory barrier too).  Unlike
+// __syncthreads() it does not wait for this wave's global stores; the DMA
+// into LDS is waited for explicitly before it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
 
 // Workgroup -> (head, group) as in the forward: the groups of a head share an
 // XCD when the head count allows.  first_small selects the order of groups
@@ -222,9 +228,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
     float gsum = 0.0f;                                          // sum_i s_dS colsum(dS codes), this half
 
+    // the dS codes of the previous query block: stored just after the next
+    // block's DMA has been waited for, so that the stores complete during
+    // the following compute instead of delaying that wait
+    v4i dc_prev[2] = {v4i{}, v4i{}};
+    float sds_prev = 0.0f;
+    size_t tix_prev = 0;
+    bool have_prev = false;
+    auto store_prev = [&]() {
+        // streaming stores: the codes are read once, by the dQ kernel
+        v4i* dst = (v4i*)(a.ds_codes + tix_prev * 4096) + kh * 128 + lane;
+        __builtin_nontemporal_store(dc_prev[0], dst);
+        __builtin_nontemporal_store(dc_prev[1], dst + 64);
+        if (lane == 0) a.ds_scale[tix_prev] = sds_prev;   // both waves of the tile write the same value
+    };
+
     fetch(i0, 0);
     wait_vmem();
-    __syncthreads();
+    lds_barrier();
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
     for (int i = i0; i < T; ++i) {
         const int buf = (i - i0) & 1;
@@ -258,7 +279,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         // the next query block goes to the other buffer by DMA
         if (more) fetch(i + 1, buf ^ 1);
         wait_vmem();
-        __syncthreads();
+        lds_barrier();
+        if (have_prev) store_prev();
+        have_prev = false;
         float dsm = 0.0f;
         if (active) {
             float sP, invP;
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                         dump_at<float>(dp, dumpoff::F2)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (active) {
             float sdS, invdS;
             block_scale(__builtin_fmaxf(sm.red[1][wave], sm.red[1][wave ^ 1]), sdS, invdS);
@@ -363,6 +386,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                              pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invdS),
                              pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invdS),
                              pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invdS)};
+            // hand the tile's codes and scale to the dQ kernel: 16-byte chunk
+            // (kh * 2 + qs) * 64 + lane of the tile holds this lane's key with
+            // the 16 queries of dc[qs] (the A-operand layout of dS^T Q)
+            dc_prev[0] = dc[0];
+            dc_prev[1] = dc[1];
+            sds_prev = sdS;
+            tix_prev = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, i, kvb, T);
+            have_prev = true;
             if (SMOOTHQ) {
                 int cs = 0;
 #pragma unroll
@@ -385,8 +416,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
+    if (have_prev) store_prev();
 
     // epilogue: dK (x 1/8, plus colsum(dS) mu_q for Q-smoothing) and dV in bf16;
     // lane = channel, registers = keys of this wave's half block
@@ -437,215 +469,106 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ
 
-struct DqSmem {
-    v4i k_r[2][256];     // K row-operand codes (A operand of K Q^T)
-    v4i k_t[2][256];     // K transposed codes (A operand of K^T dS^T)
-    v8h v16[2][512];     // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
-    float bias[2][64];   // Q-smoothing key bias (log2 domain)
-    float sk[2][4];      // [0]: K block scale, [1]: V block scale (all-INT8 dO V^T)
-    float red[4];        // partial dS tile maxima, per wave
+// dQ from the dS codes and scales the key-block kernel stored: for each key
+// block t, dQ_i += s_dS(i,t) s_K,t (dS codes(i,t) K codes_t), so nothing is
+// recomputed.  The stored codes hold, per lane, one key and 16 queries (the
+// layout in which the key-block kernel contracts over queries); dQ contracts
+// over keys, so each 32x32 code block is first transposed on the MFMA
+// itself, as the product with an INT8 identity matrix: D = A I puts query n
+// in lane n and keys 8(r/4) + 4h + r%4 in register r, exact small integers
+// whose low bytes are the codes in the B-operand layout of K^T dS^T.
+//
+// Each wave owns 32 queries and streams its tiles independently (no LDS, no
+// barriers): per key block 2 KB of dS codes (HBM) and the 4 KB K^T code block
+// (shared by every query block of the head, so an L2 hit), prefetched two
+// blocks ahead.  The kernel is bound by the HBM read of the dS codes.
+
+struct DqStep {
+    v4i ds[2];     // dS codes of key halves kh = 0, 1 (A operand, lane = key)
+    v4i kt[4];     // K^T codes: (db * 2 + kh), lane = channel
+    float sds, sk; // s_dS(i, t) and s_K,t
 };
 
-// dS for one 32-query x 64-key half tile in the S^T layout (lane = query,
-// registers = keys); same float32 operations as the key-block kernel.
-template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool MASK>
-__device__ __forceinline__ void dq_dscores(const DqSmem& sm, int buf, const v4i (&qop)[2], const v8h (&doh)[4],
-                                           const v4i (&doop)[2], float wdp,
-                                           float sc, float lq, const v16f& nd, int t, int q, int N, int lane, int h,
-                                           float (&ds)[2][16], uint8_t* dp = nullptr) {
-    const int l32 = lane % 32;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        v16i s = mfma_i8(sm.k_r[buf][(kb * 2 + 0) * 64 + lane], qop[0], v16i{});
-        s = mfma_i8(sm.k_r[buf][(kb * 2 + 1) * 64 + lane], qop[1], s);
-        if (dp) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dump_at<int>(dp, dumpoff::A)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[r];
-        }
-        const int row = 32 * kb + l32;
-        v16f dpd;
-        if (INT8DP) {
-            // (dP - Delta)^T = s_dO s_V (V codes dO codes^T) + (-Delta)
-            const v4i* vr = (const v4i*)sm.v16[buf];
-            v16i ai = mfma_i8(vr[(kb * 2 + 0) * 64 + lane], doop[0], v16i{});
-            ai = mfma_i8(vr[(kb * 2 + 1) * 64 + lane], doop[1], ai);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dpd[r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
-        } else {
-            dpd = mfma_f16(sm.v16[buf][swz(row, 0 + h)], doh[0], nd);
-            dpd = mfma_f16(sm.v16[buf][swz(row, 2 + h)], doh[1], dpd);
-            dpd = mfma_f16(sm.v16[buf][swz(row, 4 + h)], doh[2], dpd);
-            dpd = mfma_f16(sm.v16[buf][swz(row, 6 + h)], doh[3], dpd);
-        }
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (SMOOTHQ) {
-                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
-                bv[0] = b4.x;
-                bv[1] = b4.y;
-                bv[2] = b4.z;
-                bv[3] = b4.w;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * r4 + j;
-                float pv = bwd_prob<SMOOTHQ>(s[r], sc, bv[j], lq);
-                if (MASK) {
-                    const int key = t * BLK + 32 * kb + 8 * r4 + 4 * h + j;
-                    if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
-                }
-                ds[kb][r] = pv * dpd[r];
-            }
-        }
-    }
-}
-
-template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool DUMP>
-__global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
-    __shared__ DqSmem sm;
+template <bool CAUSAL, bool DUMP>
+__global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
     map_group_bwd(a.ngroups, a.BH, false, bh, g);
     const int T = a.T;
     const int qblk = 2 * g + wave / 2, qh = wave % 2;
-    const bool live = qblk < T;
-    const int q = qblk * BLK + 32 * qh + l32;                 // this lane's query (S^T layout)
-    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;
+    if (qblk >= T) return;                                    // waves never synchronize
+    const int q = qblk * BLK + 32 * qh + l32;                 // this lane's query
+    const int t_end = CAUSAL ? qblk + 1 : T;
     const size_t bt = (size_t)bh * T;
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
+    const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
+    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + qh * 64 + lane;
+    const float* dss = a.ds_scale + tile0;
+    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096) + lane;
+    const float* skg = a.sk + bt;
 
-    // persistent operands of this wave's 32 queries: Q codes, and dO in FP16
-    // (or, for the all-INT8 dO V^T, dO codes and the dO block scale)
-    v4i qop[2] = {v4i{}, v4i{}}, doop[2] = {v4i{}, v4i{}};
-    v8h doh[4];
-    float lq = 0.0f, dlq = 0.0f, sQ = 0.0f, sDO = 0.0f;
+    // INT8 identity as the B operand: column n = l32 has its one at k
+    // position n, which lies in half (n % 8) / 4, byte 4 (n / 8) + n % 4
+    v4i eye = v4i{0, 0, 0, 0};
+    if (h == (l32 % 8) / 4) eye[l32 / 8] = 1 << (8 * (l32 % 4));
+
+    auto load = [&](int t, DqStep& s) {
+        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);          // read once
+        s.ds[1] = __builtin_nontemporal_load(dsg + (size_t)t * 256 + 128);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) doh[ks] = v8h{};
-    if (live) {
-        const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
-        qop[0] = src[(qh * 2 + 0) * 64 + lane];
-        qop[1] = src[(qh * 2 + 1) * 64 + lane];
-        if (INT8DP) {
-            const v4i* ds = (const v4i*)(a.do_r + (bt + qblk) * 4096);
-            doop[0] = ds[(qh * 2 + 0) * 64 + lane];
-            doop[1] = ds[(qh * 2 + 1) * 64 + lane];
-            sDO = a.sdo[bt + qblk];
-        } else {
+        for (int j = 0; j < 4; ++j) s.kt[j] = ktg[(size_t)t * 256 + j * 64];
+        s.sds = dss[t];
+        s.sk = skg[t];
+    };
+    v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
+    auto step = [&](int t, const DqStep& s) {
+        v4i dc[2];
+        v16i tr[2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) doh[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+        for (int kh = 0; kh < 2; ++kh) {
+            tr[kh] = mfma_i8(s.ds[kh], eye, v16i{});
+            dc[kh] = v4i{(int)pack4(tr[kh][0], tr[kh][1], tr[kh][2], tr[kh][3]),
+                         (int)pack4(tr[kh][4], tr[kh][5], tr[kh][6], tr[kh][7]),
+                         (int)pack4(tr[kh][8], tr[kh][9], tr[kh][10], tr[kh][11]),
+                         (int)pack4(tr[kh][12], tr[kh][13], tr[kh][14], tr[kh][15])};
         }
-        lq = a.lse2[rowbase + q];
-        dlq = a.delta[rowbase + q];
-        sQ = a.sq[bt + qblk];
-    }
-
-    const v4i* krg = (const v4i*)(a.k_r + bt * 4096);
-    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
-    // key block t -> LDS buffer b by DMA; LDS slot s of the FP16 V tile
-    // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
-    // (the all-INT8 dO V^T stages the V row-operand codes there instead, and
-    // the V block scale next to the K block scale)
-    auto fetch = [&](int t, int b) {
-        dma16_to_lds(krg + (size_t)t * 256 + tid, &sm.k_r[b][64 * wave]);
-        dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.k_t[b][64 * wave]);
-        if (INT8DP) {
-            dma16_to_lds((const v4i*)(a.v_r + bt * 4096) + (size_t)t * 256 + tid, (v4i*)sm.v16[b] + 64 * wave);
-        } else {
-            const v4i* vs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
+        const float wq = s.sds * s.sk;
+        const bool dump_here = DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t;
+        if (dump_here) {
+            uint8_t* dp = a.dump;
+            if (lane == 0 && qh == 0) dump_at<float>(dp, dumpoff::SC)[0] = s.sds;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int s = 256 * j + tid, row = s / 8;
-                dma16_to_lds(vs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    dp[dumpoff::C1 + (q % 64) * 64 + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4)] = (uint8_t)tr[kh][r];
+        }
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            v16i acc = mfma_i8(s.kt[db * 2 + 0], dc[0], v16i{});
+            acc = mfma_i8(s.kt[db * 2 + 1], dc[1], acc);
+            if (dump_here) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    dump_at<int>(a.dump, dumpoff::ACC1)[(q % 64) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc[r];
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
         }
-        if (SMOOTHQ && wave == 0 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
-        if (wave == 1 && lane < (INT8DP ? 2 : 1)) dma4_to_lds((lane == 0 ? a.sk : a.sv) + bt + t, &sm.sk[b][0]);
     };
 
-    v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
-    v16f nd;                         // -Delta of this lane's query: accumulator input of V dO^T
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nd[r] = dlq;
-    fetch(0, 0);
-    wait_vmem();
-    __syncthreads();
-    const bool ragged = (a.N & (BLK - 1)) != 0;
-    for (int t = 0; t <= t_last_wg; ++t) {
-        const int buf = t & 1;
-        const bool more = t < t_last_wg;
-        const bool active = live && (!CAUSAL || t <= qblk);
-        const bool masked = (CAUSAL && t == qblk) || (ragged && t == T - 1);
-        const float sK = sm.sk[buf][0];
-        float ds[2][16];             // [kb]: lane = query, regs = keys
-        uint8_t* dp = (DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t) ? a.dump : nullptr;
-        if (active) {
-            const float sc = tile_scale(sQ, sK);
-            const float wdp = INT8DP ? sDO * sm.sk[buf][1] : 0.0f;   // s_dO s_V, as in the key-block kernel
-            if (masked)
-                dq_dscores<CAUSAL, SMOOTHQ, INT8DP, true>(sm, buf, qop, doh, doop, wdp, sc, lq, nd, t, q, a.N, lane, h,
-                                                          ds, DUMP ? dp : nullptr);
-            else
-                dq_dscores<CAUSAL, SMOOTHQ, INT8DP, false>(sm, buf, qop, doh, doop, wdp, sc, lq, nd, t, q, a.N, lane,
-                                                           h, ds, DUMP ? dp : nullptr);
-            if (DUMP && dp) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<float>(dp, dumpoff::F1)[(q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = ds[kb][r];
-            }
-            float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
-                m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
-            }
-            const float dsm = wave_max64(max3f(m0, m1, m1));
-            if (lane == 0) sm.red[wave] = dsm;
-        }
-        // the next key block goes to the other buffer by DMA; its latency is
-        // covered by the other workgroups on the CU (three per CU)
-        if (more) fetch(t + 1, buf ^ 1);
-        wait_vmem();
-        __syncthreads();
-        if (active) {
-            float sdS, invdS;
-            block_scale(__builtin_fmaxf(sm.red[wave], sm.red[wave ^ 1]), sdS, invdS);
-            if (DUMP && dp) {
-                if (lane == 0 && qh == 0) dump_at<float>(dp, dumpoff::SC)[0] = sdS;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dp[dumpoff::C1 + (q % 64) * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] =
-                            (uint8_t)code_bits(ds[kb][r], invdS);
-            }
-            v4i dc[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                dc[ks] = v4i{pack_codes(ds[ks][0], ds[ks][1], ds[ks][2], ds[ks][3], invdS),
-                             pack_codes(ds[ks][4], ds[ks][5], ds[ks][6], ds[ks][7], invdS),
-                             pack_codes(ds[ks][8], ds[ks][9], ds[ks][10], ds[ks][11], invdS),
-                             pack_codes(ds[ks][12], ds[ks][13], ds[ks][14], ds[ks][15], invdS)};
-            const float wq = sdS * sK;
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(sm.k_t[buf][(db * 2 + 0) * 64 + lane], dc[0], v16i{});
-                acc = mfma_i8(sm.k_t[buf][(db * 2 + 1) * 64 + lane], dc[1], acc);
-                if (DUMP && dp) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<int>(dp, dumpoff::ACC1)[(q % 64) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc[r];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
-            }
-        }
-        __syncthreads();
+    DqStep s0, s1;
+    load(0, s0);
+    if (1 < t_end) load(1, s1);
+    int t = 0;
+    for (; t + 1 < t_end; t += 2) {
+        step(t, s0);
+        if (t + 2 < t_end) load(t + 2, s0);
+        step(t + 1, s1);
+        if (t + 3 < t_end) load(t + 3, s1);
     }
+    if (t < t_end) step(t, s0);
 
     // dQ (x 1/8); with QK-norm then dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
     // other 32 channels of this lane's query being in the other half of the wave
@@ -653,7 +576,7 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dq[db][r] *= 0.125f;
-    const bool qok = live && q < a.N;
+    const bool qok = q < a.N;
     if (a.rq) {
         const float rr = qok ? a.rq[rowbase + q] : 0.0f;
         const uint16_t* qrow = a.q_in + ((size_t)bh * a.N + (qok ? q : 0)) * HD;
@@ -671,8 +594,8 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) part = __builtin_fmaf(dq[db][4 * r4 + j], qn[db][4 * r4 + j], part);
             }
-        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        const float mean = (__uint_as_float(s[0]) + __uint_as_float(s[1])) * (1.0f / HD);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        const float mean = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (1.0f / HD);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -719,9 +642,18 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
     SAGEBWD_LAUNCH_BWD(k_bwd_dkdv)
 }
 
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st, bool dump) {
-    SAGEBWD_LAUNCH_BWD(k_bwd_dq)
-}
 #undef SAGEBWD_LAUNCH_BWD
+
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, hipStream_t st, bool dump) {
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
+    if (causal) {
+        if (dump) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);
+    } else {
+        if (dump) hipLaunchKernelGGL((k_bwd_dq<false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<false, false>), grid, block, 0, st, a);
+    }
+    return 0;
+}
 
 }  // namespace sagebwd

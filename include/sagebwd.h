@@ -53,7 +53,7 @@ extern "C" {
 typedef struct sagebwd_params {
     int32_t B;          /* batch, >= 1 */
     int32_t H;          /* heads, >= 1 */
-    int32_t N;          /* tokens (queries = keys), 1 <= N <= 2^20 */
+    int32_t N;          /* tokens (queries = keys), 1 <= N <= 2^18 */
     int32_t D;          /* head dimension, must be 64 */
     int32_t causal;     /* 0 or 1 */
     int32_t smooth_q;   /* 0 or 1: subtract the per-head token mean of Q */
@@ -82,7 +82,13 @@ typedef struct sagebwd_params {
 #define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
 
 /* Workspace bytes needed by sagebwd_fwd / sagebwd_bwd for these params;
- * 0 if the params are invalid. */
+ * 0 if the params are invalid.  The forward's grows linearly with B*H*N.
+ * The backward's also holds the INT8 dS codes of every computed 64x64 tile
+ * of a group of heads (4096 bytes per tile: T(T+1)/2 tiles per head when
+ * causal, T^2 otherwise, T = ceil(N/64)), which its dK/dV kernel writes and
+ * its dQ kernel reads instead of recomputing them; a group is as many heads
+ * as fit in 16 GiB of codes, at least one, the heads split evenly over the
+ * groups (e.g. B=1, H=32, N=16384 causal: one group, 4.3 GB). */
 size_t sagebwd_fwd_workspace_size(const sagebwd_params* p);
 size_t sagebwd_bwd_workspace_size(const sagebwd_params* p);
 
@@ -114,17 +120,21 @@ int sagebwd_bwd(const sagebwd_params* p,
                 void* ws, size_t ws_bytes, void* stream);
 
 /* Stages.  sagebwd_fwd runs FWD_PREPARE then FWD_ATTN; sagebwd_bwd runs
- * BWD_PREPARE, BWD_DKDV, BWD_DQ, all on the same stream.  The stage calls run
- * one stage each, for callers that schedule or time them separately; a stage
- * reads what the earlier stages of its pass wrote into ``ws`` (same params,
- * inputs and workspace), and the full sequence is exactly the pass.
+ * BWD_PREPARE, then BWD_DKDV and BWD_DQ for each head group in turn, all on
+ * the same stream.  The stage calls run one stage each, for callers that
+ * schedule or time them separately; a stage reads what the earlier stages of
+ * its pass wrote into ``ws`` (same params, inputs and workspace), and the
+ * full sequence is exactly the pass.  BWD_DKDV and BWD_DQ return
+ * SAGEBWD_ERR_UNSUPPORTED when the backward has more than one head group
+ * (sagebwd_bwd handles that case itself).
  *   FWD_PREPARE  smoothing means; Q, K, V block quantization
  *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
  *   BWD_PREPARE  (without fwd_ws) means and quantization again; then
  *                -Delta, log2 LSE, dO codes, FP16 copies of dO and V
  *                (int8_dp: also row-layout dO codes, V codes and scales)
- *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T)
- *   BWD_DQ       dQ (INT8 QK^T and dS K; FP16 dO V^T) */
+ *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T); also
+ *                stores every tile's dS codes and scale in ws
+ *   BWD_DQ       dQ (INT8 dS K from the stored dS codes) */
 #define SAGEBWD_STAGE_FWD_PREPARE 0
 #define SAGEBWD_STAGE_FWD_ATTN    1
 #define SAGEBWD_STAGE_BWD_PREPARE 2
@@ -173,6 +183,13 @@ const char* sagebwd_status_string(int status);
  *   19 V_R    int8  [BH][T][4096]    V codes, row operand layout (int8_dp only)
  *   20 RQ     float32 [BH][Np]       QK-norm factor r of each Q token (qk_norm only; 0 past N)
  *   21 RK     float32 [BH][Np]       likewise for K
+ *   22 DS     int8  [G][tiles][4096] dS codes of one head group (G heads), tile
+ *                                    (i, t) at i(i+1)/2 + t causal, i T + t
+ *                                    otherwise; in a tile, 16-byte chunk
+ *                                    (kh*2 + qs)*64 + l holds key 32 kh + l%32
+ *                                    and byte b the query
+ *                                    32 qs + 8(b/4) + 4(l/32) + b%4
+ *   23 DS_SCALE float32 [G][tiles]   their block scales s_dS
  * with T = ceil(N/64), Np = 64 T.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
  * 64 channels, element (token r, channel c) sits at byte
  *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16
@@ -191,9 +208,9 @@ const char* sagebwd_status_string(int status);
  *     A at 0, P f32[q][k] at 16384, P codes u8[q][k] at 32768,
  *     P^T dO i32[k][c] at 36864, dS f32[q][k] at 53248, dS codes u8[q][k] at
  *     69632, dS^T Q i32[k][c] at 73728, s_P and s_dS f32 at 90112
- *   kernel 2 (dQ; runs the backward preparation first; writes dQ):
- *     A at 0, dS f32[q][k] at 16384, dS codes u8[q][k] at 32768,
- *     dS K i32[q][c] at 36864, s_dS f32 at 90112
+ *   kernel 2 (dQ; runs the backward preparation and the dK/dV kernel first;
+ *     writes dK, dV, dQ): the dS codes it read, transposed, u8[q][k] at
+ *     32768, dS K i32[q][c] at 36864, s_dS f32 at 90112
  * (q, k: query and key within the blocks; c: channel), so that the INT8
  * codes, block scales and integer tile products can be re-derived exactly
  * from the kernel's own pre-quantization values.  Tiles above the causal

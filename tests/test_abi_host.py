@@ -68,7 +68,7 @@ def test_param_validation(lib):
     assert call_bwd(lib, P(int8_dp=-1)) == INVALID
     assert call_fwd(lib, P(qk_norm=3)) == INVALID
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED
-    assert call_fwd(lib, P(N=(1 << 20) + 1)) == UNSUPPORTED
+    assert call_fwd(lib, P(N=(1 << 18) + 1)) == UNSUPPORTED
     assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED
     assert call_bwd(lib, P(D=32)) == UNSUPPORTED
     assert call_bwd(lib, P(N=-5)) == INVALID
@@ -126,7 +126,8 @@ def test_ws_regions_layout(lib, int8_dp, qk_norm):
                   "CORR": BH * Np * 4, "BIAS": BH * Np * 4, "NDELTA": BH * Np * 4, "LSE2": BH * Np * 4,
                   "DO16": BH * Np * 128, "V16": BH * Np * 128,
                   "DO_R": int8_dp * BH * T * 4096, "V_R": int8_dp * BH * T * 4096,
-                  "RQ": qk_norm * BH * Np * 4, "RK": qk_norm * BH * Np * 4}
+                  "RQ": qk_norm * BH * Np * 4, "RK": qk_norm * BH * Np * 4,
+                  "DS": BH * T * T * 4096, "DS_SCALE": BH * T * T * 4}
         spans = []
         for name, rid in sb.REGIONS.items():
             off, nb = sb.ws_region(p, rid)
@@ -184,3 +185,31 @@ def test_forward_workspace_validation(lib):
     assert call_bwd(lib, p, ws=ws, nbytes=bsz, fwd_ws=ws - fsz + 256, fwd_nbytes=fsz) == INVALID      # overlaps the start
     # the forward layout holds every region the backward reads from it
     assert fsz < bsz
+
+
+def _head_groups(BH, T, causal):
+    """The grouping rule the header documents: as many heads as fit in
+    16 GiB of dS codes (4096 bytes per computed tile), at least one, split
+    into equal groups."""
+    nt = T * (T + 1) // 2 if causal else T * T
+    hmax = max(1, (16 << 30) // (nt * 4096))
+    count = -(-BH // hmax)
+    return -(-BH // count), count, nt
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 32, 16384, 1), (2, 30, 17776, 0), (1, 4, 1 << 18, 1), (8, 16, 2048, 1),
+                                          (3, 1, 100, 0)])
+def test_backward_head_groups(lib, B, H, N, causal):
+    """The dS-code region holds one head group; the two attention stages of
+    the backward can only be called on their own when there is one group
+    (sagebwd_bwd runs the groups itself).  Every case fails before any HIP
+    call."""
+    p = P(B=B, H=H, N=N, causal=causal)
+    T = (N + 63) // 64
+    heads, count, nt = _head_groups(B * H, T, causal)
+    assert sb.ws_region(p, "DS")[1] == heads * nt * 4096
+    assert sb.ws_region(p, "DS_SCALE")[1] == heads * nt * 4
+    b = lambda stage: lib.sagebwd_bwd_stage(ctypes.byref(p), stage, *([FAKE] * 9), None, 0, FAKE, 1 << 50, None)
+    if count > 1:
+        assert b(3) == UNSUPPORTED and b(4) == UNSUPPORTED
+    assert (count > 1) == ((B, H, N) in ((2, 30, 17776), (1, 4, 1 << 18)))

@@ -12,8 +12,8 @@ values exactly:
   fwd    P~ codes = rne(127 P^) of the dumped values, P~V = codes V_code
   dkdv   s_P, P codes = F3 of the dumped P; P^T dO = codes^T dO_code;
          s_dS, dS codes = F3 of the dumped dS; dS^T Q = codes^T Q_code
-  dq     the same dS tile, scale and codes as the dK/dV kernel (bit for bit);
-         dS K = codes K_code
+  dq     the dS codes and scale the dK/dV kernel stored, after its
+         transposition (bit for bit); dS K = codes K_code
 The codes the oracle forms from its own float64 P and dS agree except at
 rounding boundaries; that rate is reported and bounded."""
 import numpy as np
@@ -100,11 +100,10 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         assert np.array_equal(_blk(d1, C2, np.int8).astype(np.int64), cdS.astype(np.int64)), ("dS codes", i, t)
         assert np.array_equal(_blk(d1, ACC2, np.int32).astype(np.int64),
                               (cdS.T @ pp.qc[rows]).astype(np.int64)), ("dS^T Q", i, t)
-        # ---- dQ kernel: the same dS tile, bit for bit
+        # ---- dQ kernel: the dK/dV kernel's dS codes and scale, read back and
+        # transposed, bit for bit
         d2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
                            int8_dp).numpy().tobytes()
-        assert np.array_equal(_blk(d2, A, np.int32), a_ref.astype(np.int32)), ("dq A", i, t)
-        assert np.array_equal(_blk(d2, F1, np.float32).view(np.uint32), dS.view(np.uint32)), ("dq dS bits", i, t)
         assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32)
         assert np.array_equal(_blk(d2, C1, np.int8), _blk(d1, C2, np.int8)), ("dq codes", i, t)
         assert np.array_equal(_blk(d2, ACC1, np.int32).astype(np.int64),
