@@ -67,15 +67,6 @@ __host__ __device__ inline size_t ds_tiles_per_head(bool causal, int T) {
 template <class T>
 __device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }
 
-// Score-to-probability step shared by both backward kernels, so that the two
-// recompute bit-identical P (and hence identical dS codes): z is the
-// log2-domain score, lse2 the log2-domain log-sum-exp of its row.
-template <bool SMOOTHQ>
-__device__ __forceinline__ float bwd_prob(int acc, float sc, float bias, float lse2) {
-    const float a = (float)acc;
-    if (SMOOTHQ) return __builtin_amdgcn_exp2f(__builtin_fmaf(a, sc, bias) - lse2);
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(a, sc, -lse2));
-}
 __device__ __forceinline__ float tile_scale(float sq, float sk) { return (sq * sk) * SCORE_SCALE_LOG2; }
 
 }  // namespace sagebwd

@@ -128,35 +128,35 @@ struct DkdvSmem {
 };
 
 // P for one 64-query x 32-key half tile in the S layout (lane = key,
-// registers = queries).  MASK only on the causal diagonal tile and the ragged
-// last key block, so the common path carries no per-element selects.
-template <bool CAUSAL, bool SMOOTHQ, bool MASK>
-__device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float kbias,
+// registers = queries): P = exp2(sc A + (bias_j - lse2_i)), log2 domain.  The
+// outer difference bias_j - lse2_i is the rank-2 product [-lse2 | 1] [1 | bias]^T,
+// formed on the FP32 MFMA (32x32x2: lane l carries A[l%32][l/32] and
+// B[l/32][l%32]) in the accumulator layout of the score product, so each score
+// costs one FMA before its exp.  MASK only on the causal diagonal tile and the
+// ragged last key block, so the common path carries no per-element selects.
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float brow,
                                            int i, int key, int N, int lane, int h, float (&p)[2][16],
                                            uint8_t* dp = nullptr) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
         s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
+        const float arow = h == 0 ? -sm.lse2[buf][32 * qb + lane % 32] : 1.0f;
+        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
         if (dp) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 dump_at<int>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = s[r];
         }
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * r4 + j;
-                float pv = bwd_prob<SMOOTHQ>(s[r], sc, kbias, lv[j]);
-                if (MASK) {
-                    const int q = i * BLK + 32 * qb + 8 * r4 + 4 * h + j;
-                    if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
-                }
-                p[qb][r] = pv;
+        for (int r = 0; r < 16; ++r) {
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], sc, corr[r]));
+            if (MASK) {
+                const int q = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
+                if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
             }
+            p[qb][r] = pv;
         }
     }
 }
@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         if (SMOOTHQ) kbias = a.bias[rowbase + key];
         sK = a.sk[bt + kvb];
     }
+    const float brow = h == 0 ? 1.0f : kbias;   // B operand of the rank-2 score correction
 
     const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
     // query block i -> LDS buffer b by DMA; LDS slot s of the FP16 dO tile
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         const float sc = tile_scale(sQ, sK);
         uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
         if (active) {
-            if (masked) dkdv_probs<CAUSAL, SMOOTHQ, true>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
-            else dkdv_probs<CAUSAL, SMOOTHQ, false>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+            if (masked) dkdv_probs<CAUSAL, true>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+            else dkdv_probs<CAUSAL, false>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
             if (DUMP && dp) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -483,9 +484,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 // (shared by every query block of the head, so an L2 hit), prefetched two
 // blocks ahead.  The kernel is bound by the HBM read of the dS codes.
 
+constexpr int DQ_DEPTH = 4;
+
 struct DqStep {
     v4i ds[2];     // dS codes of key halves kh = 0, 1 (A operand, lane = key)
-    v4i kt[4];     // K^T codes: (db * 2 + kh), lane = channel
     float sds, sk; // s_dS(i, t) and s_K,t
 };
 
@@ -513,16 +515,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     v4i eye = v4i{0, 0, 0, 0};
     if (h == (l32 % 8) / 4) eye[l32 / 8] = 1 << (8 * (l32 % 4));
 
+    // the dS codes (read once, from HBM) are prefetched DQ_DEPTH key blocks
+    // ahead; the K^T codes (L2 hits) are loaded at their step
     auto load = [&](int t, DqStep& s) {
-        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);          // read once
+        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);
         s.ds[1] = __builtin_nontemporal_load(dsg + (size_t)t * 256 + 128);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s.kt[j] = ktg[(size_t)t * 256 + j * 64];
         s.sds = dss[t];
         s.sk = skg[t];
     };
     v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
     auto step = [&](int t, const DqStep& s) {
+        v4i kt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kt[j] = ktg[(size_t)t * 256 + j * 64];
         v4i dc[2];
         v16i tr[2];
 #pragma unroll
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         }
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-            v16i acc = mfma_i8(s.kt[db * 2 + 0], dc[0], v16i{});
-            acc = mfma_i8(s.kt[db * 2 + 1], dc[1], acc);
+            v16i acc = mfma_i8(kt[db * 2 + 0], dc[0], v16i{});
+            acc = mfma_i8(kt[db * 2 + 1], dc[1], acc);
             if (dump_here) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -558,17 +563,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         }
     };
 
-    DqStep s0, s1;
-    load(0, s0);
-    if (1 < t_end) load(1, s1);
-    int t = 0;
-    for (; t + 1 < t_end; t += 2) {
-        step(t, s0);
-        if (t + 2 < t_end) load(t + 2, s0);
-        step(t + 1, s1);
-        if (t + 3 < t_end) load(t + 3, s1);
+    DqStep ring[DQ_DEPTH];
+#pragma unroll
+    for (int j = 0; j < DQ_DEPTH; ++j)
+        if (j < t_end) load(j, ring[j]);
+    for (int t0 = 0; t0 < t_end; t0 += DQ_DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DQ_DEPTH; ++j) {
+            const int t = t0 + j;
+            if (t < t_end) {
+                step(t, ring[j]);
+                if (t + DQ_DEPTH < t_end) load(t + DQ_DEPTH, ring[j]);
+            }
+        }
     }
-    if (t < t_end) step(t, s0);
 
     // dQ (x 1/8); with QK-norm then dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
     // other 32 channels of this lane's query being in the other half of the wave
