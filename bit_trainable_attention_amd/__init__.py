@@ -31,7 +31,7 @@ REGIONS = {"MU_Q": 0, "MU_K": 1, "Q_R": 2, "K_R": 3, "V_T": 4, "Q_T": 5, "K_T": 
            "DS": 22, "DS_SCALE": 23}
 
 
-STAGES = {"FWD_PREPARE": 0, "FWD_ATTN": 1, "BWD_PREPARE": 2, "BWD_DKDV": 3, "BWD_DQ": 4}
+STAGES = {"FWD_PREPARE": 0, "FWD_ATTN": 1, "BWD_PREPARE": 2, "BWD_DKDV": 3, "BWD_DQ": 4, "BWD_ATTN": 5}
 
 
 class SageBwdError(RuntimeError):

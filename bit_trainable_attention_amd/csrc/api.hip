@@ -375,7 +375,8 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
                       const void* fwd_ws, size_t fwd_ws_bytes, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_params(p);
     if (rc) return rc;
-    if (stage != SAGEBWD_STAGE_BWD_PREPARE && stage != SAGEBWD_STAGE_BWD_DKDV && stage != SAGEBWD_STAGE_BWD_DQ)
+    if (stage != SAGEBWD_STAGE_BWD_PREPARE && stage != SAGEBWD_STAGE_BWD_DKDV && stage != SAGEBWD_STAGE_BWD_DQ &&
+        stage != SAGEBWD_STAGE_BWD_ATTN)
         return SAGEBWD_ERR_INVALID_ARG;
     for (const void* t : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV}) {
         if ((rc = check_tensor(t))) return rc;
@@ -397,10 +398,15 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         run_bwd_pre(*p, L, qk, V, O, LSE, dO, ws, st);
         return hip_status();
     }
-    // the two attention stages hand the dS codes of all heads from one to the
-    // other, which needs a single head group
-    if (head_groups(*p).count != 1) return SAGEBWD_ERR_UNSUPPORTED;
     const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
+    const int groups = head_groups(*p).count;
+    if (stage == SAGEBWD_STAGE_BWD_ATTN) {
+        for (int g = 0; g < groups; ++g) run_bwd_group(*p, a, g, 3, 0, st);
+        return hip_status();
+    }
+    // the two attention stages on their own hand the dS codes of all heads
+    // from one to the other, which needs a single head group
+    if (groups != 1) return SAGEBWD_ERR_UNSUPPORTED;
     run_bwd_group(*p, a, 0, stage == SAGEBWD_STAGE_BWD_DKDV ? 1 : 2, 0, st);
     return hip_status();
 }
@@ -413,13 +419,8 @@ static int bwd_pass(const sagebwd_params* p, const void* Q, const void* K, const
     int rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes,
                                ws, ws_bytes, st);
     if (rc) return rc;
-    const Layout L = make_layout(*p, PASS_BWD);
-    QkSource qk{ws, L};
-    if (fwd_ws) qk = QkSource{const_cast<void*>(fwd_ws), make_layout(*p, PASS_FWD)};
-    const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
-    const int groups = head_groups(*p).count;
-    for (int g = 0; g < groups; ++g) run_bwd_group(*p, a, g, 3, 0, st);
-    return hip_status();
+    return sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_ATTN, Q, K, V, O, LSE, dO, dQ, dK, dV, fwd_ws, fwd_ws_bytes, ws,
+                             ws_bytes, st);
 }
 
 int sagebwd_bwd(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,

@@ -120,13 +120,13 @@ int sagebwd_bwd(const sagebwd_params* p,
                 void* ws, size_t ws_bytes, void* stream);
 
 /* Stages.  sagebwd_fwd runs FWD_PREPARE then FWD_ATTN; sagebwd_bwd runs
- * BWD_PREPARE, then BWD_DKDV and BWD_DQ for each head group in turn, all on
- * the same stream.  The stage calls run one stage each, for callers that
- * schedule or time them separately; a stage reads what the earlier stages of
- * its pass wrote into ``ws`` (same params, inputs and workspace), and the
- * full sequence is exactly the pass.  BWD_DKDV and BWD_DQ return
- * SAGEBWD_ERR_UNSUPPORTED when the backward has more than one head group
- * (sagebwd_bwd handles that case itself).
+ * BWD_PREPARE then BWD_ATTN, all on the same stream.  The stage calls run one
+ * stage each, for callers that schedule or time them separately; a stage
+ * reads what the earlier stages of its pass wrote into ``ws`` (same params,
+ * inputs and workspace), and the full sequence is exactly the pass.
+ * BWD_ATTN is BWD_DKDV then BWD_DQ for each head group in turn; BWD_DKDV and
+ * BWD_DQ on their own return SAGEBWD_ERR_UNSUPPORTED when the backward has
+ * more than one head group.
  *   FWD_PREPARE  smoothing means; Q, K, V block quantization
  *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
  *   BWD_PREPARE  (without fwd_ws) means and quantization again; then
@@ -134,12 +134,14 @@ int sagebwd_bwd(const sagebwd_params* p,
  *                (int8_dp: also row-layout dO codes, V codes and scales)
  *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T); also
  *                stores every tile's dS codes and scale in ws
- *   BWD_DQ       dQ (INT8 dS K from the stored dS codes) */
+ *   BWD_DQ       dQ (INT8 dS K from the stored dS codes)
+ *   BWD_ATTN     BWD_DKDV and BWD_DQ over every head group */
 #define SAGEBWD_STAGE_FWD_PREPARE 0
 #define SAGEBWD_STAGE_FWD_ATTN    1
 #define SAGEBWD_STAGE_BWD_PREPARE 2
 #define SAGEBWD_STAGE_BWD_DKDV    3
 #define SAGEBWD_STAGE_BWD_DQ      4
+#define SAGEBWD_STAGE_BWD_ATTN    5
 int sagebwd_fwd_stage(const sagebwd_params* p, int stage,
                       const void* Q, const void* K, const void* V,
                       void* O, float* LSE,

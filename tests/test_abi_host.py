@@ -164,10 +164,10 @@ def test_stage_validation(lib):
     b = lambda stage, nb=1 << 40: lib.sagebwd_bwd_stage(ctypes.byref(p), stage, *([FAKE] * 9), None, 0, FAKE, nb, None)
     for bad in (-1, 2, 3, 4, 5):
         assert f(bad) == INVALID
-    for bad in (-1, 0, 1, 5):
+    for bad in (-1, 0, 1, 6):
         assert b(bad) == INVALID
     assert f(0, nb=1) == WORKSPACE and f(1, nb=1) == WORKSPACE
-    assert b(2, nb=1) == WORKSPACE and b(3, nb=1) == WORKSPACE and b(4, nb=1) == WORKSPACE
+    assert b(2, nb=1) == WORKSPACE and b(3, nb=1) == WORKSPACE and b(4, nb=1) == WORKSPACE and b(5, nb=1) == WORKSPACE
 
 
 def test_forward_workspace_validation(lib):
