@@ -73,7 +73,10 @@ __device__ __forceinline__ int pack_codes(float x0, float x1, float x2, float x3
     return (int)pack4(code_bits(x0, inv), code_bits(x1, inv), code_bits(x2, inv), code_bits(x3, inv));
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// FP16 rows of 8 chunks of 16 bytes in LDS: chunk c of row r sits at slot
+// c ^ ((r / 2) % 8), so any 16 consecutive rows read at one chunk cover all
+// 64 banks (with c ^ (r % 8), rows r and r + 8 would collide).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
 // Global -> LDS copies that bypass the registers (global_load_lds): every
 // lane of the wave moves 16 (4) bytes from its own global address to
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 
     const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
     // query block i -> LDS buffer b by DMA; LDS slot s of the FP16 dO tile
-    // holds global chunk (s / 8, (s % 8) ^ (s / 8 % 8)), the swizzled layout
+    // holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
     // (the all-INT8 dO V^T stages the dO row-operand codes there instead)
     const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
     const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int s = 256 * j + tid, row = s / 8;
-                dma16_to_lds(hs + row * 8 + ((s % 8) ^ (row % 8)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
+                dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
             }
         }
         if (wave == 0 && lane < 32)
