@@ -24,10 +24,13 @@ Modules:
                INT8 codes, block scales and integer tile products as the method
                defines them; a ``rounding=False`` switch removes every rounding
                step so the result must collapse to ``exact``.
+  mxfp8     -- the FP8 variant for MI355X's scaled matrix instructions: OCP
+               E4M3 codes with one power-of-two (E8M0) scale per 32 x 32 block,
+               step by step, with the same ``rounding=False`` switch.
   metrics   -- cosine similarity, relative L2, L1, RMSE.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against something
 other than itself: finite differences, closed forms, invariants, brute-force
 integer products, an exact-rational quantizer and the rounding-free reduction.
 """
-from . import exact, faithful, metrics  # noqa: F401
+from . import exact, faithful, metrics, mxfp8  # noqa: F401

@@ -1,0 +1,358 @@
+"""MXFP8 SageBwd forward and backward (test infrastructure only).
+
+The SageBwd page compares INT8 with FP8 quantization of the same attention and
+finds INT8 more accurate (dQ L1 error 0.0290 against 0.0696, and a higher
+GSM8K score after fine-tuning).  MI355X runs FP8 matmuls at the INT8 rate and
+applies power-of-two block scales inside the matrix instruction, so this
+module defines the FP8 variant in the form that hardware computes: OCP FP8
+E4M3 elements with one E8M0 (power-of-two) scale per block of 32 x 32 elements.
+It is a reading of "FP8" for this hardware, written out step by step:
+
+  X1  QK-norm, smoothing means and centring exactly as the INT8 steps F0-F2.
+  X2  block quantizer  per block of 32 rows x 32 columns (valid rows only):
+                         a = max|x|;  a = 0 -> scale 2^-127, codes 0;
+                         else e = min integer with 448 * 2^e >= a (clamped to
+                         [-127, 127]), scale 2^e, code = E4M3_rne(x * 2^-e),
+                       so |x * 2^-e| <= 448 (the largest finite E4M3) and the
+                       codes never overflow.  The blocks are square, so one
+                       quantization serves an operand in both orientations.
+  X3  Q-smoothing bias b_j = mu_q . K^_j with K^ the dequantized K (as F4).
+  X4  scores           S = (Q^ K^^T + b_j) / 8, products of the dequantized
+                       operands (exact), masked entries -inf.
+  X5  P~ codes         online over the 64-key tiles in increasing order with
+                       the running row maximum M_t = max(M_{t-1}, m_t) (m_t the
+                       tile-row max): P~ = exp(S - M_t) in (0, 1] and
+                       code = E4M3_rne(256 P~) (the fixed scale 2^-8).
+  X6  combine          l = sum_t exp(M_t - M) sum_j P~  (unquantized P~),
+                       O = sum_t exp(M_t - M) (codes_t / 256) V^_t / l,
+                       LSE = M + ln l + (q_raw . mu_k) / 8.
+  X7  backward prep    dO quantized with X2 (no centring); Delta, LSE - corr
+                       as B1.
+  X8  P = exp(S - (LSE - corr)), masked -> 0; P codes per 32 x 32 block
+      (queries x keys) with X2 on fp32(P).
+  X9  dV = P^^T dO^ (dequantized, exact products).
+  X10 dP = fp16(dO) fp16(V)^T, the one 16-bit matmul (as B5).
+  X11 dS = P (dP - Delta) with the unquantized P; dS codes per 32 x 32 block
+      with X2 on fp32(dS).
+  X12 dQ = dS^ K^ / 8;  dK = (dS^^T Q^ + colsum(dS^) mu_q) / 8 (as B8, B9);
+      with QK-norm the gradients go through the norm as B11.
+
+With ``rounding=False`` the E4M3 rounding of every code and the fp32/fp16
+roundings are removed (the power-of-two scales stay, and they are exact), so
+the result must equal the exact attention of ``oracle.exact``.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import faithful as _F
+
+BLK = 64                 # tile side (keys per online step, rows per block of the GPU layouts)
+MX = 32                  # side of a quantization block
+D = 64
+SCALE = 1.0 / 8.0
+E4M3_MAX = 448.0
+PT_SHIFT = 8             # P~ codes hold 2^8 P~
+
+
+# ---------------------------------------------------------------- X2
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the 256 OCP FP8 E4M3 codes (NaN for 0x7F and 0xFF)."""
+    vals = np.zeros(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = s * m * 2.0 ** -9
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Code bytes of round-to-nearest-even E4M3 for finite |y| <= 448 (values
+    given exactly in float64).  Normal range: the 3 mantissa bits of y's
+    binade, rounded half to even (a carry moves to the next binade); below
+    2^-6 the subnormal grid of step 2^-9."""
+    y = np.asarray(y, np.float64)
+    a = np.abs(y)
+    if np.any(~np.isfinite(a)) or np.any(a > E4M3_MAX):
+        raise ValueError("E4M3 input out of range")
+    code = np.zeros(a.shape, np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)           # 8 -> 0x08 = 2^-6, the carry
+    nrm = ~sub
+    f, E = np.frexp(a[nrm])                                           # a = f 2^E, f in [0.5, 1)
+    e = E - 1
+    q = np.rint((a[nrm] * np.ldexp(1.0, -e) - 1.0) * 8.0).astype(np.int64)
+    carry = q == 8
+    e = e + carry
+    q = np.where(carry, 0, q)
+    code[nrm] = ((e + 7) << 3) | q
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_round(y) -> np.ndarray:
+    """Nearest E4M3 value (ties to even) of each finite |y| <= 448."""
+    y = np.asarray(y, np.float64)
+    v = E4M3_VALUES[e4m3_encode(y)]
+    return np.where(y == 0, y, v)          # keep the sign of zero
+
+
+def e8m0_exponent(a) -> np.ndarray:
+    """X2 scale exponent: the least integer e with 448 2^e >= a (a > 0),
+    clamped to [-127, 127]; -127 for a = 0."""
+    a = np.asarray(a, np.float64)
+    e = np.zeros(a.shape, np.int64)
+    pos = a > 0
+    g = np.ceil(np.log2(a[pos] / E4M3_MAX)).astype(np.int64)
+    # fix the floating log2 by exact comparisons (448 * 2^e is exact)
+    g = np.where(np.ldexp(E4M3_MAX, g) < a[pos], g + 1, g)
+    g = np.where(np.ldexp(E4M3_MAX, g - 1) >= a[pos], g - 1, g)
+    e[pos] = g
+    e[~pos] = -127
+    return np.clip(e, -127, 127)
+
+
+def quantize_blocks(x, nrows: int = None, rounding: bool = True):
+    """X2 over an [R, C] array (R, C multiples of 32); rows >= nrows are
+    padding (code 0, excluded from the absmax).  Returns (dequantized values
+    [R, C] float64, scale exponents [R/32, C/32] int64, codes [R, C] float64
+    = value / 2^e)."""
+    x = np.asarray(x, np.float64)
+    R, C = x.shape
+    if nrows is not None and nrows < R:
+        x = x.copy()
+        x[nrows:] = 0.0
+    xb = x.reshape(R // MX, MX, C // MX, MX)
+    e = e8m0_exponent(np.max(np.abs(xb), axis=(1, 3)))
+    scaled = xb * np.ldexp(1.0, -e)[:, None, :, None]
+    codes = e4m3_round(scaled) if rounding else scaled
+    deq = codes * np.ldexp(1.0, e)[:, None, :, None]
+    return deq.reshape(R, C), e, codes.reshape(R, C)
+
+
+# ---------------------------------------------------------------- X1-X4
+
+@dataclass
+class Prepared:
+    N: int
+    T: int
+    mu_q: np.ndarray
+    mu_k: np.ndarray
+    qh: np.ndarray       # [Np, 64] dequantized smoothed Q (X2)
+    kh: np.ndarray       # [Np, 64] dequantized smoothed K
+    vh: np.ndarray       # [Np, 64] dequantized V
+    eq: np.ndarray       # [Np/32, 2] scale exponents
+    ek: np.ndarray
+    ev: np.ndarray
+    b: np.ndarray        # [Np] Q-smoothing bias (X3)
+    corr: np.ndarray     # [Np]
+    q_raw: np.ndarray
+    rounding: bool
+    k_in: np.ndarray = None
+    rq: np.ndarray = None
+    rk: np.ndarray = None
+
+
+def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_norm: bool = False) -> Prepared:
+    """X1-X3 for one head (q, k, v: [N, 64] arrays of bf16 values)."""
+    fp = _F.prepare(q, k, v, smooth_q, smooth_k, rounding, qk_norm)    # F0-F2 and the means
+    N, T = fp.N, fp.T
+    Np = T * BLK
+    dt = np.float32 if rounding else np.float64
+
+    def centre(x, mu):
+        out = np.zeros((Np, D), dt)
+        if rounding:
+            out[:N] = np.float32(np.asarray(x, np.float32)) - np.float32(mu)
+        else:
+            out[:N] = np.asarray(x, np.float64) - np.asarray(mu, np.float64)
+        return out
+
+    zero = np.zeros(D, dt)
+    # the values the scores use: the inputs, or x_n with QK-norm (exact in float32)
+    qh, eq, _ = quantize_blocks(centre(fp.q_raw, fp.mu_q), N, rounding)
+    kh, ek, _ = quantize_blocks(centre(fp.k_in, fp.mu_k), N, rounding)
+    vh, ev, _ = quantize_blocks(centre(v, zero), N, rounding)
+    b = kh @ np.asarray(fp.mu_q, np.float64)
+    return Prepared(N, T, fp.mu_q, fp.mu_k, qh, kh, vh, eq, ek, ev, b, fp.corr, fp.q_raw, rounding,
+                    fp.k_in, fp.rq, fp.rk)
+
+
+def _score_block(pp: Prepared, rows, cols, causal: bool):
+    S = (pp.qh[rows] @ pp.kh[cols].T + pp.b[cols][None, :]) * SCALE
+    keep = (cols[None, :] < pp.N) & (rows[:, None] < pp.N)
+    if causal:
+        keep &= cols[None, :] <= rows[:, None]
+    return np.where(keep, S, -np.inf), keep
+
+
+def _rows(blocks) -> np.ndarray:
+    return np.concatenate([np.arange(i * BLK, (i + 1) * BLK) for i in blocks])
+
+
+# ---------------------------------------------------------------- X5-X6
+
+def fwd_head(pp: Prepared, causal: bool, qblocks=None, chunk_blocks: int = 4, return_codes: bool = False):
+    """X4-X6 for the query blocks ``qblocks`` (default all).  Returns (O, LSE)
+    for their padded rows, plus (P~ codes [R, Np] as values 256 P~ rounded, the
+    running maxima [R, T]) if return_codes."""
+    T = pp.T
+    qblocks = list(range(T)) if qblocks is None else list(qblocks)
+    cols = np.arange(T * BLK)
+    vb = pp.vh.reshape(T, BLK, D)
+    oo, ll, cc, mm = [], [], [], []
+    for c0 in range(0, len(qblocks), chunk_blocks):
+        rows = _rows(qblocks[c0:c0 + chunk_blocks])
+        R = rows.size
+        S, keep = _score_block(pp, rows, cols, causal)
+        St = S.reshape(R, T, BLK)
+        kt = keep.reshape(R, T, BLK)
+        Mt = np.maximum.accumulate(np.max(St, axis=2), axis=1)             # [R, T] running max
+        Mf = np.where(np.isfinite(Mt), Mt, 0.0)
+        with np.errstate(invalid="ignore"):
+            pt = np.where(kt, np.exp(St - Mf[:, :, None]), 0.0)
+        scaled = pt * 2.0 ** PT_SHIFT
+        codes = e4m3_round(scaled) if pp.rounding else scaled
+        M = Mt[:, -1]
+        with np.errstate(invalid="ignore"):
+            w = np.where(np.isfinite(Mt), np.exp(Mf - M[:, None]), 0.0)   # [R, T]
+        l = np.sum(w * np.sum(pt, axis=2), axis=1)
+        pv = np.matmul(codes.transpose(1, 0, 2), vb) * 2.0 ** -PT_SHIFT    # [T, R, 64]
+        acc = np.einsum("rt,trc->rc", w, pv)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            oo.append(acc / l[:, None])
+            ll.append(M + np.log(l) + pp.corr[rows])
+        if return_codes:
+            cc.append(codes.reshape(R, T * BLK))
+            mm.append(Mt)
+    o, lse = np.concatenate(oo), np.concatenate(ll)
+    if return_codes:
+        return o, lse, np.concatenate(cc), np.concatenate(mm)
+    return o, lse
+
+
+def fwd(q, k, v, causal: bool, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_norm: bool = False):
+    """MXFP8 forward over [B, H, N, 64] arrays of bf16 values."""
+    B, H, N, _ = q.shape
+    o = np.zeros((B, H, N, D))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding, qk_norm)
+            ob, lb = fwd_head(pp, causal)
+            o[b, h], lse[b, h] = ob[:N], lb[:N]
+    return o, lse
+
+
+# ---------------------------------------------------------------- X7-X12
+
+@dataclass
+class BwdPrepared:
+    pp: Prepared
+    doh: np.ndarray      # [Np, 64] dequantized dO (X7)
+    edo: np.ndarray
+    do16: np.ndarray
+    v16: np.ndarray
+    delta: np.ndarray
+    lsep: np.ndarray
+
+
+def prepare_bwd(pp: Prepared, v, o, lse, do) -> BwdPrepared:
+    """X7 for one head (o: forward output values handed to the backward, lse:
+    float32 natural-log LSE in the true-score frame, do: bf16 values)."""
+    N, T = pp.N, pp.T
+    Np = T * BLK
+    r = pp.rounding
+    do32 = np.zeros((Np, D), np.float32 if r else np.float64)
+    do32[:N] = np.asarray(do, np.float32 if r else np.float64)
+    doh, edo, _ = quantize_blocks(do32, N, r)
+    do16 = np.zeros((Np, D))
+    v16 = np.zeros((Np, D))
+    if r:
+        do16[:N] = np.asarray(do, np.float32).astype(np.float16).astype(np.float64)
+        v16[:N] = np.asarray(v, np.float32).astype(np.float16).astype(np.float64)
+    else:
+        do16[:N] = np.asarray(do, np.float64)
+        v16[:N] = np.asarray(v, np.float64)
+    delta = np.zeros(Np)
+    delta[:N] = np.sum(np.asarray(do, np.float64) * np.asarray(o, np.float64), axis=1)
+    lsep = np.full(Np, np.inf)
+    lsep[:N] = np.asarray(lse, np.float64) - pp.corr[:N]
+    return BwdPrepared(pp, doh, edo, do16, v16, delta, lsep)
+
+
+def bwd_tiles(bp: BwdPrepared, iblocks, tblocks, causal: bool):
+    """X8-X11 on the tile grid iblocks x tblocks: P, dS, their dequantized
+    values and scale exponents, and the codes (value / scale)."""
+    pp = bp.pp
+    r = pp.rounding
+    rows, cols = _rows(iblocks), _rows(tblocks)
+    S, keep = _score_block(pp, rows, cols, causal)
+    with np.errstate(invalid="ignore", over="ignore"):
+        P = np.where(keep, np.exp(S - bp.lsep[rows][:, None]), 0.0)
+    Pq = P.astype(np.float32).astype(np.float64) if r else P
+    Ph, eP, cP = quantize_blocks(Pq, rounding=r)
+    dP = bp.do16[rows] @ bp.v16[cols].T
+    dS = np.where(keep, P * (dP - bp.delta[rows][:, None]), 0.0)
+    dSq = dS.astype(np.float32).astype(np.float64) if r else dS
+    dSh, edS, cdS = quantize_blocks(dSq, rounding=r)
+    return {"rows": rows, "cols": cols, "P": P, "dS": dS, "Ph": Ph, "eP": eP, "cP": cP,
+            "dSh": dSh, "edS": edS, "cdS": cdS}
+
+
+def bwd_head(bp: BwdPrepared, causal: bool, qblocks=None, kblocks=None, chunk: int = 4):
+    """X8-X12 for one head: dQ for the rows of ``qblocks``, dK and dV for the
+    keys of ``kblocks`` (default all)."""
+    pp = bp.pp
+    T = pp.T
+    allb = list(range(T))
+    qblocks = allb if qblocks is None else list(qblocks)
+    kblocks = allb if kblocks is None else list(kblocks)
+    mu_q = np.asarray(pp.mu_q, np.float64)
+    dq = np.zeros((len(qblocks) * BLK, D))
+    for c0 in range(0, len(qblocks), chunk):
+        ib = qblocks[c0:c0 + chunk]
+        tl = bwd_tiles(bp, ib, allb, causal)
+        dq[c0 * BLK:(c0 + len(ib)) * BLK] = (tl["dSh"] @ pp.kh) * SCALE
+    dk = np.zeros((len(kblocks) * BLK, D))
+    dv = np.zeros((len(kblocks) * BLK, D))
+    for c0 in range(0, len(kblocks), chunk):
+        tb = kblocks[c0:c0 + chunk]
+        for i0 in range(0, T, 16):
+            ib = allb[i0:i0 + 16]
+            tl = bwd_tiles(bp, ib, tb, causal)
+            rows = tl["rows"]
+            dv[c0 * BLK:(c0 + len(tb)) * BLK] += tl["Ph"].T @ bp.doh[rows]
+            dkc = tl["dSh"].T @ pp.qh[rows] + np.sum(tl["dSh"], axis=0)[:, None] * mu_q[None, :]
+            dk[c0 * BLK:(c0 + len(tb)) * BLK] += dkc * SCALE
+    return dq, dk, dv
+
+
+def bwd(q, k, v, o, lse, do, causal: bool, smooth_q: bool, smooth_k: bool, rounding: bool = True,
+        qk_norm: bool = False):
+    """MXFP8 backward over [B, H, N, 64] arrays (o, lse: the forward outputs
+    handed to the backward).  Returns (dQ, dK, dV) float64."""
+    B, H, N, _ = q.shape
+    out = [np.zeros((B, H, N, D)) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            pp = prepare(q[b, h], k[b, h], v[b, h], smooth_q, smooth_k, rounding, qk_norm)
+            bp = prepare_bwd(pp, v[b, h], o[b, h], lse[b, h], do[b, h])
+            dq, dk, dv = bwd_head(bp, causal)
+            if pp.rq is not None:
+                dq = _F.qk_norm_grad(dq[:N], pp.q_raw, pp.rq)
+                dk = _F.qk_norm_grad(dk[:N], pp.k_in, pp.rk)
+            out[0][b, h], out[1][b, h], out[2][b, h] = dq[:N], dk[:N], dv[:N]
+    return tuple(out)
