@@ -10,9 +10,10 @@ It is a reading of "FP8" for this hardware, written out step by step:
 
   X1  QK-norm, smoothing means and centring exactly as the INT8 steps F0-F2.
   X2  block quantizer  per block of 32 rows x 32 columns (valid rows only):
-                         a = max|x|;  a = 0 -> scale 2^-127, codes 0;
-                         else e = min integer with 448 * 2^e >= a (clamped to
-                         [-127, 127]), scale 2^e, code = E4M3_rne(x * 2^-e),
+                         a = max|x|;  e = the least integer with
+                         448 * 2^e >= a, clamped to [-126, 127] (an all-zero
+                         block gets -126; the floor keeps 2^e a normal float32),
+                         scale 2^e, code = E4M3_rne(x * 2^-e),
                        so |x * 2^-e| <= 448 (the largest finite E4M3) and the
                        codes never overflow.  The blocks are square, so one
                        quantization serves an operand in both orientations.
@@ -23,7 +24,8 @@ It is a reading of "FP8" for this hardware, written out step by step:
                        the running row maximum M_t = max(M_{t-1}, m_t) (m_t the
                        tile-row max): P~ = exp(S - M_t) in (0, 1] and
                        code = E4M3_rne(256 P~) (the fixed scale 2^-8).
-  X6  combine          l = sum_t exp(M_t - M) sum_j P~  (unquantized P~),
+  X6  combine          l = sum_t exp(M_t - M) sum_j codes_t / 256 (the row sum
+                       of the quantized P~, as the INT8 mode's F8),
                        O = sum_t exp(M_t - M) (codes_t / 256) V^_t / l,
                        LSE = M + ln l + (q_raw . mu_k) / 8.
   X7  backward prep    dO quantized with X2 (no centring); Delta, LSE - corr
@@ -111,7 +113,7 @@ def e4m3_round(y) -> np.ndarray:
 
 def e8m0_exponent(a) -> np.ndarray:
     """X2 scale exponent: the least integer e with 448 2^e >= a (a > 0),
-    clamped to [-127, 127]; -127 for a = 0."""
+    clamped to [-126, 127]; -126 for a = 0."""
     a = np.asarray(a, np.float64)
     e = np.zeros(a.shape, np.int64)
     pos = a > 0
@@ -120,8 +122,8 @@ def e8m0_exponent(a) -> np.ndarray:
     g = np.where(np.ldexp(E4M3_MAX, g) < a[pos], g + 1, g)
     g = np.where(np.ldexp(E4M3_MAX, g - 1) >= a[pos], g - 1, g)
     e[pos] = g
-    e[~pos] = -127
-    return np.clip(e, -127, 127)
+    e[~pos] = -126
+    return np.clip(e, -126, 127)
 
 
 def quantize_blocks(x, nrows: int = None, rounding: bool = True):
@@ -228,7 +230,7 @@ def fwd_head(pp: Prepared, causal: bool, qblocks=None, chunk_blocks: int = 4, re
         M = Mt[:, -1]
         with np.errstate(invalid="ignore"):
             w = np.where(np.isfinite(Mt), np.exp(Mf - M[:, None]), 0.0)   # [R, T]
-        l = np.sum(w * np.sum(pt, axis=2), axis=1)
+        l = np.sum(w * np.sum(codes, axis=2), axis=1) * 2.0 ** -PT_SHIFT
         pv = np.matmul(codes.transpose(1, 0, 2), vb) * 2.0 ** -PT_SHIFT    # [T, R, 64]
         acc = np.einsum("rt,trc->rc", w, pv)
         with np.errstate(invalid="ignore", divide="ignore"):

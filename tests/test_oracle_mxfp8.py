@@ -64,7 +64,8 @@ def test_e8m0_exponent_inequality():
     assert np.all(np.ldexp(448.0, e) >= a)
     assert np.all(np.ldexp(448.0, e - 1) < a)
     assert np.array_equal(X.e8m0_exponent(448.0 * np.ldexp(1.0, np.arange(-20, 21))), np.arange(-20, 21))
-    assert X.e8m0_exponent(np.array([0.0]))[0] == -127
+    assert X.e8m0_exponent(np.array([0.0]))[0] == -126
+    assert X.e8m0_exponent(np.array([2.0 ** -130]))[0] == -126          # clamped: 2^e stays a normal float32
 
 
 def test_quantize_blocks_properties():
