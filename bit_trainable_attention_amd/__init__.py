@@ -41,7 +41,7 @@ class SageBwdError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32), ("smooth_k", ctypes.c_int32),
-                ("int8_dp", ctypes.c_int32), ("qk_norm", ctypes.c_int32)]
+                ("int8_dp", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("mxfp8", ctypes.c_int32)]
 
 
 _lib = None
@@ -83,11 +83,12 @@ def load_library() -> ctypes.CDLL:
     return _lib
 
 
-def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False, qk_norm=False) -> Params:
+def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False, qk_norm=False, mxfp8=False) -> Params:
     """int8_dp: the all-INT8 ablation (dO V^T from INT8 codes); backward only.
-    qk_norm: QK-norm fused in (same value for forward and backward)."""
+    qk_norm: QK-norm fused in; mxfp8: E4M3 codes with E8M0 32x32 block scales
+    instead of INT8 (both: same value for forward and backward)."""
     return Params(int(B), int(H), int(N), int(D), int(bool(causal)), int(bool(smooth_q)), int(bool(smooth_k)),
-                  int(bool(int8_dp)), int(bool(qk_norm)))
+                  int(bool(int8_dp)), int(bool(qk_norm)), int(bool(mxfp8)))
 
 
 def _check(rc: int, what: str):
@@ -114,8 +115,8 @@ def _check_qkv(*ts):
 
 
 def workspace_size(B, H, N, causal=False, smooth_q=False, smooth_k=True, backward=False, int8_dp=False,
-                   qk_norm=False) -> int:
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp, qk_norm=qk_norm)
+                   qk_norm=False, mxfp8=False) -> int:
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp, qk_norm=qk_norm, mxfp8=mxfp8)
     lib = load_library()
     n = (lib.sagebwd_bwd_workspace_size if backward else lib.sagebwd_fwd_workspace_size)(ctypes.byref(p))
     if n == 0:
@@ -131,13 +132,14 @@ def _workspace(nbytes, device, ws=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None, qk_norm=False):
+def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None, qk_norm=False,
+        mxfp8=False):
     """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N]).  Pass a
     forward-sized uint8 ``workspace`` to keep the quantized Q and K for a
     backward that reuses them (``bwd(..., fwd_workspace=workspace)``)."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, qk_norm=qk_norm)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, qk_norm=qk_norm, mxfp8=mxfp8)
     lib = load_library()
     ws = _workspace(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     if out is None:
@@ -152,7 +154,7 @@ def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, ou
 
 
 def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None,
-        fwd_workspace=None, int8_dp=False, qk_norm=False):
+        fwd_workspace=None, int8_dp=False, qk_norm=False, mxfp8=False):
     """Backward.  Returns (dQ, dK, dV) bf16 [B,H,N,64].  ``fwd_workspace``:
     the workspace of the forward call on the same q, k, v and flags, whose
     quantized Q and K are then reused (bit-identical results).  ``int8_dp``:
@@ -161,7 +163,7 @@ def bwd(q, k, v, o, lse, do, causal=False, smooth_q=False, smooth_k=True, worksp
     if not (lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:3]):
         raise SageBwdError("lse must be a contiguous float32 CUDA tensor [B, H, N]")
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
     lib = load_library()
     ws = _workspace(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     if out is None:
@@ -197,12 +199,12 @@ def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params, fwd_ws
 
 
 def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True, int8_dp=False,
-            qk_norm=False):
+            qk_norm=False, mxfp8=False):
     """Run only the preparation kernels into a fresh backward-sized workspace
     (uint8 tensor) for inspection; see ws_region for the layout."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
     lib = load_library()
     nbytes = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
@@ -217,14 +219,14 @@ DEBUG_KERNELS = {"fwd": 0, "dkdv": 1, "dq": 2}
 
 
 def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=False, smooth_q=False,
-               smooth_k=True, int8_dp=False, qk_norm=False):
+               smooth_k=True, int8_dp=False, qk_norm=False, mxfp8=False):
     """Run one attention kernel's debug instantiation and return the raw
     SAGEBWD_DUMP_BYTES dump of tile (bh, qblock, kblock) as a CPU uint8
     tensor (see include/sagebwd.h for the layout).  kernel: "fwd" writes into
     o and lse; "dkdv" and "dq" read o, lse and do."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
     lib = load_library()
     ws = torch.empty(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=q.device)
     dump = torch.zeros(DUMP_BYTES, dtype=torch.uint8, device=q.device)
@@ -252,19 +254,19 @@ class SageBwdAttention(torch.autograd.Function):
     backward reuses the forward's quantized Q and K (its workspace is kept)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True, qk_norm=False):
+    def forward(ctx, q, k, v, causal=False, smooth_q=False, smooth_k=True, qk_norm=False, mxfp8=False):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         B, H, N, D = q.shape
-        ws = torch.empty(workspace_size(B, H, N, causal, smooth_q, smooth_k, qk_norm=qk_norm), dtype=torch.uint8,
-                         device=q.device)
-        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k, workspace=ws, qk_norm=qk_norm)
+        ws = torch.empty(workspace_size(B, H, N, causal, smooth_q, smooth_k, qk_norm=qk_norm, mxfp8=mxfp8),
+                         dtype=torch.uint8, device=q.device)
+        o, lse = fwd(q, k, v, causal, smooth_q, smooth_k, workspace=ws, qk_norm=qk_norm, mxfp8=mxfp8)
         ctx.save_for_backward(q, k, v, o, lse, ws)
         ctx.flags = (causal, smooth_q, smooth_k)
-        ctx.qk_norm = qk_norm
+        ctx.modes = dict(qk_norm=qk_norm, mxfp8=mxfp8)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse, ws = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags, fwd_workspace=ws, qk_norm=ctx.qk_norm)
-        return dq, dk, dv, None, None, None, None
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), *ctx.flags, fwd_workspace=ws, **ctx.modes)
+        return dq, dk, dv, None, None, None, None, None

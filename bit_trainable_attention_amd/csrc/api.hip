@@ -105,9 +105,10 @@ int check_params(const sagebwd_params* p) {
     if (p->B < 1 || p->H < 1 || p->N < 1) return SAGEBWD_ERR_INVALID_ARG;
     if ((p->causal != 0 && p->causal != 1) || (p->smooth_q != 0 && p->smooth_q != 1) ||
         (p->smooth_k != 0 && p->smooth_k != 1) || (p->int8_dp != 0 && p->int8_dp != 1) ||
-        (p->qk_norm != 0 && p->qk_norm != 1))
+        (p->qk_norm != 0 && p->qk_norm != 1) || (p->mxfp8 != 0 && p->mxfp8 != 1))
         return SAGEBWD_ERR_INVALID_ARG;
     if (p->D != HD) return SAGEBWD_ERR_UNSUPPORTED;
+    if (p->mxfp8 && p->int8_dp) return SAGEBWD_ERR_UNSUPPORTED;   // the INT8 ablation has no MXFP8 form
     if (p->N > MAX_N || (int64_t)p->B * p->H > MAX_BH) return SAGEBWD_ERR_UNSUPPORTED;
     return SAGEBWD_OK;
 }
@@ -176,7 +177,7 @@ void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, co
     a.smooth_q = p.smooth_q;
     a.smooth_k = p.smooth_k;
     // V's block scales are only needed by the forward and the inspection call
-    launch_quantize(a, BH, want_vt ? 3 : 2, st);
+    launch_quantize(a, BH, want_vt ? 3 : 2, p.mxfp8 != 0, st);
 }
 
 // Where the backward reads the quantized Q and K (means, codes in both
@@ -206,7 +207,7 @@ void run_bwd_pre(const sagebwd_params& p, const Layout& L, const QkSource& qk, c
     b.sv = b.v_r ? region<float>(ws, L, R_S_V) : nullptr;
     b.N = p.N;
     b.T = (p.N + BLK - 1) / BLK;
-    launch_bwd_pre(b, p.B * p.H, st);
+    launch_bwd_pre(b, p.B * p.H, p.mxfp8 != 0, st);
 }
 
 FwdArgs fwd_args(const sagebwd_params& p, const Layout& L, void* ws, void* O, float* LSE) {
@@ -313,8 +314,8 @@ void run_bwd_group(const sagebwd_params& p, const BwdArgs& a, int grp, int which
     const Groups G = head_groups(p);
     const int bh0 = grp * G.heads, nbh = std::min(G.heads, p.B * p.H - bh0);
     const BwdArgs c = group_args(a, bh0, nbh);
-    if (which & 1) launch_bwd_dkdv(c, nbh, p.causal, p.smooth_q, p.int8_dp, st, kernel_dump == 1);
-    if (which & 2) launch_bwd_dq(c, nbh, p.causal, st, kernel_dump == 2);
+    if (which & 1) launch_bwd_dkdv(c, nbh, p.causal, p.smooth_q, p.int8_dp, p.mxfp8, st, kernel_dump == 1);
+    if (which & 2) launch_bwd_dq(c, nbh, p.causal, p.mxfp8, st, kernel_dump == 2);
 }
 
 }  // namespace
@@ -359,7 +360,7 @@ int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         return hip_status();
     }
     const FwdArgs a = fwd_args(*p, L, ws, O, LSE);
-    launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, st);
+    launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, p->mxfp8, st);
     return hip_status();
 }
 
@@ -439,6 +440,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         kblock >= T || (p->causal && kblock > qblock))
         return SAGEBWD_ERR_INVALID_ARG;
     if (!dump || dump_bytes < (size_t)dumpoff::BYTES) return SAGEBWD_ERR_INVALID_ARG;
+    if (p->mxfp8) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 kernels only
     if (kernel == 0) {
         if ((rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream))) return rc;
         const Layout L = make_layout(*p, PASS_FWD);
@@ -447,7 +449,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         a.dump_bh = bh;
         a.dump_i = qblock;
         a.dump_t = kblock;
-        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, (hipStream_t)stream, true);
+        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, false, (hipStream_t)stream, true);
         return hip_status();
     }
     if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, nullptr, 0, ws,

@@ -21,7 +21,7 @@ constexpr int A = 0, F1 = 16384, C1 = 32768, ACC1 = 36864, F2 = 53248, C2 = 6963
 
 struct FwdArgs {
     const int8_t *q_r, *k_r, *v_t;     // code blocks [BH][T][4096]
-    const float *sq, *sk, *sv;         // [BH][T]
+    const float *sq, *sk, *sv;         // [BH][T] (MX: 4 exponent bytes per block)
     const float *corr, *bias;          // [BH][Np]
     uint16_t* o;                       // bf16 [BH][N][64]
     float* lse;                        // [BH][N]
@@ -41,18 +41,20 @@ struct BwdArgs {
     const float *rq, *rk;              // QK-norm factors [BH][Np], or null (no QK-norm)
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
     int8_t* ds_codes;                  // dS codes of every computed tile [BH][ntiles][4096] (see ds_tile_index)
-    float* ds_scale;                   // their block scales [BH][ntiles]
+    float* ds_scale;                   // their block scales [BH][ntiles] (MX: 4 exponent bytes per tile)
     size_t ntiles;                     // tiles per head: T (T + 1) / 2 causal, T^2 otherwise
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
     uint8_t* dump;                     // tile dump (debug instantiation only)
     int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
 };
 
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump = false);
-// int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st,
+// mx: MXFP8 codes and block exponents (no tile dump)
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, bool mx, hipStream_t st, bool dump = false);
+// int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16;
+// mx: MXFP8 codes and block exponents (neither int8_dp nor a tile dump)
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, bool mx, hipStream_t st,
                     bool dump = false);
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, hipStream_t st, bool dump = false);
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump = false);
 
 // Position of the dS tile (query block i, key block t) among the tiles of
 // its head: query-block major, so the tiles of one query block are

@@ -494,6 +494,52 @@ struct DqStep {
     float sds, sk; // s_dS(i, t) and s_K,t
 };
 
+// dQ (x 1/8) in bf16; with QK-norm dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
+// other 32 channels of this lane's query being in the other half of the wave.
+__device__ __forceinline__ void dq_epilogue(const BwdArgs& a, v16f (&dq)[2], int bh, int q, int h, size_t rowbase) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[db][r] *= 0.125f;
+    const bool qok = q < a.N;
+    if (a.rq) {
+        const float rr = qok ? a.rq[rowbase + q] : 0.0f;
+        const uint16_t* qrow = a.q_in + ((size_t)bh * a.N + (qok ? q : 0)) * HD;
+        float qn[2][16];
+        float part = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const uint2 u = qok ? *(const uint2*)(qrow + 32 * db + 8 * r4 + 4 * h) : make_uint2(0, 0);
+                qn[db][4 * r4 + 0] = qk_normed(u.x & 0xFFFFu, rr);
+                qn[db][4 * r4 + 1] = qk_normed(u.x >> 16, rr);
+                qn[db][4 * r4 + 2] = qk_normed(u.y & 0xFFFFu, rr);
+                qn[db][4 * r4 + 3] = qk_normed(u.y >> 16, rr);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part = __builtin_fmaf(dq[db][4 * r4 + j], qn[db][4 * r4 + j], part);
+            }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        const float mean = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (1.0f / HD);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[db][r] = rr * __builtin_fmaf(-qn[db][r], mean, dq[db][r]);
+    }
+    if (qok) {
+        uint16_t* row = a.dq + ((size_t)bh * a.N + q) * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * h;
+                const uint32_t w0 = f32_to_bf16_rne(dq[db][4 * r4 + 0]) | (f32_to_bf16_rne(dq[db][4 * r4 + 1]) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(dq[db][4 * r4 + 2]) | (f32_to_bf16_rne(dq[db][4 * r4 + 3]) << 16);
+                *(uint2*)(row + d) = make_uint2(w0, w1);
+            }
+    }
+}
+
 template <bool CAUSAL, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -581,49 +627,312 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         }
     }
 
-    // dQ (x 1/8); with QK-norm then dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
-    // other 32 channels of this lane's query being in the other half of the wave
+    dq_epilogue(a, dq, bh, q, h, rowbase);
+}
+
+// ------------------------------------------------------------------ MXFP8
+// The same two kernels with OCP E4M3 codes and E8M0 exponents per 32x32 block
+// on the scaled FP8 MFMA (block scales applied inside the instruction, so
+// dK, dV and dQ accumulate in the MFMA accumulators with no per-tile
+// multiply).  A 32x32 block of P or dS (32 queries of one half of the query
+// block x the 32 keys of one wave) lies within one wave, so the block maxima
+// need no exchange between waves, and the key-block kernel synchronizes once
+// per query block (double-buffered operand tiles).  The dS codes handed to
+// the dQ kernel carry four exponent bytes per tile (byte 2 * key half + query
+// half) in the slot of the INT8 block scale.
+
+struct DkdvMxSmem {
+    v4i q_r[2][256];     // Q row-operand codes (A operand of Q K^T)
+    v4i q_t[2][256];     // Q transposed codes (B operand of dS^T Q)
+    v4i do_t[2][256];    // dO transposed codes (B operand of P^T dO)
+    v8h do16[2][512];    // dO in FP16, swizzled rows (A operand of dO V^T)
+    float lse2[2][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta
+    uint32_t qs[2][4];   // [0]: Q block exponents, [1]: dO block exponents
+};
+
+// Codes of a 32x32 block held as 16 registers x 64 lanes (E4M3(x / 2^e)),
+// packed four registers to a dword in register order.
+__device__ __forceinline__ v4i fp8_block_codes(const float (&x)[16], float scale) {
+    return v4i{(int)fp8_quad(x[0], x[1], x[2], x[3], scale), (int)fp8_quad(x[4], x[5], x[6], x[7], scale),
+               (int)fp8_quad(x[8], x[9], x[10], x[11], scale), (int)fp8_quad(x[12], x[13], x[14], x[15], scale)};
+}
+
+template <bool CAUSAL, bool SMOOTHQ>
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
+    __shared__ DkdvMxSmem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group_bwd(a.ngroups, a.BH, true, bh, g);
+    const int T = a.T;
+    const int kvb = 2 * g + wave / 2, kh = wave % 2;
+    const bool live = kvb < T;
+    const int key = kvb * BLK + 32 * kh + l32;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
+    const size_t rowbase = bh * np;
+
+    v8i kop = v8i{};
+    v8h vh[4];
+    float kbias = 0.0f;
+    int sk_e = E8M0_ONE;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int ks = 0; ks < 4; ++ks) vh[ks] = v8h{};
+    if (live) {
+        const v4i* src = (const v4i*)(a.k_r + (bt + kvb) * 4096);
+        kop = cat8(src[(kh * 2 + 0) * 64 + lane], src[(kh * 2 + 1) * 64 + lane]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dq[db][r] *= 0.125f;
-    const bool qok = q < a.N;
-    if (a.rq) {
-        const float rr = qok ? a.rq[rowbase + q] : 0.0f;
-        const uint16_t* qrow = a.q_in + ((size_t)bh * a.N + (qok ? q : 0)) * HD;
-        float qn[2][16];
-        float part = 0.0f;
+        for (int ks = 0; ks < 4; ++ks) vh[ks] = *(const v8h*)(a.v16 + (rowbase + key) * HD + 16 * ks + 8 * h);
+        if (SMOOTHQ) kbias = a.bias[rowbase + key];
+        sk_e = ebyte(((const uint32_t*)a.sk)[bt + kvb], 2 * kh + h);   // column = key, 32-channel block h
+    }
+    const float brow = h == 0 ? 1.0f : kbias;
+    const int e_one = opaque(E8M0_ONE);
+    const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                         0x38383838};
+
+    const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
+    const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
+    const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
+    const v4i* dtg = (const v4i*)(a.do_t + bt * 4096);
+    auto fetch = [&](int i, int b) {
+        dma16_to_lds(qrg + (size_t)i * 256 + tid, &sm.q_r[b][64 * wave]);
+        dma16_to_lds(qtg + (size_t)i * 256 + tid, &sm.q_t[b][64 * wave]);
+        dma16_to_lds(dtg + (size_t)i * 256 + tid, &sm.do_t[b][64 * wave]);
+        const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int j = 0; j < 2; ++j) {
+            const int s = 256 * j + tid, row = s / 8;
+            dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
+        }
+        if (wave == 0 && lane < 32)
+            dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
+        if (wave == 1 && lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
+    };
+
+    v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
+    v16f csum = v16f{};   // Q-smoothing: every column holds sum over queries of dS^ for key (row)
+
+    v4i dc_prev[2] = {v4i{}, v4i{}};
+    uint32_t e_prev = 0;
+    size_t tix_prev = 0;
+    bool have_prev = false;
+    auto store_prev = [&]() {
+        v4i* dst = (v4i*)(a.ds_codes + tix_prev * 4096) + kh * 128 + lane;
+        __builtin_nontemporal_store(dc_prev[0], dst);
+        __builtin_nontemporal_store(dc_prev[1], dst + 64);
+        if (lane == 0) ((uint16_t*)(a.ds_scale + tix_prev))[kh] = (uint16_t)e_prev;   // bytes 2 kh, 2 kh + 1
+    };
+
+    fetch(i0, 0);
+    const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
+    for (int i = i0; i < T; ++i) {
+        const int buf = (i - i0) & 1;
+        // query block i has landed in buf, and every wave is done with the
+        // other buffer (query block i - 1), which the next fetch overwrites
+        wait_vmem();
+        lds_barrier();
+        if (i + 1 < T) fetch(i + 1, buf ^ 1);
+        if (have_prev) store_prev();
+        have_prev = false;
+        if (!live || (CAUSAL && i < kvb)) continue;
+        const bool masked = (CAUSAL && i == kvb) || ragged_keys;
+        const uint32_t q_w = sm.qs[buf][0], do_w = sm.qs[buf][1];
+        float p[2][16];   // [qb]: lane = key, registers = queries
+        {
+            // S = Q K^T (dequantized), P = exp2(S log2(e)/8 + bias_j - lse2_i)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const v16f sx = mfma_fp8(cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]),
+                                         kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
+                const float arow = h == 0 ? -sm.lse2[buf][32 * qb + l32] : 1.0f;
+                const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], SCORE_SCALE_LOG2, corr[r]));
+                    if (masked) {
+                        const int qq = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
+                        if (key >= a.N || (CAUSAL && key > qq)) pv = 0.0f;
+                    }
+                    p[qb][r] = pv;
+                }
+            }
+        }
+        // P codes per 32x32 block (query half qb x this wave's keys)
+        int eP[2];
+        v4i pc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            uint32_t pm = 0;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) pm = umax(pm, umax(__float_as_uint(p[qb][r]), __float_as_uint(p[qb][r + 1])));
+            eP[qb] = mx_exponent(wave_max64(__uint_as_float(pm)));
+            pc[qb] = fp8_block_codes(p[qb], pow2f(eP[qb]));
+        }
+        // dV += P^T dO: A = P codes (row = key, 32-query block h), B = dO^T
+        {
+            const v8i pa = cat8(pc[0], pc[1]);
+            const int pe = (h ? eP[1] : eP[0]) + 127;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                dv[db] = mfma_fp8(pa, cat8(sm.do_t[buf][(db * 2 + 0) * 64 + lane], sm.do_t[buf][(db * 2 + 1) * 64 + lane]),
+                                  dv[db], pe, ebyte(do_w, 2 * h + db));
+        }
+        // dS = P * (dO V^T - Delta) (FP16 MFMA, -Delta as the accumulator input)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int row = 32 * qb + l32;
+            v16f nd;
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const uint2 u = qok ? *(const uint2*)(qrow + 32 * db + 8 * r4 + 4 * h) : make_uint2(0, 0);
-                qn[db][4 * r4 + 0] = qk_normed(u.x & 0xFFFFu, rr);
-                qn[db][4 * r4 + 1] = qk_normed(u.x >> 16, rr);
-                qn[db][4 * r4 + 2] = qk_normed(u.y & 0xFFFFu, rr);
-                qn[db][4 * r4 + 3] = qk_normed(u.y >> 16, rr);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) part = __builtin_fmaf(dq[db][4 * r4 + j], qn[db][4 * r4 + j], part);
+                const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
+                nd[4 * r4 + 0] = d4.x;
+                nd[4 * r4 + 1] = d4.y;
+                nd[4 * r4 + 2] = d4.z;
+                nd[4 * r4 + 3] = d4.w;
             }
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        const float mean = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (1.0f / HD);
+            v16f dpd = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
+            dpd = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dpd);
+            dpd = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dpd);
+            dpd = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dpd);
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+            for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpd[r];
+        }
+        int eS[2];
+        v4i dc[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dq[db][r] = rr * __builtin_fmaf(-qn[db][r], mean, dq[db][r]);
+        for (int qb = 0; qb < 2; ++qb) {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) m = max_abs2f(m, p[qb][r], p[qb][r + 1]);
+            eS[qb] = mx_exponent(wave_max64(m));
+            dc[qb] = fp8_block_codes(p[qb], pow2f(eS[qb]));
+        }
+        // dK += dS^T Q (and the dS column sums for the Q-smoothing term)
+        {
+            const v8i da = cat8(dc[0], dc[1]);
+            const int de = (h ? eS[1] : eS[0]) + 127;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                dk[db] = mfma_fp8(da, cat8(sm.q_t[buf][(db * 2 + 0) * 64 + lane], sm.q_t[buf][(db * 2 + 1) * 64 + lane]),
+                                  dk[db], de, ebyte(q_w, 2 * h + db));
+            if (SMOOTHQ) csum = mfma_fp8(da, ones, csum, de, e_one);
+        }
+        dc_prev[0] = dc[0];
+        dc_prev[1] = dc[1];
+        e_prev = (uint32_t)(eS[0] + 127) | ((uint32_t)(eS[1] + 127) << 8);
+        tix_prev = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, i, kvb, T);
+        have_prev = true;
     }
-    if (qok) {
-        uint16_t* row = a.dq + ((size_t)bh * a.N + q) * HD;
+    if (have_prev) store_prev();
+
+    if (!live) return;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db) {
+        const float muq = SMOOTHQ ? a.mu_q[(size_t)bh * HD + 32 * db + l32] : 0.0f;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d = 32 * db + 8 * r4 + 4 * h;
-                const uint32_t w0 = f32_to_bf16_rne(dq[db][4 * r4 + 0]) | (f32_to_bf16_rne(dq[db][4 * r4 + 1]) << 16);
-                const uint32_t w1 = f32_to_bf16_rne(dq[db][4 * r4 + 2]) | (f32_to_bf16_rne(dq[db][4 * r4 + 3]) << 16);
-                *(uint2*)(row + d) = make_uint2(w0, w1);
+        for (int r = 0; r < 16; ++r)
+            dk[db][r] = (SMOOTHQ ? __builtin_fmaf(csum[r], muq, dk[db][r]) : dk[db][r]) * 0.125f;
+    }
+    if (a.rk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kvb * BLK + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4);
+            const bool ok = kk < a.N;
+            const float rr = ok ? a.rk[rowbase + kk] : 0.0f;
+            const uint16_t* krow = a.k_in + ((size_t)bh * a.N + (ok ? kk : 0)) * HD;
+            const float kn0 = ok ? qk_normed(krow[l32], rr) : 0.0f;
+            const float kn1 = ok ? qk_normed(krow[32 + l32], rr) : 0.0f;
+            const float mean = half_sum32(__builtin_fmaf(dk[1][r], kn1, dk[0][r] * kn0)) * (1.0f / HD);
+            dk[0][r] = rr * __builtin_fmaf(-kn0, mean, dk[0][r]);
+            dk[1][r] = rr * __builtin_fmaf(-kn1, mean, dk[1][r]);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+        const int d = 32 * db + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = kvb * BLK + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4);
+            if (kk < a.N) {
+                a.dk[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dk[db][r]);
+                a.dv[((size_t)bh * a.N + kk) * HD + d] = (uint16_t)f32_to_bf16_rne(dv[db][r]);
             }
+        }
     }
+}
+
+// dQ from the stored E4M3 dS codes: each 32-key half of a tile is transposed
+// on the MFMA as its product with an E4M3 identity (the codes in the first 32
+// k positions, zeros in the other 32; every output is one exact product),
+// re-coded (exact: the values are E4M3 values), and contracted with the K^T
+// codes, the block exponents applied inside the instruction.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void k_bwd_dq_mx(BwdArgs a) {
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group_bwd(a.ngroups, a.BH, false, bh, g);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qh = wave % 2;
+    if (qblk >= T) return;
+    const int q = qblk * BLK + 32 * qh + l32;
+    const int t_end = CAUSAL ? qblk + 1 : T;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
+    const size_t rowbase = bh * np;
+    const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
+    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + qh * 64 + lane;
+    const uint32_t* dss = (const uint32_t*)(a.ds_scale + tile0);
+    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096) + lane;
+    const uint32_t* skg = (const uint32_t*)a.sk + bt;
+
+    // E4M3 identity (B operand): column n = l32 has 1.0 at k position n,
+    // which lies in half (n % 8) / 4, byte 4 (n / 8) + n % 4
+    v8i eye = v8i{};
+    if (h == (l32 % 8) / 4) eye[l32 / 8] = E4M3_ONE << (8 * (l32 % 4));
+    const int e_one = opaque(E8M0_ONE);
+
+    auto load = [&](int t, DqStep& s) {
+        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);
+        s.ds[1] = __builtin_nontemporal_load(dsg + (size_t)t * 256 + 128);
+        s.sds = __uint_as_float(dss[t]);
+        s.sk = __uint_as_float(skg[t]);
+    };
+    v16f dq[2] = {v16f{}, v16f{}};
+    auto step = [&](int t, const DqStep& s) {
+        v8i kt[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db) kt[db] = cat8(ktg[(size_t)t * 256 + (db * 2 + 0) * 64], ktg[(size_t)t * 256 + (db * 2 + 1) * 64]);
+        v4i dc[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const v16f tr = mfma_fp8(cat8(s.ds[kh], v4i{}), eye, v16f{}, e_one, e_one);
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = tr[r];
+            dc[kh] = fp8_block_codes(x, 1.0f);
+        }
+        const uint32_t ds_w = __float_as_uint(s.sds), sk_w = __float_as_uint(s.sk);
+        const v8i db8 = cat8(dc[0], dc[1]);
+        const int de = ebyte(ds_w, 2 * h + qh);   // key half h, this wave's query half
+#pragma unroll
+        for (int db = 0; db < 2; ++db) dq[db] = mfma_fp8(kt[db], db8, dq[db], ebyte(sk_w, 2 * h + db), de);
+    };
+
+    DqStep ring[DQ_DEPTH];
+#pragma unroll
+    for (int j = 0; j < DQ_DEPTH; ++j)
+        if (j < t_end) load(j, ring[j]);
+    for (int t0 = 0; t0 < t_end; t0 += DQ_DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DQ_DEPTH; ++j) {
+            const int t = t0 + j;
+            if (t < t_end) {
+                step(t, ring[j]);
+                if (t + DQ_DEPTH < t_end) load(t + DQ_DEPTH, ring[j]);
+            }
+        }
+    }
+    dq_epilogue(a, dq, bh, q, h, rowbase);
 }
 
 // Instantiation by (causal, Q-smoothing, all-INT8 dO V^T, tile dump).
@@ -649,14 +958,31 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     }                                                                                                \
     return 0;
 
-int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, hipStream_t st, bool dump) {
+int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, bool mx, hipStream_t st,
+                    bool dump) {
+    if (mx) {
+        dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
+        if (causal) {
+            if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv_mx<true, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_dkdv_mx<true, false>), grid, block, 0, st, a);
+        } else {
+            if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv_mx<false, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_bwd_dkdv_mx<false, false>), grid, block, 0, st, a);
+        }
+        return 0;
+    }
     SAGEBWD_LAUNCH_BWD(k_bwd_dkdv)
 }
 
 #undef SAGEBWD_LAUNCH_BWD
 
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, hipStream_t st, bool dump) {
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
+    if (mx) {
+        if (causal) hipLaunchKernelGGL((k_bwd_dq_mx<true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq_mx<false>), grid, block, 0, st, a);
+        return 0;
+    }
     if (causal) {
         if (dump) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);

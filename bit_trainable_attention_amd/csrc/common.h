@@ -16,6 +16,12 @@
 //                 token order of a D register column: byte b of half h is
 //                 token 8*(b/4) + 4*h + b%4 of the 32-token k-step),
 // so the P / dS codes produced in D registers feed the next MFMA directly.
+//   FP8   v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3): A/B lane l hold 32
+//         k-bytes of row/column l%32, byte b at k = 32*(b/16) + 16*h + b%16,
+//         so the two 16-byte chunks of the INT8 layouts (k-steps 0 and 1)
+//         form one operand; each lane also passes the E8M0 scale of row/column
+//         l%32 for the 32-k block h, and every product is multiplied by the
+//         two scales.  D as above, in float32.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,6 +32,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int BLK = 64;                    // tokens per block, tile side
 constexpr int HD = 64;                     // head dimension
@@ -77,6 +84,41 @@ __device__ __forceinline__ uint32_t code_bits(float x, float inv) {
 __device__ __forceinline__ int code_int(float x, float inv) {
     return (int)(code_bits(x, inv) - MAGIC_BITS);
 }
+// MXFP8 (OCP E4M3 codes, one E8M0 power-of-two scale per 32 x 32 block):
+// the least e with 448 2^e >= a, clamped to [-126, 127].  a = m 2^E with m in
+// [1, 2): e = E - 8, plus 1 when m > 1.75 (448 = 1.75 2^8); zero and
+// subnormal a clamp to -126.
+__device__ __forceinline__ int mx_exponent(float a) {
+    const uint32_t u = __float_as_uint(a);
+    const int e = (int)((u >> 23) & 0xFFu) - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+// 2^e as a float32 (e in [-126, 127]).
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// Two E4M3 codes rne(x / scale), rne(y / scale) (scale a power of two) in the
+// low (hi = false) or high 16 bits of old.
+typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t old, float x, float y, float scale, bool hi) {
+    v2s o = __builtin_bit_cast(v2s, old);
+    o = hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x, y, scale, true)
+           : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x, y, scale, false);
+    return __builtin_bit_cast(uint32_t, o);
+}
+// Four E4M3 codes of x0..x3 / scale packed in one dword (byte 0 from x0).
+__device__ __forceinline__ uint32_t fp8_quad(float x0, float x1, float x2, float x3, float scale) {
+    return fp8_pair(fp8_pair(0u, x0, x1, scale, false), x2, x3, scale, true);
+}
+
+// Value of E4M3 code byte j of w (j a constant after unrolling).
+__device__ __forceinline__ float fp8_value(uint32_t w, int j) {
+    switch (j) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+    }
+}
+
 // rne(v) for v already scaled (0 <= v < 2^22), as magic-biased bits.
 __device__ __forceinline__ uint32_t round_bits(float v) {
     return __float_as_uint(v + MAGIC);
@@ -95,11 +137,31 @@ __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
 __device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// E4M3 x E4M3 with E8M0 scales sa (this lane's row of A) and sb (column of B),
+// each a biased exponent in bits 0..7.
+__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+__device__ __forceinline__ v8i cat8(v4i x, v4i y) { return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]}; }
+// Byte i of a word of four block exponents.
+__device__ __forceinline__ int ebyte(uint32_t w, int i) { return (int)((w >> (8 * i)) & 0xFFu); }
+// A value the compiler cannot fold: a literal scale operand would be encoded
+// as an inline float constant rather than as the integer exponent.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+constexpr int E8M0_ONE = 127;              // biased exponent of 2^0
+constexpr int E4M3_ONE = 0x38;             // E4M3 code of 1.0
 
 // max(a, b, c) and max(a, |b|, |c|) as one v_max3_f32.  fmaxf in IEEE mode
 // makes the compiler quiet every operand it cannot prove canonical (one extra
 // v_max_f32 per value); the operands here are arithmetic results, never
 // signaling NaNs, so the raw instruction gives the same maximum.
+// The compiler does not look inside inline assembly when it inserts the wait
+// states between an MFMA and a VALU read of its result, so operands must
+// never come straight from an MFMA accumulator (pass them through an
+// ordinary VALU operation first).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     float d;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));

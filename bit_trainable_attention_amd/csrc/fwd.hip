@@ -249,8 +249,200 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     }
 }
 
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, hipStream_t st, bool dump) {
+// ---------------------------------------------------------------- MXFP8
+// The same work split with OCP E4M3 codes and E8M0 block exponents (one per
+// 32 tokens x 32 channels) on the scaled FP8 MFMA, which applies the block
+// scales inside the instruction: S^T = K Q^T arrives dequantized in float32,
+// so no per-tile dequantization multiply remains.  P~ = exp(S - M_t) against
+// the running row maximum M_t is coded as E4M3(256 P~) (scale 2^-8 on the
+// P~ side of V^T P~^T).  O and the row sum l accumulate in the MFMA
+// accumulators themselves (l as the product of an all-ones A operand with
+// P~^T, every row of which is the same sum) and are rescaled whenever M_t
+// rises.
+
+template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+__device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop, int sq_e, uint32_t sk_w,
+                                            uint32_t sv_w, int t, int q, int N, int lane, int h, float& M,
+                                            v16f (&O)[2], v16f& Lacc, v8i ones, int e_one, int e_pt) {
+    v16f s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma_fp8(cat8(sm.k[buf][(kb * 2 + 0) * 64 + lane], sm.k[buf][(kb * 2 + 1) * 64 + lane]), qop,
+                         v16f{}, ebyte(sk_w, 2 * kb + h), sq_e);
+    float z[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float bias[16];
+        if (SMOOTHQ) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                bias[4 * r4 + 0] = b4.x;
+                bias[4 * r4 + 1] = b4.y;
+                bias[4 * r4 + 2] = b4.z;
+                bias[4 * r4 + 3] = b4.w;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // log2-domain scores; the product also keeps the MFMA result away
+            // from the inline-assembly maximum below
+            z[kb][r] = SMOOTHQ ? __builtin_fmaf(s[kb][r], SCORE_SCALE_LOG2, bias[r]) : s[kb][r] * SCORE_SCALE_LOG2;
+            if (MASK) {
+                const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+                if (key >= N || (CAUSAL && key > q)) z[kb][r] = -__builtin_inff();
+            }
+        }
+    }
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        m0 = max3f(m0, z[0][r], z[0][r + 1]);
+        m1 = max3f(m1, z[1][r], z[1][r + 1]);
+    }
+    float mx = max3f(m0, m1, m1);
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // running maximum (log2 units); O and l follow it.  The rescale runs for
+    // the whole wave when any of its rows rises (factor 1 for the others), so
+    // the accumulators are never updated under a partial execution mask.
+    const float mt = mx;
+    const bool rise = mt > M;
+    if (__builtin_amdgcn_ballot_w64(rise)) {
+        const float alpha = !rise ? 1.0f : M > -__builtin_inff() ? __builtin_amdgcn_exp2f(M - mt) : 0.0f;
+        M = rise ? mt : M;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+        Lacc[0] *= alpha;   // only register 0 of the row-sum accumulator is read
+    }
+    const float off = -M;
+    v8i pc;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float zz = z[kb][4 * d4 + j];
+                v[j] = __builtin_amdgcn_exp2f(zz + off);
+                if (MASK && !(zz > -__builtin_inff())) v[j] = 0.0f;
+            }
+            pc[4 * kb + d4] = (int)fp8_quad(v[0], v[1], v[2], v[3], 0x1p-8f);
+        }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+        O[db] = mfma_fp8(cat8(sm.v[buf][(db * 2 + 0) * 64 + lane], sm.v[buf][(db * 2 + 1) * 64 + lane]), pc, O[db],
+                         ebyte(sv_w, 2 * h + db), e_pt);
+    Lacc = mfma_fp8(ones, pc, Lacc, e_one, e_pt);
+}
+
+template <bool CAUSAL, bool SMOOTHQ>
+__global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
+    __shared__ FwdSmem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group(a.ngroups, a.BH, bh, g);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
+    const bool live = qblk < T;
+    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;
+    const int t_last = CAUSAL ? qblk : T - 1;
+    const bool ragged = (a.N & (BLK - 1)) != 0;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
+    const v4i* kg = (const v4i*)(a.k_r + bt * 4096);
+    const v4i* vg = (const v4i*)(a.v_t + bt * 4096);
+    const float* bg = a.bias + bh * np;
+    const uint32_t* skw = (const uint32_t*)a.sk + bt;
+    const uint32_t* svw = (const uint32_t*)a.sv + bt;
+
+    // Q codes of this wave's 32 queries (B operand), the exponent of their
+    // 32-channel block h
+    v8i qop = v8i{};
+    int sq_e = E8M0_ONE;
+    if (live) {
+        const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
+        qop = cat8(src[(qhalf * 2 + 0) * 64 + lane], src[(qhalf * 2 + 1) * 64 + lane]);
+        sq_e = ebyte(((const uint32_t*)a.sq)[bt + qblk], 2 * qhalf + h);
+    }
+    const int e_one = opaque(E8M0_ONE), e_pt = opaque(E8M0_ONE - 8);
+    const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                         0x38383838};
+    const int q = qblk * BLK + 32 * qhalf + l32;
+
+    v4i pk = kg[tid], pv = vg[tid];
+    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
+    sm.k[0][tid] = pk;
+    sm.v[0][tid] = pv;
+    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
+    __syncthreads();
+
+    float M = -__builtin_inff();   // running row maximum (log2)
+    v16f O[2] = {v16f{}, v16f{}};  // [db]: lane = query, registers = channels
+    v16f Lacc = v16f{};            // register 0: the row sum of the dequantized P~
+
+    for (int t = 0; t <= t_last_wg; ++t) {
+        const int buf = t & 1;
+        const bool more = t < t_last_wg;
+        if (more) {
+            pk = kg[(size_t)(t + 1) * 256 + tid];
+            pv = vg[(size_t)(t + 1) * 256 + tid];
+            if (SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
+        }
+        if (live && t <= t_last) {
+            const uint32_t sk_w = skw[t], sv_w = svw[t];
+            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+                fwd_tile_mx<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O, Lacc,
+                                                   ones, e_one, e_pt);
+            else
+                fwd_tile_mx<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O, Lacc,
+                                                    ones, e_one, e_pt);
+        }
+        if (more) {
+            sm.k[buf ^ 1][tid] = pk;
+            sm.v[buf ^ 1][tid] = pv;
+            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
+        }
+        __syncthreads();
+    }
+
+    if (live && q < a.N) {
+        const float Lt = Lacc[0];
+        const float inv_l = 1.0f / Lt;
+        uint16_t* orow = a.o + ((size_t)bh * a.N + q) * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * h;
+                const uint32_t w0 = f32_to_bf16_rne(O[db][4 * r4 + 0] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 1] * inv_l) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(O[db][4 * r4 + 2] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 3] * inv_l) << 16);
+                *(uint2*)(orow + d) = make_uint2(w0, w1);
+            }
+        if (h == 0) a.lse[(size_t)bh * a.N + q] = (M + log2f(Lt)) * LN2 + a.corr[bh * np + q];
+    }
+}
+
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, bool mx, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * FWD_WAVES);
+    if (mx) {
+        if (causal) {
+            if (smooth_q) hipLaunchKernelGGL((k_fwd_mx<true, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd_mx<true, false>), grid, block, 0, st, a);
+        } else {
+            if (smooth_q) hipLaunchKernelGGL((k_fwd_mx<false, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd_mx<false, false>), grid, block, 0, st, a);
+        }
+        return 0;
+    }
 #define SAGEBWD_FWD(C, S)                                                                        \
     do {                                                                                         \
         if (dump) hipLaunchKernelGGL((k_fwd<C, S, true>), grid, block, 0, st, a);                \

@@ -22,7 +22,7 @@ struct QuantArgs {
     const float *mu_q, *mu_k;          // [BH][64]
     int8_t *q_r, *k_r;                 // row operand layout (nullable)
     int8_t *q_t, *k_t, *v_t;           // transposed operand layout (nullable)
-    float *sq, *sk, *sv;               // [BH][T]
+    float *sq, *sk, *sv;               // [BH][T] (MX: 4 exponent bytes per block)
     float* corr;                       // [BH][Np]
     float* bias;                       // [BH][Np]
     int N, T, smooth_q, smooth_k;
@@ -34,7 +34,7 @@ struct BwdPreArgs {
     const float* corr;                 // [BH][Np]
     float *delta, *lse2;               // [BH][Np]: -rowsum(dO*O), log2-domain LSE
     int8_t* do_t;                      // transposed operand layout
-    float* sdo;                        // [BH][T]
+    float* sdo;                        // [BH][T] (MX: 4 exponent bytes per block)
     int8_t *do_r, *v_r;                // row-operand dO and V codes, or null (INT8 dO V^T only)
     float* sv;                         // [BH][T] V block scales, with v_r
     _Float16 *do16, *v16;              // [BH][Np][64]
@@ -43,7 +43,7 @@ struct BwdPreArgs {
 
 int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, int N, int T, int BH, hipStream_t st);
 int launch_means(const MeansArgs& m, hipStream_t st);
-int launch_quantize(const QuantArgs& a, int BH, int ntensors, hipStream_t st);
-int launch_bwd_pre(const BwdPreArgs& a, int BH, hipStream_t st);
+int launch_quantize(const QuantArgs& a, int BH, int ntensors, bool mx, hipStream_t st);
+int launch_bwd_pre(const BwdPreArgs& a, int BH, bool mx, hipStream_t st);
 
 }  // namespace sagebwd

@@ -144,7 +144,23 @@ __device__ __forceinline__ void store_transposed(const int8_t (*codes)[HD], int8
     *(uint4*)(dst + tid * 16) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// tensor 0 = Q, 1 = K, 2 = V.
+// MXFP8: the absmax of this thread's 32 x 32 block (tokens 32 (r/32).., channels
+// 32 (g/2)..) over the 4 waves of the workgroup: lanes of one wave share a
+// block when they differ only in lane bits 0 (g % 2) and 2..5 (token).
+__device__ __forceinline__ float mx_block_absmax(float v, float (*red)[2]) {
+#pragma unroll
+    for (int o : {1, 4, 8, 16, 32}) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int w = threadIdx.x / 64, cb = (threadIdx.x % 4) / 2;
+    if ((threadIdx.x & 61) == 0) red[w][cb] = v;       // lanes 0 and 2 of each wave
+    __syncthreads();
+    const int tb = threadIdx.x / 128;
+    return fmaxf(red[2 * tb][cb], red[2 * tb + 1][cb]);
+}
+
+// tensor 0 = Q, 1 = K, 2 = V.  MX: E4M3 codes and E8M0 scales instead of INT8
+// codes and absmax/127 scales (same code layouts; the scale slot of a 64x64
+// block holds its four exponent bytes + 127, byte 2 (token half) + channel half).
+template <bool MX>
 __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
     const int t = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
     const int r = threadIdx.x / 4, g = threadIdx.x % 4;
@@ -182,22 +198,38 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         amax = fmaxf(amax, fabsf(x[j]));
     }
     __shared__ float red[4];
+    __shared__ float red_mx[4][2];
     __shared__ int8_t codes[BLK][HD];
-    const float a_blk = block_absmax_256(amax, red);
-    float s, inv;
-    block_scale(a_blk, s, inv);
     const size_t blk = (size_t)bh * a.T + t;
     float* scale_out = tensor == 0 ? a.sq : tensor == 1 ? a.sk : a.sv;
-    if (threadIdx.x == 0) scale_out[blk] = s;
-
     uint32_t cw[4] = {0, 0, 0, 0};
-    float mu_dot = 0.0f;   // K only: sum_c mu_q[c] * code[c]
+    float mu_dot = 0.0f;   // K only: sum_c mu_q[c] * code[c] (dequantized code for MX)
+    float s;
+    if (MX) {
+        const int e = mx_exponent(mx_block_absmax(amax, red_mx));
+        const float sc = pow2f(e);
+        if (r % 32 == 0 && g % 2 == 0) ((uint8_t*)scale_out)[blk * 4 + 2 * (r / 32) + g / 2] = (uint8_t)(e + 127);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int cq = code_int(x[j], inv);
-        codes[r][16 * g + j] = (int8_t)cq;
-        cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
-        if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], (float)cq, mu_dot);
+        for (int j4 = 0; j4 < 4; ++j4) cw[j4] = fp8_quad(x[4 * j4], x[4 * j4 + 1], x[4 * j4 + 2], x[4 * j4 + 3], sc);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int byte = (cw[j / 4] >> (8 * (j % 4))) & 0xFF;
+            codes[r][16 * g + j] = (int8_t)byte;
+            if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], fp8_value(cw[j / 4], j % 4), mu_dot);
+        }
+        s = sc;
+    } else {
+        const float a_blk = block_absmax_256(amax, red);
+        float inv;
+        block_scale(a_blk, s, inv);
+        if (threadIdx.x == 0) scale_out[blk] = s;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int cq = code_int(x[j], inv);
+            codes[r][16 * g + j] = (int8_t)cq;
+            cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
+            if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], (float)cq, mu_dot);
+        }
     }
     int8_t* rdst = tensor == 0 ? a.q_r : tensor == 1 ? a.k_r : nullptr;
     if (rdst) *(uint4*)(rdst + blk * 4096 + row_operand_offset(r, 16 * g)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
@@ -213,9 +245,13 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         cd += __shfl_xor(cd, 2, 64);
         if (g == 0) a.corr[(size_t)bh * a.T * BLK + tok] = valid ? cd * 0.125f : 0.0f;
     } else if (tensor == 1) {
+        // MX: the two channel halves of a token have their own scale, so each
+        // thread scales its partial sum before the reduction
+        if (MX) mu_dot *= s;
         mu_dot += __shfl_xor(mu_dot, 1, 64);
         mu_dot += __shfl_xor(mu_dot, 2, 64);
-        if (g == 0) a.bias[(size_t)bh * a.T * BLK + tok] = (valid && a.smooth_q) ? mu_dot * s * SCORE_SCALE_LOG2 : 0.0f;
+        const float bias = MX ? mu_dot * SCORE_SCALE_LOG2 : mu_dot * s * SCORE_SCALE_LOG2;
+        if (g == 0) a.bias[(size_t)bh * a.T * BLK + tok] = (valid && a.smooth_q) ? bias : 0.0f;
     }
 
     int8_t* tdst = tensor == 0 ? a.q_t : tensor == 1 ? a.k_t : a.v_t;
@@ -232,6 +268,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
 // LSE is +inf so every P of such a row is 0).  For the all-INT8 ablation also
 // the dO codes in the row-operand layout and the V codes (the same quantizer
 // as the forward's, V not centred) with their block scales.
+template <bool MX>
 __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     const int t = blockIdx.x, bh = blockIdx.y;
     const int r = threadIdx.x / 4, g = threadIdx.x % 4;
@@ -293,18 +330,29 @@ __global__ __launch_bounds__(256) void k_bwd_pre(BwdPreArgs a) {
     }
     // dO codes
     __shared__ float red[4];
+    __shared__ float red_mx[4][2];
     __shared__ int8_t codes[BLK][HD];
-    const float a_blk = block_absmax_256(amax, red);
-    float s, inv;
-    block_scale(a_blk, s, inv);
     const size_t blk = (size_t)bh * a.T + t;
-    if (threadIdx.x == 0) a.sdo[blk] = s;
     uint32_t cw[4] = {0, 0, 0, 0};
+    if (MX) {
+        const int e = mx_exponent(mx_block_absmax(amax, red_mx));
+        const float sc = pow2f(e);
+        if (r % 32 == 0 && g % 2 == 0) ((uint8_t*)a.sdo)[blk * 4 + 2 * (r / 32) + g / 2] = (uint8_t)(e + 127);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int cq = code_int(dov[j], inv);
-        codes[r][16 * g + j] = (int8_t)cq;
-        cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
+        for (int j4 = 0; j4 < 4; ++j4) cw[j4] = fp8_quad(dov[4 * j4], dov[4 * j4 + 1], dov[4 * j4 + 2], dov[4 * j4 + 3], sc);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) codes[r][16 * g + j] = (int8_t)((cw[j / 4] >> (8 * (j % 4))) & 0xFF);
+    } else {
+        const float a_blk = block_absmax_256(amax, red);
+        float s, inv;
+        block_scale(a_blk, s, inv);
+        if (threadIdx.x == 0) a.sdo[blk] = s;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int cq = code_int(dov[j], inv);
+            codes[r][16 * g + j] = (int8_t)cq;
+            cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
+        }
     }
     if (a.do_r) *(uint4*)(a.do_r + blk * 4096 + row_operand_offset(r, 16 * g)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     __syncthreads();
@@ -338,13 +386,15 @@ int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, i
     return 0;
 }
 
-int launch_quantize(const QuantArgs& a, int BH, int ntensors, hipStream_t st) {
-    hipLaunchKernelGGL(k_quantize, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
+int launch_quantize(const QuantArgs& a, int BH, int ntensors, bool mx, hipStream_t st) {
+    if (mx) hipLaunchKernelGGL(k_quantize<true>, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_quantize<false>, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
     return 0;
 }
 
-int launch_bwd_pre(const BwdPreArgs& a, int BH, hipStream_t st) {
-    hipLaunchKernelGGL(k_bwd_pre, dim3(a.T, BH), dim3(256), 0, st, a);
+int launch_bwd_pre(const BwdPreArgs& a, int BH, bool mx, hipStream_t st) {
+    if (mx) hipLaunchKernelGGL(k_bwd_pre<true>, dim3(a.T, BH), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(k_bwd_pre<false>, dim3(a.T, BH), dim3(256), 0, st, a);
     return 0;
 }
 

@@ -73,11 +73,25 @@ typedef struct sagebwd_params {
                            with respect to the Q, K passed in, through
                            dx = r (dx_n - x_n mean_c(dx_n x_n)).  Forward and
                            backward must be called with the same value. */
+    int32_t mxfp8;      /* 0 or 1: the FP8 quantization that the SageBwd page
+                           compares with INT8 (and finds less accurate), in
+                           the form MI355X's scaled FP8 matrix instructions
+                           take: every quantized operand (Q, K, V, dO, P, dS)
+                           as OCP FP8 E4M3 codes with one power-of-two (E8M0)
+                           scale per 32x32 block, 2^e with e the least integer
+                           such that 448 2^e >= the block's absmax, clamped to
+                           [-126, 127]; the forward's P~ = exp(S - running row
+                           max) coded as E4M3(256 P~).  Smoothing, QK-norm,
+                           the FP16 dO V^T and the outputs are as in the INT8
+                           mode.  Not with int8_dp (SAGEBWD_ERR_UNSUPPORTED)
+                           nor with sagebwd_debug_tile.  Forward and backward
+                           must be called with the same value. */
 } sagebwd_params;
 
 #define SAGEBWD_OK               0
 #define SAGEBWD_ERR_INVALID_ARG (-1)   /* null pointer, size < 1, flag not 0/1, misaligned */
-#define SAGEBWD_ERR_UNSUPPORTED (-2)   /* D != 64, or N or B*H beyond the supported range */
+#define SAGEBWD_ERR_UNSUPPORTED (-2)   /* D != 64, N or B*H beyond the supported range, mxfp8 with
+                                          int8_dp, or an entry point without an mxfp8 form */
 #define SAGEBWD_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the required size */
 #define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
 
@@ -192,7 +206,11 @@ const char* sagebwd_status_string(int status);
  *                                    and byte b the query
  *                                    32 qs + 8(b/4) + 4(l/32) + b%4
  *   23 DS_SCALE float32 [G][tiles]   their block scales s_dS
- * with T = ceil(N/64), Np = 64 T.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
+ * with T = ceil(N/64), Np = 64 T.  With mxfp8 the code regions hold E4M3
+ * code bytes in the same layouts, and each 4-byte block scale (regions 8-11)
+ * holds the four biased exponents e + 127 of the block's 32x32 sub-blocks,
+ * byte 2*(r/32) + c/32 (token half, channel half); a DS_SCALE entry holds
+ * those of its dS tile, byte 2*(key half) + query half.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
  * 64 channels, element (token r, channel c) sits at byte
  *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16
  *   transposed operand:  ((c/32*2 + r/32)*64 + 32*((r%8)/4) + c%32)*16

@@ -37,10 +37,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def P(**kw):
-    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0, qk_norm=0)
+    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0, qk_norm=0, mxfp8=0)
     d.update(kw)
     return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"], d["int8_dp"],
-                     d["qk_norm"])
+                     d["qk_norm"], d["mxfp8"])
 
 
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -67,6 +67,13 @@ def test_param_validation(lib):
     assert call_fwd(lib, P(int8_dp=2)) == INVALID
     assert call_bwd(lib, P(int8_dp=-1)) == INVALID
     assert call_fwd(lib, P(qk_norm=3)) == INVALID
+    assert call_fwd(lib, P(mxfp8=2)) == INVALID
+    assert call_bwd(lib, P(mxfp8=1, int8_dp=1)) == UNSUPPORTED     # the INT8 ablation has no MXFP8 form
+    assert lib.sagebwd_bwd_workspace_size(ctypes.byref(P(mxfp8=1, int8_dp=1))) == 0
+    assert lib.sagebwd_bwd_workspace_size(ctypes.byref(P(mxfp8=1))) == lib.sagebwd_bwd_workspace_size(ctypes.byref(P()))
+    # the tile dump exists for the INT8 kernels only
+    assert lib.sagebwd_debug_tile(ctypes.byref(P(mxfp8=1)), 0, 0, 0, 0, *([FAKE] * 10), FAKE, 1 << 20, FAKE, 1 << 40,
+                                  None) == UNSUPPORTED
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED
     assert call_fwd(lib, P(N=(1 << 18) + 1)) == UNSUPPORTED
     assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED
@@ -114,10 +121,10 @@ def test_prepare_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, 10) == WORKSPACE
 
 
-@pytest.mark.parametrize("int8_dp,qk_norm", [(0, 0), (1, 0), (0, 1), (1, 1)])
-def test_ws_regions_layout(lib, int8_dp, qk_norm):
+@pytest.mark.parametrize("int8_dp,qk_norm,mxfp8", [(0, 0, 0), (1, 0, 0), (0, 1, 0), (1, 1, 0), (0, 0, 1), (0, 1, 1)])
+def test_ws_regions_layout(lib, int8_dp, qk_norm, mxfp8):
     for N in (1, 63, 64, 65, 1000, 17776):
-        p = P(B=2, H=3, N=N, int8_dp=int8_dp, qk_norm=qk_norm)
+        p = P(B=2, H=3, N=N, int8_dp=int8_dp, qk_norm=qk_norm, mxfp8=mxfp8)
         BH, T = 6, (N + 63) // 64
         Np = 64 * T
         expect = {"MU_Q": BH * 256, "MU_K": BH * 256, "Q_R": BH * T * 4096, "K_R": BH * T * 4096,

@@ -1,0 +1,272 @@
+"""Parity of the MXFP8 mode (E4M3 codes, E8M0 exponents per 32x32 block) with
+the oracle's MXFP8 mode.
+
+The preparation is compared bit for bit: every E4M3 code of Q, K, V and dO in
+both operand layouts and every block exponent (both sides quantize the same
+float32 values with round-to-nearest-even).  The attention outputs are
+compared element by element with the oracle (relative L2 <= 1e-2), on small
+cases spanning several tiles and ragged tails, and on one sampled head of
+full-size workloads in the launch configuration bench.py times; against
+exact attention the MXFP8 mode is held to looser cosine bars than INT8 (the
+SageBwd page finds FP8 less accurate than INT8)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_trainable_attention_amd as sb
+import workloads as W
+from oracle import exact, metrics as M, mxfp8 as X
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2                 # HIP vs the oracle's MXFP8 mode, O / dQ / dK / dV
+# LSE: the two sides compute the scores with different rounding (float32 and
+# the MFMA's accumulation against float64), so a P~ code whose 256 P~ lies
+# next to a rounding midpoint can round to neighbouring E4M3 values.  One such
+# flip moves the row sum l (>= 1, the row maximum's code is exactly 256) by
+# one E4M3 step of a code <= 256, at most 1/16 of l: |dLSE| <= ln(17/16).
+# Flips are rare, so the mean error stays at float32 level.
+LSE_MAX = 0.0625
+LSE_MEAN = 2e-4
+COS_O, COS_G = 0.995, 0.98    # HIP vs exact attention
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    W.custom(1, 2, 200, True, True, True, "kbias", 151),
+    W.custom(2, 1, 129, False, True, True, "outlier", 152),
+    W.custom(1, 1, 320, False, False, False, "normal", 154),
+    W.custom(1, 1, 1, True, True, True, "normal", 155),
+    W.custom(1, 1, 63, True, True, False, "normal", 156),
+    W.custom(1, 1, 65, True, True, True, "kbias", 158),
+]
+
+
+def _ids(ws):
+    return [f"{w.name}_c{int(w.causal)}q{int(w.smooth_q)}k{int(w.smooth_k)}" for w in ws]
+
+
+def _bf16(x):
+    return W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+def _codes_bytes(wsh, p, name, kind, BH, T):
+    return G.decode_codes(wsh, p, name, kind, BH, T).view(np.uint8)
+
+
+def _exponents(wsh, p, name, BH, T):
+    """[BH, 2T, 2] unbiased exponents of the 32x32 blocks (token block, channel half)."""
+    e = G.region(wsh, p, name, np.uint8).reshape(BH, T, 2, 2).astype(np.int64) - 127
+    return e.reshape(BH, 2 * T, 2)
+
+
+def _same_values(got_bytes, codes):
+    """E4M3 bytes decode to exactly the oracle's codes (the sign of a zero aside)."""
+    assert not np.any((got_bytes & 0x7F) == 0x7F), "NaN code"
+    return np.array_equal(X.E4M3_VALUES[got_bytes], codes)
+
+
+PREP = [
+    W.WORKLOADS["tiny"],
+    W.custom(1, 2, 200, True, True, True, "kbias", 141),
+    W.custom(2, 1, 129, False, True, True, "outlier", 142),
+    W.custom(1, 1, 1, True, True, True, "normal", 143),
+    W.custom(1, 2, 65, False, False, False, "normal", 144),
+    W.custom(1, 2, 130, True, True, True, "rowscale", 145),
+]
+
+
+@pytest.mark.parametrize("w", PREP, ids=_ids(PREP))
+@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
+def test_mx_prepare_bit_exact(w, qk_norm):
+    print(f"[mx prepare] {w.name} B{w.B} H{w.H} N{w.N} qk_norm={qk_norm}", flush=True)
+    x = W.make_inputs(w)
+    r = np.random.default_rng(6)
+    o_bits = W.f32_to_bf16_bits(r.standard_normal(x["q"].shape).astype(np.float32))
+    lse = (r.standard_normal(x["q"].shape[:3]) * 3 + 5).astype(np.float32)
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    ws = sb.prepare(tq, tk, tv, G.dev(o_bits), torch.from_numpy(lse).cuda(), tdo, w.causal, w.smooth_q, w.smooth_k,
+                    qk_norm=qk_norm, mxfp8=True)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, qk_norm=qk_norm, mxfp8=True)
+    BH, T = w.B * w.H, (w.N + 63) // 64
+    Np = 64 * T
+    got = {n: _codes_bytes(wsh, p, reg, kind, BH, T) for n, reg, kind in
+           (("q_r", "Q_R", "row"), ("k_r", "K_R", "row"), ("q_t", "Q_T", "t"), ("k_t", "K_T", "t"),
+            ("v_t", "V_T", "t"), ("do_t", "DO_T", "t"))}
+    ex = {n: _exponents(wsh, p, reg, BH, T) for n, reg in (("q", "S_Q"), ("k", "S_K"), ("v", "S_V"), ("do", "S_DO"))}
+    bias = G.region(wsh, p, "BIAS", np.float32).reshape(BH, Np)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    for b in range(w.B):
+        for h in range(w.H):
+            i = b * w.H + h
+            pp = X.prepare(f32["q"][b, h], f32["k"][b, h], f32["v"][b, h], w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+            bp = X.prepare_bwd(pp, f32["v"][b, h], W.bf16_bits_to_f32(o_bits[b, h]), lse[b, h], f32["do"][b, h])
+            for name, deq, e, regs in (("q", pp.qh, pp.eq, ("q_r", "q_t")), ("k", pp.kh, pp.ek, ("k_r", "k_t")),
+                                       ("v", pp.vh, pp.ev, ("v_t",)), ("do", bp.doh, bp.edo, ("do_t",))):
+                assert np.array_equal(ex[name][i], e), (name, b, h)
+                codes = deq * np.ldexp(1.0, -np.repeat(np.repeat(e, 32, axis=0), 32, axis=1))
+                for reg in regs:
+                    assert _same_values(got[reg][i], codes), (reg, b, h)
+            # Q-smoothing bias: a float32 sum of 64 products (order differs)
+            want = pp.b * (np.log2(np.e) / 8) if w.smooth_q else np.zeros(Np)
+            tol = 1e-5 * (np.abs(pp.kh) @ np.abs(np.asarray(pp.mu_q, np.float64))) + 1e-30
+            assert np.all(np.abs(bias[i] - want) <= tol), (b, h)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids(SMALL))
+def test_mx_forward_parity(w):
+    print(f"[mx fwd] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    o, lse = sb.fwd(G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]), w.causal, w.smooth_q, w.smooth_k, mxfp8=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o), lse.cpu().numpy()
+    o_f, lse_f = X.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k)
+    o_e, lse_e = exact.fwd_bh(f32["q"], f32["k"], f32["v"], w.causal)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    print(f"  O: rel-L2 vs oracle {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}, "
+          f"LSE max err {np.max(np.abs(lse_g - lse_f)):.2e} mean {np.mean(np.abs(lse_g - lse_f)):.2e}")
+    assert M.rel_l2(o_g, o_f) <= REL_L2, M.rel_l2(o_g, o_f)
+    _check_lse(lse_g, lse_f)
+    assert M.cos_sim(o_g, o_e) >= COS_O
+    # E4M3 Q and K codes move the scores by up to ~2^-4 of their size, so the
+    # oracle's own LSE is up to ~0.17 from exact attention on these cases
+    assert np.max(np.abs(lse_g - lse_e)) <= 0.3
+
+
+def _check_lse(a, b):
+    err = np.abs(a - b)
+    assert np.max(err) <= LSE_MAX and np.mean(err) <= LSE_MEAN, (np.max(err), np.mean(err))
+
+
+def _check_grads(g, ref, ex, N):
+    for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
+        assert np.all(np.isfinite(a)), name
+        print(f"  {name}: rel-L2 vs oracle {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
+        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
+        # one token: exact attention has dS = 0, so dQ = dK = 0; the method's
+        # O is the E4M3-coded V, so its dS = dO.(V - O) is a few percent of
+        # dO.V and only the oracle comparison applies to dQ and dK
+        if N > 1 or name == "dV":
+            assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids(SMALL))
+def test_mx_backward_parity(w):
+    """The backward alone: both sides take the oracle's O (bf16) and LSE."""
+    print(f"[mx bwd] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    o_f, lse_f = X.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k)
+    o_bits = W.f32_to_bf16_bits(o_f.astype(np.float32))
+    lse32 = lse_f.astype(np.float32)
+    dq, dk, dv = sb.bwd(G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]), G.dev(o_bits), torch.from_numpy(lse32).cuda(),
+                        G.dev(x["do"]), w.causal, w.smooth_q, w.smooth_k, mxfp8=True)
+    torch.cuda.synchronize()
+    g = [G.host_f32(t) for t in (dq, dk, dv)]
+    ref = X.bwd(f32["q"], f32["k"], f32["v"], W.bf16_bits_to_f32(o_bits), lse32, f32["do"], w.causal,
+                w.smooth_q, w.smooth_k)
+    ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal)
+    _check_grads(g, ref, ex, w.N)
+
+
+E2E = [SMALL[1], SMALL[2], W.custom(1, 2, 256, True, True, False, "qknorm", 153)]
+
+
+@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
+@pytest.mark.parametrize("w", E2E, ids=_ids(E2E))
+def test_mx_end_to_end_and_determinism(w, qk_norm):
+    """Each side feeds its own forward into its own backward; the GPU pass is
+    bitwise repeatable with and without reusing the forward's workspace."""
+    print(f"[mx e2e] {w.name} qk_norm={qk_norm}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    outs = []
+    for reuse in (False, True):
+        ws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, qk_norm=qk_norm,
+                                           mxfp8=True), dtype=torch.uint8, device="cuda") if reuse else None
+        o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, workspace=ws, qk_norm=qk_norm, mxfp8=True)
+        dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k, fwd_workspace=ws,
+                            qk_norm=qk_norm, mxfp8=True)
+        torch.cuda.synchronize()
+        outs.append([G.host_bits(t) for t in (o, dq, dk, dv)] + [lse.cpu().numpy().view(np.uint32)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    o_f, lse_f = X.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+    assert M.rel_l2(W.bf16_bits_to_f32(outs[0][0]), o_f) <= REL_L2
+    ref = X.bwd(f32["q"], f32["k"], f32["v"], _bf16(o_f), lse_f.astype(np.float32), f32["do"], w.causal,
+                w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+    ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal, qk_norm=qk_norm)
+    _check_grads([W.bf16_bits_to_f32(a) for a in outs[0][1:4]], ref, ex, w.N)
+
+
+def test_mx_zero_inputs():
+    z = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
+    for causal in (False, True):
+        o, lse = sb.fwd(z, z, z, causal, True, True, mxfp8=True)
+        dq, dk, dv = sb.bwd(z, z, z, o, lse, z, causal, True, True, mxfp8=True)
+        torch.cuda.synchronize()
+        for t in (o, dq, dk, dv):
+            assert torch.all(t == 0)
+        n = torch.arange(1, 101, device="cuda", dtype=torch.float32) if causal else torch.full((100,), 100.0, device="cuda")
+        assert torch.allclose(lse[0, 0], torch.log(n), atol=1e-5)
+
+
+def test_mx_rejections():
+    z = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(sb.SageBwdError):
+        sb.bwd(z, z, z, z, torch.zeros(1, 1, 64, device="cuda"), z, mxfp8=True, int8_dp=True)
+    with pytest.raises(sb.SageBwdError, match="unsupported"):
+        sb.debug_tile("fwd", 0, 0, 0, z, z, z, torch.empty_like(z), torch.zeros(1, 1, 64, device="cuda"),
+                      mxfp8=True)
+
+
+FULL = [("llama16k", (0, 29)), ("video", (1, 3))]
+
+
+@pytest.mark.parametrize("name,head", FULL, ids=[c[0] for c in FULL])
+def test_mx_fullsize_sampled_parity(name, head):
+    """One sampled head of the full workload, the forward over all its rows and
+    the backward's first, middle and last query and key blocks, end to end."""
+    w = W.WORKLOADS[name]
+    b, h = head
+    print(f"[mx fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} head={head}", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    fws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, mxfp8=True),
+                      dtype=torch.uint8, device="cuda")
+    o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, workspace=fws, mxfp8=True)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k, fwd_workspace=fws, mxfp8=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o[b, h]), lse[b, h].cpu().numpy()
+    dq_g, dk_g, dv_g = (G.host_f32(t[b, h]) for t in (dq, dk, dv))
+    for t in (o_g, lse_g, dq_g, dk_g, dv_g):
+        assert np.all(np.isfinite(t))
+    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv, fws
+    f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
+    N, T = w.N, (w.N + 63) // 64
+    pp = X.prepare(f["q"], f["k"], f["v"], w.smooth_q, w.smooth_k)
+    o_f, lse_f = X.fwd_head(pp, w.causal)
+    o_f, lse_f = o_f[:N], lse_f[:N]
+    assert M.rel_l2(o_g, o_f) <= REL_L2, M.rel_l2(o_g, o_f)
+    _check_lse(lse_g, lse_f)
+    blocks = sorted({0, T // 2, T - 1})
+    rows = np.concatenate([np.arange(i * 64, min(N, i * 64 + 64)) for i in blocks])
+    bp = X.prepare_bwd(pp, f["v"], _bf16(o_f), lse_f.astype(np.float32), f["do"])
+    dq_f, dk_f, dv_f = X.bwd_head(bp, w.causal, blocks, blocks)
+    sel = np.concatenate([np.arange(j * 64, j * 64 + min(64, N - i * 64)) for j, i in enumerate(blocks)])
+    errs = {"dQ": M.rel_l2(dq_g[rows], dq_f[sel]), "dK": M.rel_l2(dk_g[rows], dk_f[sel]),
+            "dV": M.rel_l2(dv_g[rows], dv_f[sel])}
+    print("  rel-L2 vs oracle:", {k: f"{v:.2e}" for k, v in errs.items()}, f"O {M.rel_l2(o_g, o_f):.2e}", flush=True)
+    for k, v in errs.items():
+        assert v <= REL_L2, (k, v)
+    oe, le, dqe, dke, dve = exact.sampled(f["q"], f["k"], f["v"], f["do"], w.causal, rows, rows)
+    cos = {"O": M.cos_sim(o_g[rows], oe), "dQ": M.cos_sim(dq_g[rows], dqe), "dK": M.cos_sim(dk_g[rows], dke),
+           "dV": M.cos_sim(dv_g[rows], dve)}
+    print("  cos vs exact:", {k: f"{v:.6f}" for k, v in cos.items()}, flush=True)
+    assert cos["O"] >= COS_O
+    for k in ("dQ", "dK", "dV"):
+        assert cos[k] >= COS_G, (k, cos[k])
