@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd attention TOPS, causal H=32 d=64 N=8K/16K; % of MFMA peak"
-INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published
+INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published (dense FP8 is the same 5.0 PFLOP/s)
 KERNEL_SOURCES = {
     "FWD_ATTN": ["fwd.hip", "attn.h", "common.h"],
     "BWD_DKDV": ["bwd.hip", "attn.h", "common.h"],
@@ -64,15 +64,18 @@ def load_traffic(stage: str, workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
-    """Time the oracle (faithful forward + backward) on whole heads of a
-    causal-prefix sub-problem of the workload: the first n tokens of head
-    (0, h), h = 0, 1, ... until about ``seconds`` have elapsed."""
+def cpu_baseline(w, seconds: float, mxfp8: bool = False):
+    """Time the oracle (faithful forward + backward, or its MXFP8 mode) on
+    whole heads of a causal-prefix sub-problem of the workload: the first n
+    tokens of head (0, h), h = 0, 1, ... until about ``seconds`` have
+    elapsed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import workloads as W
-    from oracle import faithful as F
+    from oracle import faithful, mxfp8 as mx
+
+    F = mx if mxfp8 else faithful
 
     n = min(w.N, 2048)
     done_heads = 0
@@ -92,7 +95,7 @@ def cpu_baseline(w, seconds: float):
     ops = done_heads * 14.0 * n * n * 64 * (0.5 if w.causal else 1.0)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"faithful fwd+bwd of {done_heads} whole head(s) of the first {n} tokens of {w.name} "
+            "sample": f"{'mxfp8' if mxfp8 else 'faithful'} fwd+bwd of {done_heads} whole head(s) of the first {n} tokens of {w.name} "
                       f"(causal={w.causal}) in {el:.1f} s; {os.cpu_count()} host cores visible, "
                       f"BLAS threads {threads}"}
 
@@ -108,6 +111,8 @@ def main():
     ap.add_argument("--int8-dp", action="store_true",
                     help="time the all-INT8 ablation (dO V^T from INT8 codes) instead of the method's FP16 dO V^T")
     ap.add_argument("--qk-norm", action="store_true", help="fuse QK-norm into the path (normalizes the inputs' rows)")
+    ap.add_argument("--mxfp8", action="store_true",
+                    help="time the MXFP8 mode (E4M3 codes, E8M0 exponents per 32x32 block) instead of INT8")
     ap.add_argument("--no-reuse", action="store_true",
                     help="let the backward re-quantize Q and K instead of reading the forward's workspace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -134,7 +139,8 @@ def main():
 
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     del x
-    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp, qk_norm=args.qk_norm)
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp, qk_norm=args.qk_norm,
+                       mxfp8=args.mxfp8)
     lib = sb.load_library()
     import ctypes
     ws_f = torch.empty(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
@@ -190,7 +196,8 @@ def main():
     dom = max((s for s in KERNEL_UNITS if s in stage_ms), key=lambda s: stage_ms[s])
     ach = KERNEL_UNITS[dom] * unit / (stage_ms[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name),
+            "frac": round(ach / INT8_PEAK_TOPS, 4),
+            "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name + ("_mxfp8" if args.mxfp8 else "")),
             "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {
         "metric": METRIC,
@@ -203,12 +210,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if args.int8_dp else "i8 (dO.V^T f16)",
+        "dtype": "i8" if args.int8_dp else "e4m3 (dO.V^T f16)" if args.mxfp8 else "i8 (dO.V^T f16)",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
                    "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp),
-                   "qk_norm": bool(args.qk_norm)},
+                   "qk_norm": bool(args.qk_norm), "mxfp8": bool(args.mxfp8)},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         # 12 of the 14 N^2 d units are INT8 and 2 (dO V^T, fwd-side none) FP16 at half the INT8 rate,
         # so the MFMA floor of the mix is 14/16 of the INT8 peak
@@ -217,7 +224,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.mxfp8)
     print(json.dumps(out), flush=True)
 
 
