@@ -27,10 +27,14 @@ Modules:
   mxfp8     -- the FP8 variant for MI355X's scaled matrix instructions: OCP
                E4M3 codes with one power-of-two (E8M0) scale per 32 x 32 block,
                step by step, with the same ``rounding=False`` switch.
+  fp4       -- the FP4 inference forward (SageAttention3 summary, "Approach")
+               in the MXFP4 form of MI355X's scaled matrix instructions: E2M1
+               codes with one E8M0 scale per 32 values of the contraction
+               index, step by step, with the same ``rounding=False`` switch.
   metrics   -- cosine similarity, relative L2, L1, RMSE.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against something
 other than itself: finite differences, closed forms, invariants, brute-force
 integer products, an exact-rational quantizer and the rounding-free reduction.
 """
-from . import exact, faithful, metrics, mxfp8  # noqa: F401
+from . import exact, faithful, fp4, metrics, mxfp8  # noqa: F401
