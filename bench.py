@@ -28,7 +28,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fwd+bwd attention TOPS, causal H=32 d=64 N=8K/16K; % of MFMA peak"
+METRIC_FP4 = "fwd attention TOPS (FP4 inference forward), causal H=32 d=64 N=16K; % of MFMA peak"
 INT8_PEAK_TOPS = 5000.0          # MI355X dense INT8 MFMA, published (dense FP8 is the same 5.0 PFLOP/s)
+FP4_PEAK_TOPS = 10100.0          # MI355X dense FP4 MFMA, published
 KERNEL_SOURCES = {
     "FWD_ATTN": ["fwd.hip", "attn.h", "common.h"],
     "BWD_DKDV": ["bwd.hip", "attn.h", "common.h"],
@@ -64,18 +66,18 @@ def load_traffic(stage: str, workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float, mxfp8: bool = False):
-    """Time the oracle (faithful forward + backward, or its MXFP8 mode) on
-    whole heads of a causal-prefix sub-problem of the workload: the first n
-    tokens of head (0, h), h = 0, 1, ... until about ``seconds`` have
-    elapsed."""
+def cpu_baseline(w, seconds: float, mode: str = "int8"):
+    """Time the oracle (faithful forward + backward, its MXFP8 mode, or the
+    FP4 forward alone) on whole heads of a causal-prefix sub-problem of the
+    workload: the first n tokens of head (0, h), h = 0, 1, ... until about
+    ``seconds`` have elapsed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import workloads as W
-    from oracle import faithful, mxfp8 as mx
+    from oracle import faithful, fp4, mxfp8
 
-    F = mx if mxfp8 else faithful
+    F = {"int8": faithful, "mxfp8": mxfp8, "fp4": fp4}[mode]
 
     n = min(w.N, 2048)
     done_heads = 0
@@ -85,17 +87,18 @@ def cpu_baseline(w, seconds: float, mxfp8: bool = False):
         f = {k: W.bf16_bits_to_f32(v)[:n] for k, v in x.items()}
         pp = F.prepare(f["q"], f["k"], f["v"], w.smooth_q, w.smooth_k)
         o, lse = F.fwd_head(pp, w.causal)
-        o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o[:n].astype(np.float32)))
-        bp = F.prepare_bwd(pp, f["v"], o_b, lse[:n].astype(np.float32), f["do"])
-        F.bwd_head(bp, w.causal)
+        if mode != "fp4":
+            o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o[:n].astype(np.float32)))
+            bp = F.prepare_bwd(pp, f["v"], o_b, lse[:n].astype(np.float32), f["do"])
+            F.bwd_head(bp, w.causal)
         done_heads += 1
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    ops = done_heads * 14.0 * n * n * 64 * (0.5 if w.causal else 1.0)
+    ops = done_heads * (4.0 if mode == "fp4" else 14.0) * n * n * 64 * (0.5 if w.causal else 1.0)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"{'mxfp8' if mxfp8 else 'faithful'} fwd+bwd of {done_heads} whole head(s) of the first {n} tokens of {w.name} "
+            "sample": f"{'faithful' if mode == 'int8' else mode} {'fwd' if mode == 'fp4' else 'fwd+bwd'} of {done_heads} whole head(s) of the first {n} tokens of {w.name} "
                       f"(causal={w.causal}) in {el:.1f} s; {os.cpu_count()} host cores visible, "
                       f"BLAS threads {threads}"}
 
@@ -113,6 +116,8 @@ def main():
     ap.add_argument("--qk-norm", action="store_true", help="fuse QK-norm into the path (normalizes the inputs' rows)")
     ap.add_argument("--mxfp8", action="store_true",
                     help="time the MXFP8 mode (E4M3 codes, E8M0 exponents per 32x32 block) instead of INT8")
+    ap.add_argument("--fp4", action="store_true",
+                    help="time the FP4 inference forward (MXFP4: E2M1 codes, E8M0 exponents per 32 values) alone")
     ap.add_argument("--no-reuse", action="store_true",
                     help="let the backward re-quantize Q and K instead of reading the forward's workspace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -140,11 +145,12 @@ def main():
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     del x
     p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, int8_dp=args.int8_dp, qk_norm=args.qk_norm,
-                       mxfp8=args.mxfp8)
+                       mxfp8=args.mxfp8, fp4=args.fp4)
     lib = sb.load_library()
     import ctypes
     ws_f = torch.empty(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(0 if args.fp4 else lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8,
+                       device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -156,6 +162,8 @@ def main():
     tiles = T * (T + 1) // 2 if w.causal else T * T
     one_group = sb.ws_region(p, "DS")[1] == w.bh * tiles * 4096
     stages = ["FWD_PREPARE", "FWD_ATTN", "BWD_PREPARE"] + (["BWD_DKDV", "BWD_DQ"] if one_group else ["BWD_ATTN"])
+    if args.fp4:
+        stages = ["FWD_PREPARE", "FWD_ATTN"]                 # an inference forward: no backward
 
     def step(events=None):
         for i, s in enumerate(stages):
@@ -190,17 +198,19 @@ def main():
 
     causal_f = 0.5 if w.causal else 1.0
     unit = 2.0 * w.N * w.N * w.d * w.bh * causal_f          # one 2*N^2*d matmul over all heads
-    ops_step = 7 * unit                                      # 4 + 10 = 14 N^2 d
+    ops_step = (2 if args.fp4 else 7) * unit                 # fwd+bwd: 4 + 10 = 14 N^2 d; fwd alone 4 N^2 d
     tops = ops_step / (ms_step * 1e-3) / 1e12
 
+    mode_suffix = "_mxfp8" if args.mxfp8 else "_fp4" if args.fp4 else ""
     dom = max((s for s in KERNEL_UNITS if s in stage_ms), key=lambda s: stage_ms[s])
     ach = KERNEL_UNITS[dom] * unit / (stage_ms[dom] * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(ach / INT8_PEAK_TOPS, 4),
-            "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name + ("_mxfp8" if args.mxfp8 else "")),
+    peak = FP4_PEAK_TOPS if args.fp4 else INT8_PEAK_TOPS
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4),
+            "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name + mode_suffix),
             "avg_launch_ms": round(stage_ms[dom], 4)}
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FP4 if args.fp4 else METRIC,
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -210,21 +220,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if args.int8_dp else "e4m3 (dO.V^T f16)" if args.mxfp8 else "i8 (dO.V^T f16)",
+        "dtype": "i8" if args.int8_dp else "e4m3 (dO.V^T f16)" if args.mxfp8 else "e2m1" if args.fp4 else "i8 (dO.V^T f16)",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "smooth_q": w.smooth_q, "smooth_k": w.smooth_k, "ops_per_step": ops_step,
                    "bwd_reuses_fwd_quantization": not args.no_reuse, "int8_dp": bool(args.int8_dp),
-                   "qk_norm": bool(args.qk_norm), "mxfp8": bool(args.mxfp8)},
+                   "qk_norm": bool(args.qk_norm), "mxfp8": bool(args.mxfp8), "fp4": bool(args.fp4)},
         "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4),
         # 12 of the 14 N^2 d units are INT8 and 2 (dO V^T, fwd-side none) FP16 at half the INT8 rate,
-        # so the MFMA floor of the mix is 14/16 of the INT8 peak
-        "frac_blended_mfma_peak": round(tops / (INT8_PEAK_TOPS * 14.0 / 16.0), 4),
+        # so the MFMA floor of the mix is 14/16 of the INT8 peak (FP4 forward: the FP4 peak)
+        "frac_blended_mfma_peak": round(tops / (FP4_PEAK_TOPS if args.fp4 else INT8_PEAK_TOPS * 14.0 / 16.0), 4),
         "stage_ms": {s: round(t, 4) for s, t in stage_ms.items()},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.mxfp8)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, "fp4" if args.fp4 else "mxfp8" if args.mxfp8 else "int8")
     print(json.dumps(out), flush=True)
 
 

@@ -41,7 +41,8 @@ class SageBwdError(RuntimeError):
 class Params(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("smooth_q", ctypes.c_int32), ("smooth_k", ctypes.c_int32),
-                ("int8_dp", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("mxfp8", ctypes.c_int32)]
+                ("int8_dp", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("mxfp8", ctypes.c_int32),
+                ("fp4", ctypes.c_int32)]
 
 
 _lib = None
@@ -83,12 +84,14 @@ def load_library() -> ctypes.CDLL:
     return _lib
 
 
-def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False, qk_norm=False, mxfp8=False) -> Params:
+def make_params(B, H, N, causal, smooth_q, smooth_k, D=64, int8_dp=False, qk_norm=False, mxfp8=False,
+                fp4=False) -> Params:
     """int8_dp: the all-INT8 ablation (dO V^T from INT8 codes); backward only.
     qk_norm: QK-norm fused in; mxfp8: E4M3 codes with E8M0 32x32 block scales
-    instead of INT8 (both: same value for forward and backward)."""
+    instead of INT8 (both: same value for forward and backward); fp4: the
+    MXFP4 inference forward (forward only)."""
     return Params(int(B), int(H), int(N), int(D), int(bool(causal)), int(bool(smooth_q)), int(bool(smooth_k)),
-                  int(bool(int8_dp)), int(bool(qk_norm)), int(bool(mxfp8)))
+                  int(bool(int8_dp)), int(bool(qk_norm)), int(bool(mxfp8)), int(bool(fp4)))
 
 
 def _check(rc: int, what: str):
@@ -115,8 +118,8 @@ def _check_qkv(*ts):
 
 
 def workspace_size(B, H, N, causal=False, smooth_q=False, smooth_k=True, backward=False, int8_dp=False,
-                   qk_norm=False, mxfp8=False) -> int:
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp, qk_norm=qk_norm, mxfp8=mxfp8)
+                   qk_norm=False, mxfp8=False, fp4=False) -> int:
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, int8_dp=int8_dp, qk_norm=qk_norm, mxfp8=mxfp8, fp4=fp4)
     lib = load_library()
     n = (lib.sagebwd_bwd_workspace_size if backward else lib.sagebwd_fwd_workspace_size)(ctypes.byref(p))
     if n == 0:
@@ -133,13 +136,13 @@ def _workspace(nbytes, device, ws=None):
 
 
 def fwd(q, k, v, causal=False, smooth_q=False, smooth_k=True, workspace=None, out=None, qk_norm=False,
-        mxfp8=False):
+        mxfp8=False, fp4=False):
     """Forward.  Returns (O bf16 [B,H,N,64], LSE fp32 [B,H,N]).  Pass a
     forward-sized uint8 ``workspace`` to keep the quantized Q and K for a
     backward that reuses them (``bwd(..., fwd_workspace=workspace)``)."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, qk_norm=qk_norm, mxfp8=mxfp8)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, qk_norm=qk_norm, mxfp8=mxfp8, fp4=fp4)
     lib = load_library()
     ws = _workspace(lib.sagebwd_fwd_workspace_size(ctypes.byref(p)), q.device, workspace)
     if out is None:
@@ -199,12 +202,12 @@ def bwd_stage(stage, q, k, v, o, lse, do, dq, dk, dv, ws, params: Params, fwd_ws
 
 
 def prepare(q, k, v, o=None, lse=None, do=None, causal=False, smooth_q=False, smooth_k=True, int8_dp=False,
-            qk_norm=False, mxfp8=False):
+            qk_norm=False, mxfp8=False, fp4=False):
     """Run only the preparation kernels into a fresh backward-sized workspace
     (uint8 tensor) for inspection; see ws_region for the layout."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8, fp4)
     lib = load_library()
     nbytes = lib.sagebwd_bwd_workspace_size(ctypes.byref(p))
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)

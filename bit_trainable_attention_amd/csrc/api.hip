@@ -105,10 +105,11 @@ int check_params(const sagebwd_params* p) {
     if (p->B < 1 || p->H < 1 || p->N < 1) return SAGEBWD_ERR_INVALID_ARG;
     if ((p->causal != 0 && p->causal != 1) || (p->smooth_q != 0 && p->smooth_q != 1) ||
         (p->smooth_k != 0 && p->smooth_k != 1) || (p->int8_dp != 0 && p->int8_dp != 1) ||
-        (p->qk_norm != 0 && p->qk_norm != 1) || (p->mxfp8 != 0 && p->mxfp8 != 1))
+        (p->qk_norm != 0 && p->qk_norm != 1) || (p->mxfp8 != 0 && p->mxfp8 != 1) || (p->fp4 != 0 && p->fp4 != 1))
         return SAGEBWD_ERR_INVALID_ARG;
     if (p->D != HD) return SAGEBWD_ERR_UNSUPPORTED;
     if (p->mxfp8 && p->int8_dp) return SAGEBWD_ERR_UNSUPPORTED;   // the INT8 ablation has no MXFP8 form
+    if (p->fp4 && (p->mxfp8 || p->int8_dp)) return SAGEBWD_ERR_UNSUPPORTED;
     if (p->N > MAX_N || (int64_t)p->B * p->H > MAX_BH) return SAGEBWD_ERR_UNSUPPORTED;
     return SAGEBWD_OK;
 }
@@ -131,6 +132,8 @@ T* region(void* ws, const Layout& L, int r) {
 }
 
 int hip_status() { return hipGetLastError() == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP; }
+
+int operand_format(const sagebwd_params& p) { return p.fp4 ? FMT_FP4 : p.mxfp8 ? FMT_MXFP8 : FMT_INT8; }
 
 // Means + quantization of Q, K, V into the regions of this layout.
 void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, const void* K, const void* V,
@@ -177,7 +180,7 @@ void run_prepare_qkv(const sagebwd_params& p, const Layout& L, const void* Q, co
     a.smooth_q = p.smooth_q;
     a.smooth_k = p.smooth_k;
     // V's block scales are only needed by the forward and the inspection call
-    launch_quantize(a, BH, want_vt ? 3 : 2, p.mxfp8 != 0, st);
+    launch_quantize(a, BH, want_vt ? 3 : 2, operand_format(p), st);
 }
 
 // Where the backward reads the quantized Q and K (means, codes in both
@@ -356,11 +359,11 @@ int sagebwd_fwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
     if (stage == SAGEBWD_STAGE_FWD_PREPARE) {
-        run_prepare_qkv(*p, L, Q, K, V, ws, true, true, true, st);
+        run_prepare_qkv(*p, L, Q, K, V, ws, true, true, !p->fp4, st);
         return hip_status();
     }
     const FwdArgs a = fwd_args(*p, L, ws, O, LSE);
-    launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, p->mxfp8, st);
+    launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, operand_format(*p), st);
     return hip_status();
 }
 
@@ -379,6 +382,7 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
     if (stage != SAGEBWD_STAGE_BWD_PREPARE && stage != SAGEBWD_STAGE_BWD_DKDV && stage != SAGEBWD_STAGE_BWD_DQ &&
         stage != SAGEBWD_STAGE_BWD_ATTN)
         return SAGEBWD_ERR_INVALID_ARG;
+    if (p->fp4) return SAGEBWD_ERR_UNSUPPORTED;   // the FP4 mode is an inference forward
     for (const void* t : {Q, K, V, O, dO, (const void*)dQ, (const void*)dK, (const void*)dV}) {
         if ((rc = check_tensor(t))) return rc;
     }
@@ -440,7 +444,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         kblock >= T || (p->causal && kblock > qblock))
         return SAGEBWD_ERR_INVALID_ARG;
     if (!dump || dump_bytes < (size_t)dumpoff::BYTES) return SAGEBWD_ERR_INVALID_ARG;
-    if (p->mxfp8) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 kernels only
+    if (p->mxfp8 || p->fp4) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 kernels only
     if (kernel == 0) {
         if ((rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream))) return rc;
         const Layout L = make_layout(*p, PASS_FWD);
@@ -449,7 +453,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         a.dump_bh = bh;
         a.dump_i = qblock;
         a.dump_t = kblock;
-        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, false, (hipStream_t)stream, true);
+        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, FMT_INT8, (hipStream_t)stream, true);
         return hip_status();
     }
     if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, nullptr, 0, ws,
@@ -475,6 +479,7 @@ int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const
         if ((rc = check_tensor(t))) return rc;
     }
     const bool with_bwd = dO != nullptr;
+    if (with_bwd && p->fp4) return SAGEBWD_ERR_UNSUPPORTED;
     if (with_bwd) {
         if ((rc = check_tensor(O)) || (rc = check_tensor(dO))) return rc;
         if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
@@ -484,7 +489,7 @@ int sagebwd_prepare(const sagebwd_params* p, const void* Q, const void* K, const
     const Layout L = make_layout(*p, PASS_BWD);
     if ((rc = check_ws(L, ws, ws_bytes))) return rc;
     hipStream_t st = (hipStream_t)stream;
-    run_prepare_qkv(*p, L, Q, K, V, ws, true, true, true, st);
+    run_prepare_qkv(*p, L, Q, K, V, ws, true, true, !p->fp4, st);
     if (with_bwd) run_bwd_pre(*p, L, QkSource{ws, L}, V, O, LSE, dO, ws, st);
     return hip_status();
 }

@@ -48,8 +48,8 @@ struct BwdArgs {
     int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
 };
 
-// mx: MXFP8 codes and block exponents (no tile dump)
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, bool mx, hipStream_t st, bool dump = false);
+// fmt: FMT_INT8, FMT_MXFP8 or FMT_FP4 (the tile dump exists for INT8 only)
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hipStream_t st, bool dump = false);
 // int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16;
 // mx: MXFP8 codes and block exponents (neither int8_dp nor a tile dump)
 int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, bool mx, hipStream_t st,

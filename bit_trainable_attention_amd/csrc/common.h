@@ -35,6 +35,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int BLK = 64;                    // tokens per block, tile side
+constexpr int FMT_INT8 = 0, FMT_MXFP8 = 1, FMT_FP4 = 2;   // operand formats of a pass
 constexpr int HD = 64;                     // head dimension
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -92,6 +93,27 @@ __device__ __forceinline__ int mx_exponent(float a) {
     const uint32_t u = __float_as_uint(a);
     const int e = (int)((u >> 23) & 0xFFu) - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
     return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+// FP4 (E2M1, one E8M0 scale per 32 values): the least e with 6 2^e >= a,
+// clamped to [-126, 127].  a = m 2^E with m in [1, 2): e = E - 2, plus 1
+// when m > 1.5 (6 = 1.5 2^2); zero and subnormal a clamp to -126.
+__device__ __forceinline__ int fp4_exponent(float a) {
+    const uint32_t u = __float_as_uint(a);
+    const int e = (int)((u >> 23) & 0xFFu) - 129 + ((u & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+    return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+// Two E2M1 codes rne(x / scale), rne(y / scale) (scale a power of two) into
+// byte SEL of old (x in the low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float x, float y, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x, y, scale, SEL);
+}
+// Eight E2M1 codes of x[0..7] / scale in one dword (value i in nibble i).
+__device__ __forceinline__ uint32_t fp4_oct(const float* x, float scale) {
+    uint32_t w = fp4_pair<0>(0u, x[0], x[1], scale);
+    w = fp4_pair<1>(w, x[2], x[3], scale);
+    w = fp4_pair<2>(w, x[4], x[5], scale);
+    return fp4_pair<3>(w, x[6], x[7], scale);
 }
 // 2^e as a float32 (e in [-126, 127]).
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
@@ -153,15 +175,25 @@ __device__ __forceinline__ int opaque(int v) {
 }
 constexpr int E8M0_ONE = 127;              // biased exponent of 2^0
 constexpr int E4M3_ONE = 0x38;             // E4M3 code of 1.0
+// E2M1 x E2M1 on the scaled MFMA: each half of the wave holds the 32 values
+// of its own 32-k block (16 bytes, value i in nibble i), sa/sb as mfma_fp8.
+__device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
+    const v8i a8 = cat8(a, v4i{}), b8 = cat8(b, v4i{});
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, sa, 0, sb);
+}
+constexpr uint32_t E2M1_ONES = 0x22222222u;   // eight E2M1 codes of 1.0
+constexpr int FP4_EXP_OFF = 2048;             // exponent bytes after the codes of an FP4 block
+
 
 // max(a, b, c) and max(a, |b|, |c|) as one v_max3_f32.  fmaxf in IEEE mode
 // makes the compiler quiet every operand it cannot prove canonical (one extra
 // v_max_f32 per value); the operands here are arithmetic results, never
 // signaling NaNs, so the raw instruction gives the same maximum.
 // The compiler does not look inside inline assembly when it inserts the wait
-// states between an MFMA and a VALU read of its result, so operands must
-// never come straight from an MFMA accumulator (pass them through an
-// ordinary VALU operation first).
+// states a result needs before a VALU instruction may read it, so operands
+// must never come straight from an MFMA accumulator or from a transcendental
+// instruction (v_exp_f32 and the like): pass them through an ordinary VALU
+// operation first, or reduce with compiler-visible instructions.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     float d;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));

@@ -431,9 +431,201 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     }
 }
 
-int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, bool mx, hipStream_t st, bool dump) {
+// ---------------------------------------------------------------- FP4
+// Inference forward on E2M1 codes with one E8M0 exponent per 32 values of the
+// contraction index (FP4 blocks of 2048 code bytes + 128 exponent bytes, the
+// layouts of the FP4 quantizer), the same work split and online softmax as
+// the MXFP8 forward.  A half-wave of the score product holds, for its query,
+// the 32 keys of one key class of the tile, which is exactly one FP4 block of
+// P~ (and the matching V block): the block maximum and exponent are in-lane.
+
+struct FwdFp4Smem {
+    v4i k[2][136];       // K FP4 block: 128 code chunks + 8 chunks of exponents
+    v4i v[2][136];       // V FP4 block (class layout)
+    float bias[2][64];
+};
+
+template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+__device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i qop, int sq_e, int t, int q, int N,
+                                             int lane, int h, int l32, float& M, v16f (&O)[2], v16f& Lacc,
+                                             int e_one) {
+    const uint8_t* kx = (const uint8_t*)sm.k[buf] + FP4_EXP_OFF;
+    const uint8_t* vx = (const uint8_t*)sm.v[buf] + FP4_EXP_OFF;
+    v16f s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        s[kb] = mfma_fp4(sm.k[buf][kb * 64 + lane], qop, v16f{}, kx[2 * (32 * kb + l32) + h], sq_e);
+    float z[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        float bias[16];
+        if (SMOOTHQ) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                bias[4 * r4 + 0] = b4.x;
+                bias[4 * r4 + 1] = b4.y;
+                bias[4 * r4 + 2] = b4.z;
+                bias[4 * r4 + 3] = b4.w;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // log2-domain scores (an ordinary VALU operation on the MFMA
+            // result before the inline-assembly maximum)
+            z[kb][r] = SMOOTHQ ? __builtin_fmaf(s[kb][r], SCORE_SCALE_LOG2, bias[r]) : s[kb][r] * SCORE_SCALE_LOG2;
+            if (MASK) {
+                const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+                if (key >= N || (CAUSAL && key > q)) z[kb][r] = -__builtin_inff();
+            }
+        }
+    }
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        m0 = max3f(m0, z[0][r], z[0][r + 1]);
+        m1 = max3f(m1, z[1][r], z[1][r + 1]);
+    }
+    float mx = max3f(m0, m1, m1);
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mt = mx;
+    const bool rise = mt > M;
+    if (__builtin_amdgcn_ballot_w64(rise)) {
+        const float alpha = !rise ? 1.0f : M > -__builtin_inff() ? __builtin_amdgcn_exp2f(M - mt) : 0.0f;
+        M = rise ? mt : M;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+        Lacc[0] *= alpha;   // only register 0 of the row-sum accumulator is read
+    }
+    const float off = -M;
+    float p[32];   // value 16 kb + r of this lane's P~ block
+    uint32_t pm = 0;   // P~ >= 0: its maximum is the maximum of the bit patterns
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float zz = z[kb][r];
+            float v = __builtin_amdgcn_exp2f(zz + off);
+            if (MASK && !(zz > -__builtin_inff())) v = 0.0f;
+            p[16 * kb + r] = v;
+        }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) pm = max(pm, __float_as_uint(p[i]));
+    const int pe = fp4_exponent(__uint_as_float(pm));
+    const float psc = pow2f(pe);
+    const v4i pc = v4i{(int)fp4_oct(p, psc), (int)fp4_oct(p + 8, psc), (int)fp4_oct(p + 16, psc),
+                       (int)fp4_oct(p + 24, psc)};
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+        O[db] = mfma_fp4(sm.v[buf][db * 64 + lane], pc, O[db], vx[2 * (32 * db + l32) + h], pe + 127);
+    const v4i ones = v4i{(int)E2M1_ONES, (int)E2M1_ONES, (int)E2M1_ONES, (int)E2M1_ONES};
+    Lacc = mfma_fp4(ones, pc, Lacc, e_one, pe + 127);
+}
+
+template <bool CAUSAL, bool SMOOTHQ>
+__global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
+    __shared__ FwdFp4Smem sm;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    int bh, g;
+    map_group(a.ngroups, a.BH, bh, g);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
+    const bool live = qblk < T;
+    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;
+    const int t_last = CAUSAL ? qblk : T - 1;
+    const bool ragged = (a.N & (BLK - 1)) != 0;
+    const size_t bt = (size_t)bh * T;
+    const size_t np = (size_t)T * BLK;
+    const v4i* kg = (const v4i*)(a.k_r + bt * 4096);   // 256 chunks per 4096-byte slot, 136 used
+    const v4i* vg = (const v4i*)(a.v_t + bt * 4096);
+    const float* bg = a.bias + bh * np;
+
+    v4i qop = v4i{};
+    int sq_e = E8M0_ONE;
+    if (live) {
+        const uint8_t* qb = (const uint8_t*)a.q_r + (bt + qblk) * 4096;
+        qop = ((const v4i*)qb)[qhalf * 64 + lane];
+        sq_e = qb[FP4_EXP_OFF + 2 * (32 * qhalf + l32) + h];
+    }
+    const int e_one = opaque(E8M0_ONE);
+    const int q = qblk * BLK + 32 * qhalf + l32;
+    const bool loader = tid < 136;
+
+    v4i pk = loader ? kg[tid] : v4i{}, pv = loader ? vg[tid] : v4i{};
+    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
+    if (loader) {
+        sm.k[0][tid] = pk;
+        sm.v[0][tid] = pv;
+    }
+    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
+    __syncthreads();
+
+    float M = -__builtin_inff();
+    v16f O[2] = {v16f{}, v16f{}};
+    v16f Lacc = v16f{};
+
+    for (int t = 0; t <= t_last_wg; ++t) {
+        const int buf = t & 1;
+        const bool more = t < t_last_wg;
+        if (more && loader) {
+            pk = kg[(size_t)(t + 1) * 256 + tid];
+            pv = vg[(size_t)(t + 1) * 256 + tid];
+        }
+        if (more && SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
+        if (live && t <= t_last) {
+            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+                fwd_tile_fp4<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
+            else
+                fwd_tile_fp4<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
+        }
+        if (more) {
+            if (loader) {
+                sm.k[buf ^ 1][tid] = pk;
+                sm.v[buf ^ 1][tid] = pv;
+            }
+            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
+        }
+        __syncthreads();
+    }
+
+    if (live && q < a.N) {
+        const float Lt = Lacc[0];
+        const float inv_l = 1.0f / Lt;
+        uint16_t* orow = a.o + ((size_t)bh * a.N + q) * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d = 32 * db + 8 * r4 + 4 * h;
+                const uint32_t w0 = f32_to_bf16_rne(O[db][4 * r4 + 0] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 1] * inv_l) << 16);
+                const uint32_t w1 = f32_to_bf16_rne(O[db][4 * r4 + 2] * inv_l) |
+                                    (f32_to_bf16_rne(O[db][4 * r4 + 3] * inv_l) << 16);
+                *(uint2*)(orow + d) = make_uint2(w0, w1);
+            }
+        if (h == 0) a.lse[(size_t)bh * a.N + q] = (M + log2f(Lt)) * LN2 + a.corr[bh * np + q];
+    }
+}
+
+int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * FWD_WAVES);
-    if (mx) {
+    if (fmt == FMT_FP4) {
+        if (causal) {
+            if (smooth_q) hipLaunchKernelGGL((k_fwd_fp4<true, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd_fp4<true, false>), grid, block, 0, st, a);
+        } else {
+            if (smooth_q) hipLaunchKernelGGL((k_fwd_fp4<false, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_fwd_fp4<false, false>), grid, block, 0, st, a);
+        }
+        return 0;
+    }
+    if (fmt == FMT_MXFP8) {
         if (causal) {
             if (smooth_q) hipLaunchKernelGGL((k_fwd_mx<true, true>), grid, block, 0, st, a);
             else hipLaunchKernelGGL((k_fwd_mx<true, false>), grid, block, 0, st, a);

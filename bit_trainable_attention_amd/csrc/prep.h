@@ -43,7 +43,9 @@ struct BwdPreArgs {
 
 int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, int N, int T, int BH, hipStream_t st);
 int launch_means(const MeansArgs& m, hipStream_t st);
-int launch_quantize(const QuantArgs& a, int BH, int ntensors, bool mx, hipStream_t st);
+// fmt: FMT_INT8, FMT_MXFP8 or FMT_FP4 (Q, K row FP4 blocks and V class FP4
+// blocks in q_r, k_r, v_t; q_t, k_t unused)
+int launch_quantize(const QuantArgs& a, int BH, int ntensors, int fmt, hipStream_t st);
 int launch_bwd_pre(const BwdPreArgs& a, int BH, bool mx, hipStream_t st);
 
 }  // namespace sagebwd

@@ -261,6 +261,108 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- FP4
+// E2M1 codes with one E8M0 exponent per 32 values of the contraction index,
+// in blocks of 2048 code bytes + 128 exponent bytes (in the 4096-byte slots of
+// the code regions).  Q and K (row FP4 layout): 16-byte chunk th*64 + 32h + m
+// holds the 32 channels 32h.. of token 32th + m, value i in nibble i; the
+// exponent of (token r, channel half h) is byte 2048 + 2r + h.  V (class
+// layout): chunk db*64 + 32h + m holds channel c = 32db + m at the 32 keys of
+// key class h = (key % 8) / 4, value 16kb + j at key 32kb + 8(j/4) + 4h + j%4
+// (the keys one half-wave holds in the accumulator layout of the scores);
+// the exponent of (channel c, class h) is byte 2048 + 2c + h.  One workgroup
+// per 64-token block of one tensor (tensor 0 = Q, 1 = K, 2 = V).
+__global__ __launch_bounds__(256) void k_quantize_fp4(QuantArgs a) {
+    const int t = blockIdx.x, bh = blockIdx.y, tensor = blockIdx.z;
+    const int r = threadIdx.x / 4, g = threadIdx.x % 4;
+    const int tok = t * BLK + r;
+    const bool valid = tok < a.N;
+    const uint16_t* src = (tensor == 0 ? a.q : tensor == 1 ? a.k : a.v) + ((size_t)bh * a.N + tok) * HD + 16 * g;
+    const float* mu = tensor == 0 ? a.mu_q : tensor == 1 ? a.mu_k : nullptr;
+    float raw[16], x[16];
+    uint4 u0 = make_uint4(0, 0, 0, 0), u1 = u0;
+    if (valid) {
+        u0 = *(const uint4*)src;
+        u1 = *(const uint4*)(src + 8);
+    }
+    const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const float* rn = tensor == 0 ? a.rq : tensor == 1 ? a.rk : nullptr;
+    if (rn) {
+        const float rr = valid ? rn[(size_t)bh * a.T * BLK + tok] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            raw[2 * j] = qk_normed(w[j] & 0xFFFFu, rr);
+            raw[2 * j + 1] = qk_normed(w[j] >> 16, rr);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            raw[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+            raw[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        x[j] = mu ? raw[j] - mu[(size_t)bh * HD + 16 * g + j] : raw[j];
+        if (!valid) x[j] = 0.0f;
+        amax = fmaxf(amax, fabsf(x[j]));
+    }
+    const size_t blk = (size_t)bh * a.T + t;
+    if (tensor < 2) {
+        // block (token r, channel half g / 2): this thread and its neighbour
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const int e = fp4_exponent(amax);
+        const float sc = pow2f(e);
+        uint8_t* dst = (uint8_t*)(tensor == 0 ? a.q_r : a.k_r) + blk * 4096;
+        const uint32_t c0 = fp4_oct(x, sc), c1 = fp4_oct(x + 8, sc);
+        const int h = g / 2;
+        *(uint2*)(dst + ((r / 32) * 64 + 32 * h + r % 32) * 16 + 8 * (g % 2)) = make_uint2(c0, c1);
+        if (g % 2 == 0) dst[FP4_EXP_OFF + 2 * r + h] = (uint8_t)(e + 127);
+        if (tensor == 0) {
+            float cd = 0.0f;
+            if (a.smooth_k) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], a.mu_k[(size_t)bh * HD + 16 * g + j], cd);
+            }
+            cd += __shfl_xor(cd, 1, 64);
+            cd += __shfl_xor(cd, 2, 64);
+            if (g == 0) a.corr[(size_t)bh * a.T * BLK + tok] = valid ? cd * 0.125f : 0.0f;
+        } else {
+            // Q-smoothing bias from the centred float K (not its 4-bit codes)
+            float mu_dot = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], x[j], mu_dot);
+            mu_dot += __shfl_xor(mu_dot, 1, 64);
+            mu_dot += __shfl_xor(mu_dot, 2, 64);
+            if (g == 0) a.bias[(size_t)bh * a.T * BLK + tok] = (valid && a.smooth_q) ? mu_dot * SCORE_SCALE_LOG2 : 0.0f;
+        }
+        return;
+    }
+    // V: stage the block, then thread (c, h, kb) codes 16 keys of channel c
+    __shared__ float vs[BLK][HD + 1];
+    __shared__ float red[2][2][HD];   // [kb][h][c] partial maxima
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vs[r][16 * g + j] = x[j];
+    __syncthreads();
+    const int c = threadIdx.x % HD, h = (threadIdx.x / HD) % 2, kb = threadIdx.x / 128;
+    float y[16];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        y[j] = vs[32 * kb + 8 * (j / 4) + 4 * h + j % 4][c];
+        m = fmaxf(m, fabsf(y[j]));
+    }
+    red[kb][h][c] = m;
+    __syncthreads();
+    const int e = fp4_exponent(fmaxf(red[0][h][c], red[1][h][c]));
+    const float sc = pow2f(e);
+    uint8_t* dst = (uint8_t*)a.v_t + blk * 4096;
+    const uint32_t c0 = fp4_oct(y, sc), c1 = fp4_oct(y + 8, sc);
+    *(uint2*)(dst + ((c / 32) * 64 + 32 * h + c % 32) * 16 + 8 * kb) = make_uint2(c0, c1);
+    if (kb == 0) dst[FP4_EXP_OFF + 2 * c + h] = (uint8_t)(e + 127);
+}
+
 // ---------------------------------------------------------------- backward prep
 // One workgroup per 64-token block: -Delta = -rowsum(dO*O) (fp32), the
 // log2-domain LSE of the smoothed scores, dO codes (transposed operand
@@ -386,8 +488,9 @@ int launch_rownorm(const uint16_t* q, const uint16_t* k, float* rq, float* rk, i
     return 0;
 }
 
-int launch_quantize(const QuantArgs& a, int BH, int ntensors, bool mx, hipStream_t st) {
-    if (mx) hipLaunchKernelGGL(k_quantize<true>, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
+int launch_quantize(const QuantArgs& a, int BH, int ntensors, int fmt, hipStream_t st) {
+    if (fmt == FMT_FP4) hipLaunchKernelGGL(k_quantize_fp4, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
+    else if (fmt == FMT_MXFP8) hipLaunchKernelGGL(k_quantize<true>, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(k_quantize<false>, dim3(a.T, BH, ntensors), dim3(256), 0, st, a);
     return 0;
 }

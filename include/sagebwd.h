@@ -86,12 +86,27 @@ typedef struct sagebwd_params {
                            mode.  Not with int8_dp (SAGEBWD_ERR_UNSUPPORTED)
                            nor with sagebwd_debug_tile.  Forward and backward
                            must be called with the same value. */
+    int32_t fp4;        /* 0 or 1: forward only (inference).  The FP4 attention of
+                           the SageAttention3 summary ("Approach": FP4
+                           microscaling on both matmuls) in MI355X's MXFP4
+                           form: E2M1 codes with one power-of-two (E8M0) scale
+                           per 32 values of the contraction index, 2^e with e
+                           the least integer such that 6 2^e >= the block's
+                           absmax, clamped to [-126, 127]; Q and K per token
+                           and 32 consecutive channels; V and P~ per channel
+                           (per query) and the 32 keys of one key class
+                           (key % 8) / 4 of a 64-key tile; P~ = exp(S - running
+                           row max); the Q-smoothing bias from the float
+                           centred K.  Not with mxfp8 or int8_dp; the
+                           backward entry points, sagebwd_debug_tile and
+                           sagebwd_prepare with dO return
+                           SAGEBWD_ERR_UNSUPPORTED. */
 } sagebwd_params;
 
 #define SAGEBWD_OK               0
 #define SAGEBWD_ERR_INVALID_ARG (-1)   /* null pointer, size < 1, flag not 0/1, misaligned */
-#define SAGEBWD_ERR_UNSUPPORTED (-2)   /* D != 64, N or B*H beyond the supported range, mxfp8 with
-                                          int8_dp, or an entry point without an mxfp8 form */
+#define SAGEBWD_ERR_UNSUPPORTED (-2)   /* D != 64, N or B*H beyond the supported range, a mode
+                                          combination or an entry point the modes do not have */
 #define SAGEBWD_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the required size */
 #define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
 
@@ -210,7 +225,16 @@ const char* sagebwd_status_string(int status);
  * code bytes in the same layouts, and each 4-byte block scale (regions 8-11)
  * holds the four biased exponents e + 127 of the block's 32x32 sub-blocks,
  * byte 2*(r/32) + c/32 (token half, channel half); a DS_SCALE entry holds
- * those of its dS tile, byte 2*(key half) + query half.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
+ * those of its dS tile, byte 2*(key half) + query half.  With fp4 the
+ * regions Q_R, K_R and V_T hold FP4 blocks in their 4096-byte slots: 2048
+ * bytes of E2M1 codes (two per byte, the first in the low nibble), then 128
+ * exponent bytes e + 127.  Q_R, K_R: 16-byte chunk th*64 + 32h + m holds the
+ * channels 32h..32h+31 of token 32th + m; the exponent of (token r, channel
+ * half h) is byte 2048 + 2r + h.  V_T: chunk db*64 + 32h + m holds channel
+ * 32db + m at the keys of class h, value 16kb + j at key
+ * 32kb + 8(j/4) + 4h + j%4; the exponent of (channel c, class h) is byte
+ * 2048 + 2c + h.  Regions 5-11 are unused; BIAS holds mu_Q . K~_j times
+ * log2(e)/8 with K~ the centred float K.  Regions a pass does not use have size 0.  Within a 4096-byte block of 64 tokens x
  * 64 channels, element (token r, channel c) sits at byte
  *   row operand:         ((r/32*2 + c/32)*64 + 32*((c%32)/16) + r%32)*16 + c%16
  *   transposed operand:  ((c/32*2 + r/32)*64 + 32*((r%8)/4) + c%32)*16

@@ -37,10 +37,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def P(**kw):
-    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0, qk_norm=0, mxfp8=0)
+    d = dict(B=1, H=2, N=128, causal=0, smooth_q=0, smooth_k=1, D=64, int8_dp=0, qk_norm=0, mxfp8=0, fp4=0)
     d.update(kw)
     return sb.Params(d["B"], d["H"], d["N"], d["D"], d["causal"], d["smooth_q"], d["smooth_k"], d["int8_dp"],
-                     d["qk_norm"], d["mxfp8"])
+                     d["qk_norm"], d["mxfp8"], d["fp4"])
 
 
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation first
@@ -71,7 +71,18 @@ def test_param_validation(lib):
     assert call_bwd(lib, P(mxfp8=1, int8_dp=1)) == UNSUPPORTED     # the INT8 ablation has no MXFP8 form
     assert lib.sagebwd_bwd_workspace_size(ctypes.byref(P(mxfp8=1, int8_dp=1))) == 0
     assert lib.sagebwd_bwd_workspace_size(ctypes.byref(P(mxfp8=1))) == lib.sagebwd_bwd_workspace_size(ctypes.byref(P()))
+    assert call_fwd(lib, P(fp4=2)) == INVALID
+    assert call_fwd(lib, P(fp4=1, mxfp8=1)) == UNSUPPORTED
+    assert call_bwd(lib, P(fp4=1, int8_dp=1)) == UNSUPPORTED
+    assert call_bwd(lib, P(fp4=1)) == UNSUPPORTED                     # the FP4 mode is a forward only
+    for stage in range(2, 6):
+        assert lib.sagebwd_bwd_stage(ctypes.byref(P(fp4=1)), stage, *([FAKE] * 9), None, 0, FAKE, 1 << 40,
+                                     None) == UNSUPPORTED
+    assert lib.sagebwd_prepare(ctypes.byref(P(fp4=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               None) == UNSUPPORTED
     # the tile dump exists for the INT8 kernels only
+    assert lib.sagebwd_debug_tile(ctypes.byref(P(fp4=1)), 0, 0, 0, 0, *([FAKE] * 10), FAKE, 1 << 20, FAKE, 1 << 40,
+                                  None) == UNSUPPORTED
     assert lib.sagebwd_debug_tile(ctypes.byref(P(mxfp8=1)), 0, 0, 0, 0, *([FAKE] * 10), FAKE, 1 << 20, FAKE, 1 << 40,
                                   None) == UNSUPPORTED
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED

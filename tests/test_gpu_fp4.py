@@ -1,0 +1,229 @@
+"""Parity of the FP4 inference forward (E2M1 codes, one E8M0 exponent per 32
+values of the contraction index) with the oracle's FP4 mode.
+
+The preparation is compared bit for bit: every E2M1 code of Q, K (per token
+and 32 channels) and V (per channel and key class), and every block exponent
+(both sides round the same float32 values to nearest-even).  O and LSE are
+compared element by element with the oracle (relative L2 <= 1e-2) on small
+cases spanning several tiles and ragged tails, and on sampled heads of
+full-size workloads in the launch configuration bench.py times."""
+import numpy as np
+import pytest
+import torch
+
+import bit_trainable_attention_amd as sb
+import workloads as W
+from oracle import exact, faithful as F, fp4 as Y, metrics as M
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2            # HIP vs the oracle's FP4 mode, O
+# LSE: a P~ value next to an E2M1 rounding midpoint can round to neighbouring
+# codes on the two sides (float32 against float64 scores); one such flip moves
+# the row sum l (>= 1: the row maximum's value 1 is coded exactly) by one E2M1
+# step of a block whose maximum is at most 1, at most 2 x 2^-2 = l / 2, so
+# |dLSE| <= ln(3/2).  Flips are rare, so the mean error stays at float32 level.
+LSE_MAX = 0.406
+LSE_MEAN = 2e-4
+COS_O = 0.96             # HIP vs exact attention (the oracle's own FP4 error: 0.967-0.995 on these cases)
+
+SMALL = [
+    W.WORKLOADS["tiny"],
+    W.custom(1, 2, 200, True, True, True, "kbias", 251),
+    W.custom(2, 1, 129, False, True, True, "outlier", 252),
+    W.custom(1, 1, 320, False, False, False, "normal", 254),
+    W.custom(1, 1, 1, True, True, True, "normal", 255),
+    W.custom(1, 1, 63, True, True, False, "normal", 256),
+    W.custom(1, 1, 65, True, True, True, "kbias", 258),
+]
+
+
+def _ids(ws):
+    return [f"{w.name}_c{int(w.causal)}q{int(w.smooth_q)}k{int(w.smooth_k)}" for w in ws]
+
+
+def _nibbles(block: np.ndarray) -> np.ndarray:
+    """2048 code bytes -> 4096 E2M1 codes (value 2i + n in nibble n of byte i)."""
+    b = block[:2048]
+    return np.stack([b & 0xF, b >> 4], axis=-1).reshape(-1)
+
+
+def _row_index():
+    """[64 tokens, 64 channels] -> code position in a Q/K FP4 block."""
+    r = np.arange(64)[:, None]
+    c = np.arange(64)[None, :]
+    return (((r // 32) * 64 + 32 * (c // 32) + r % 32) * 32 + c % 32).astype(np.int64)
+
+
+def _v_index():
+    """[64 keys, 64 channels] -> code position in a V FP4 block."""
+    r = np.arange(64)[:, None]
+    c = np.arange(64)[None, :]
+    h = (r % 8) // 4
+    j = 4 * ((r % 32) // 8) + r % 4
+    v = 16 * (r // 32) + j
+    return (((c // 32) * 64 + 32 * h + c % 32) * 32 + v).astype(np.int64)
+
+
+def decode(ws_host, params, name, kind, BH, T):
+    """An FP4 region -> (codes [BH, 64T, 64] as E2M1 values, exponents: Q/K
+    [BH, 64T, 2] (token, channel half), V [BH, T, 2, 64] (tile, class, channel))."""
+    raw = G.region(ws_host, params, name, np.uint8).reshape(BH, T, 4096)
+    idx = _row_index() if kind == "row" else _v_index()
+    vals = np.zeros((BH, T, 64, 64))
+    for i in range(BH):
+        for t in range(T):
+            vals[i, t] = Y.E2M1_VALUES[_nibbles(raw[i, t])[idx]]
+    ex = raw[:, :, 2048:2176].astype(np.int64) - 127
+    if kind == "row":
+        ex = ex.reshape(BH, T * 64, 2)
+    else:
+        ex = ex.reshape(BH, T, 64, 2).transpose(0, 1, 3, 2)
+    return vals.reshape(BH, T * 64, 64), ex
+
+
+def test_layout_indices_are_bijections():
+    for idx in (_row_index(), _v_index()):
+        assert np.array_equal(np.sort(idx.ravel()), np.arange(4096))
+
+
+PREP = [
+    (W.WORKLOADS["tiny"], False),
+    (W.custom(1, 2, 200, True, True, True, "kbias", 241), False),
+    (W.custom(2, 1, 129, False, True, True, "outlier", 242), False),
+    (W.custom(1, 1, 1, True, True, True, "normal", 243), False),
+    (W.custom(1, 2, 65, False, False, False, "normal", 244), False),
+    (W.custom(1, 2, 130, True, True, True, "rowscale", 245), True),
+]
+
+
+@pytest.mark.parametrize("w,qk_norm", PREP, ids=[f"{w.name}_qk{int(q)}" for w, q in PREP])
+def test_fp4_prepare_bit_exact(w, qk_norm):
+    print(f"[fp4 prepare] {w.name} B{w.B} H{w.H} N{w.N} qk_norm={qk_norm}", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv = (G.dev(x[n]) for n in ("q", "k", "v"))
+    ws = sb.prepare(tq, tk, tv, None, None, None, w.causal, w.smooth_q, w.smooth_k, qk_norm=qk_norm, fp4=True)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    p = sb.make_params(w.B, w.H, w.N, w.causal, w.smooth_q, w.smooth_k, qk_norm=qk_norm, fp4=True)
+    BH, T = w.B * w.H, (w.N + 63) // 64
+    Np = 64 * T
+    got = {"q": decode(wsh, p, "Q_R", "row", BH, T), "k": decode(wsh, p, "K_R", "row", BH, T),
+           "v": decode(wsh, p, "V_T", "v", BH, T)}
+    bias = G.region(wsh, p, "BIAS", np.float32).reshape(BH, Np)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    for b in range(w.B):
+        for h in range(w.H):
+            i = b * w.H + h
+            pp = Y.prepare(f32["q"][b, h], f32["k"][b, h], f32["v"][b, h], w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+            for name, deq, e in (("q", pp.qh, pp.eq), ("k", pp.kh, pp.ek)):
+                vals, ex = got[name]
+                assert np.array_equal(ex[i], e), (name, b, h)
+                assert np.array_equal(vals[i], deq * np.ldexp(1.0, -np.repeat(e, 32, axis=1))), (name, b, h)
+            vals, ex = got["v"]
+            assert np.array_equal(ex[i], pp.ev), ("v", b, h)
+            cls = (np.arange(Np) % 8) // 4
+            ev = pp.ev[np.arange(Np) // 64, cls, :]                  # [Np, 64] exponent of each value
+            assert np.array_equal(vals[i], pp.vh * np.ldexp(1.0, -ev)), ("v", b, h)
+            # Q-smoothing bias from the float K: a float32 sum of 64 products
+            want = pp.b * (np.log2(np.e) / 8) if w.smooth_q else np.zeros(Np)
+            fp = F.prepare(f32["q"][b, h], f32["k"][b, h], f32["v"][b, h], w.smooth_q, w.smooth_k, qk_norm=qk_norm)
+            kt = np.zeros((Np, 64))
+            kt[:w.N] = np.asarray(fp.k_in, np.float32) - np.float32(fp.mu_k)
+            tol = 1e-5 * (np.abs(kt) @ np.abs(np.asarray(pp.mu_q, np.float64))) + 1e-30
+            assert np.all(np.abs(bias[i] - want) <= tol), (b, h)
+
+
+def _check_lse(a, b):
+    err = np.abs(a - b)
+    assert np.max(err) <= LSE_MAX and np.mean(err) <= LSE_MEAN, (np.max(err), np.mean(err))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=_ids(SMALL))
+def test_fp4_forward_parity(w):
+    print(f"[fp4 fwd] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    tq, tk, tv = (G.dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, fp4=True)
+    o2, lse2 = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, fp4=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)             # bitwise repeatable
+    o_g, lse_g = G.host_f32(o), lse.cpu().numpy()
+    o_f, lse_f = Y.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k)
+    o_e, lse_e = exact.fwd_bh(f32["q"], f32["k"], f32["v"], w.causal)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    print(f"  O: rel-L2 vs oracle {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}, "
+          f"LSE max err {np.max(np.abs(lse_g - lse_f)):.2e} mean {np.mean(np.abs(lse_g - lse_f)):.2e}")
+    assert M.rel_l2(o_g, o_f) <= REL_L2, M.rel_l2(o_g, o_f)
+    _check_lse(lse_g, lse_f)
+    assert M.cos_sim(o_g, o_e) >= COS_O
+    assert np.max(np.abs(lse_g - lse_e)) <= 0.7
+
+
+QK = [W.custom(1, 2, 130, True, True, True, "rowscale", 261), W.custom(2, 1, 200, False, True, False, "rowscale", 262)]
+
+
+@pytest.mark.parametrize("w", QK, ids=_ids(QK))
+def test_fp4_qk_norm_parity(w):
+    print(f"[fp4 qk_norm] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    o, lse = sb.fwd(G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]), w.causal, w.smooth_q, w.smooth_k, qk_norm=True,
+                    fp4=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o), lse.cpu().numpy()
+    o_f, lse_f = Y.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    o_e, _ = exact.fwd_bh(f32["q"], f32["k"], f32["v"], w.causal, qk_norm=True)
+    print(f"  O: rel-L2 vs oracle {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}")
+    assert M.rel_l2(o_g, o_f) <= REL_L2
+    _check_lse(lse_g, lse_f)
+    assert M.cos_sim(o_g, o_e) >= COS_O
+
+
+def test_fp4_zero_inputs_and_rejections():
+    z = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
+    for causal in (False, True):
+        o, lse = sb.fwd(z, z, z, causal, True, True, fp4=True)
+        torch.cuda.synchronize()
+        assert torch.all(o == 0)
+        n = torch.arange(1, 101, device="cuda", dtype=torch.float32) if causal else torch.full((100,), 100.0, device="cuda")
+        assert torch.allclose(lse[0, 0], torch.log(n), atol=1e-5)
+    p = sb.make_params(1, 2, 100, True, True, True, fp4=True)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sb.SageBwdError, match="unsupported"):
+        sb.bwd_stage("BWD_PREPARE", z, z, z, z, lse, z, z, z, z, ws, p)
+
+
+FULL = [("llama16k", (0, 29)), ("video", (1, 3))]
+
+
+@pytest.mark.parametrize("name,head", FULL, ids=[c[0] for c in FULL])
+def test_fp4_fullsize_sampled_parity(name, head):
+    """The whole forward of the workload on the GPU; the oracle's forward of one
+    sampled head over every row."""
+    w = W.WORKLOADS[name]
+    b, h = head
+    print(f"[fp4 fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} head={head}", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv = (G.dev(x[n]) for n in ("q", "k", "v"))
+    o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, fp4=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o[b, h]), lse[b, h].cpu().numpy()
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    del x, tq, tk, tv, o, lse
+    f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
+    N, T = w.N, (w.N + 63) // 64
+    pp = Y.prepare(f["q"], f["k"], f["v"], w.smooth_q, w.smooth_k)
+    o_f, lse_f = Y.fwd_head(pp, w.causal)
+    o_f, lse_f = o_f[:N], lse_f[:N]
+    print(f"  O: rel-L2 vs oracle {M.rel_l2(o_g, o_f):.2e}, LSE max err {np.max(np.abs(lse_g - lse_f)):.2e}",
+          flush=True)
+    assert M.rel_l2(o_g, o_f) <= REL_L2, M.rel_l2(o_g, o_f)
+    _check_lse(lse_g, lse_f)
+    rows = np.concatenate([np.arange(i * 64, min(N, i * 64 + 64)) for i in sorted({0, T // 2, T - 1})])
+    oe, _, _, _, _ = exact.sampled(f["q"], f["k"], f["v"], f["do"], w.causal, rows, rows)
+    cos = M.cos_sim(o_g[rows], oe)
+    print(f"  cos vs exact on sampled rows {cos:.6f}", flush=True)
+    assert cos >= COS_O
