@@ -657,6 +657,31 @@ __device__ __forceinline__ v4i fp8_block_codes(const float (&x)[16], float scale
                (int)fp8_quad(x[8], x[9], x[10], x[11], scale), (int)fp8_quad(x[12], x[13], x[14], x[15], scale)};
 }
 
+// S = Q K^T (dequantized in the MFMA) and P = exp2(S log2(e)/8 + bias_j -
+// lse2_i) for one 64-query x 32-key tile (lane = key, registers = queries);
+// MASK only on the causal diagonal and the ragged last key block.
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i kop, uint32_t q_w, int sk_e,
+                                              float brow, int i, int key, int N, int lane, int h,
+                                              float (&p)[2][16]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const v16f sx = mfma_fp8(cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]),
+                                 kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
+        const float arow = h == 0 ? -sm.lse2[buf][32 * qb + lane % 32] : 1.0f;
+        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], SCORE_SCALE_LOG2, corr[r]));
+            if (MASK) {
+                const int qq = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
+                if (key >= N || (CAUSAL && key > qq)) pv = 0.0f;
+            }
+            p[qb][r] = pv;
+        }
+    }
+}
+
 template <bool CAUSAL, bool SMOOTHQ>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
     __shared__ DkdvMxSmem sm;
@@ -738,25 +763,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
         const uint32_t q_w = sm.qs[buf][0], do_w = sm.qs[buf][1];
         float p[2][16];   // [qb]: lane = key, registers = queries
-        {
-            // S = Q K^T (dequantized), P = exp2(S log2(e)/8 + bias_j - lse2_i)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const v16f sx = mfma_fp8(cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]),
-                                         kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
-                const float arow = h == 0 ? -sm.lse2[buf][32 * qb + l32] : 1.0f;
-                const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], SCORE_SCALE_LOG2, corr[r]));
-                    if (masked) {
-                        const int qq = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
-                        if (key >= a.N || (CAUSAL && key > qq)) pv = 0.0f;
-                    }
-                    p[qb][r] = pv;
-                }
-            }
-        }
+        if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p);
+        else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p);
         // P codes per 32x32 block (query half qb x this wave's keys)
         int eP[2];
         v4i pc[2];
