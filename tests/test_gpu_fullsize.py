@@ -152,3 +152,57 @@ def test_head_groups_bitwise():
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), g_full, g_one):
         assert torch.equal(a[1:2].view(torch.int16), b.view(torch.int16)), name
+
+
+MAXN_MODES = ["int8", "mxfp8", "fp4"]
+
+
+@pytest.mark.parametrize("mode", MAXN_MODES)
+def test_max_n(mode):
+    """The largest N the ABI accepts (2^18, one causal head with both
+    smoothings; its backward keeps 34 GB of dS codes): O and LSE of the first,
+    a middle and the last query block against the oracle (each side its own
+    forward), and for the trainable modes dQ of the same blocks end to end
+    (a row's dQ needs only that row's O, LSE and Delta, so the oracle's
+    forward of those blocks feeds its backward)."""
+    from oracle import fp4 as Y, mxfp8 as X
+    N = 1 << 18
+    w = W.custom(1, 1, N, True, True, True, "kbias", 310)
+    T = N // 64
+    blocks = [0, T // 2 + 3, T - 1]
+    rows = np.concatenate([np.arange(i * 64, i * 64 + 64) for i in blocks])
+    print(f"[max N] mode={mode} N={N} blocks={blocks}", flush=True)
+    x = W.make_inputs(w)
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    kw = {"mxfp8": mode == "mxfp8", "fp4": mode == "fp4"}
+    o, lse = sb.fwd(tq, tk, tv, True, True, True, **kw)
+    dq_g = None
+    if mode != "fp4":
+        dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, True, True, True, mxfp8=kw["mxfp8"])
+        torch.cuda.synchronize()
+        dq_g = G.host_f32(dq[0, 0])[rows]
+        for t in (dk, dv):
+            assert bool(torch.isfinite(t.float()).all())
+        del dq, dk, dv
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o[0, 0])[rows], lse[0, 0].cpu().numpy()[rows]
+    del tq, tk, tv, tdo, o, lse
+    f = {n: W.bf16_bits_to_f32(a)[0, 0] for n, a in x.items()}
+    mod = {"int8": F, "mxfp8": X, "fp4": Y}[mode]
+    pp = mod.prepare(f["q"], f["k"], f["v"], True, True)
+    o_f, lse_f = mod.fwd_head(pp, True, qblocks=blocks)
+    err_o = M.rel_l2(o_g, o_f)
+    print(f"  O rel-L2 vs oracle {err_o:.2e}, LSE max err {np.max(np.abs(lse_g - lse_f)):.2e}", flush=True)
+    assert np.all(np.isfinite(o_g)) and err_o <= 1e-2
+    assert np.max(np.abs(lse_g - lse_f)) <= (2e-3 if mode == "int8" else 0.0625 if mode == "mxfp8" else 0.406)
+    assert np.mean(np.abs(lse_g - lse_f)) <= 2e-4
+    if dq_g is not None:
+        o_all = np.zeros((N, 64), np.float32)
+        lse_all = np.zeros(N, np.float32)
+        o_all[rows] = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
+        lse_all[rows] = lse_f
+        bp = mod.prepare_bwd(pp, f["v"], o_all, lse_all, f["do"])
+        dq_f, _, _ = mod.bwd_head(bp, True, qblocks=blocks, kblocks=[])
+        err = M.rel_l2(dq_g, dq_f)
+        print(f"  dQ rel-L2 vs oracle {err:.2e}", flush=True)
+        assert np.all(np.isfinite(dq_g)) and err <= 1e-2
