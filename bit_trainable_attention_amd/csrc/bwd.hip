@@ -482,17 +482,52 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 // in lane n and keys 8(r/4) + 4h + r%4 in register r, exact small integers
 // whose low bytes are the codes in the B-operand layout of K^T dS^T.
 //
-// Each wave owns 32 queries and streams its tiles independently (no LDS, no
-// barriers): per key block 2 KB of dS codes (HBM) and the 4 KB K^T code block
-// (shared by every query block of the head, so an L2 hit), prefetched two
-// blocks ahead.  The kernel is bound by the HBM read of the dS codes.
+// Each wave owns one 64-query block: per key block it streams the 4 KB dS
+// code tile of its block (HBM, read once, prefetched DQ_DEPTH key blocks
+// ahead) and reads the 4 KB K^T code block of the key block, which every
+// query block of the head needs.  The K^T reads from L2, not the dS stream,
+// bounded an earlier form with 32 queries per wave and one K^T read per wave;
+// here each K^T block serves 64 queries, and the four waves of a workgroup
+// (four consecutive query blocks, so nearly the same key-block range) share
+// one copy staged through LDS, loaded a quarter per wave.
 
-constexpr int DQ_DEPTH = 4;
+constexpr int DQ_DEPTH = 3;
+constexpr int DQ_BLOCKS_PER_WG = 4;   // one query block per wave
 
 struct DqStep {
-    v4i ds[2];     // dS codes of key halves kh = 0, 1 (A operand, lane = key)
-    float sds, sk; // s_dS(i, t) and s_K,t
+    v4i ds[2][2];  // [qs][kh]: dS codes of query half qs, key half kh (A operand, lane = key)
+    v4i kq;        // this wave's quarter of the K^T code block (INT8 kernel)
+    float sds, sk; // s_dS(i, t) and s_K,t (MXFP8 kernel: their exponent words)
 };
+
+// Vector loads the compiler does not track (inline assembly): the INT8 dQ
+// kernel waits for them itself with dq_wait, which names the registers of a
+// ring slot as operands so that no use of them can move above the wait.
+// (The compiler's own wait counts lose precision around the prefetch loop and
+// fall back to waiting for every load in flight.)
+__device__ __forceinline__ v4i gload_nt(const v4i* p) {
+    v4i r;
+    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p));
+    return r;
+}
+__device__ __forceinline__ v4i gload(const v4i* p) {
+    v4i r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p));
+    return r;
+}
+__device__ __forceinline__ float gload1(const float* p) {
+    float r;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p));
+    return r;
+}
+// Wait until at most N of this wave's vector loads are outstanding.
+template <int N>
+__device__ __forceinline__ void dq_wait(DqStep& s) {
+    asm volatile("s_waitcnt vmcnt(%7)"
+                 : "+v"(s.ds[0][0]), "+v"(s.ds[0][1]), "+v"(s.ds[1][0]), "+v"(s.ds[1][1]), "+v"(s.kq), "+v"(s.sds),
+                   "+v"(s.sk)
+                 : "n"(N));
+}
 
 // dQ (x 1/8) in bf16; with QK-norm dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
 // other 32 channels of this lane's query being in the other half of the wave.
@@ -542,21 +577,24 @@ __device__ __forceinline__ void dq_epilogue(const BwdArgs& a, v16f (&dq)[2], int
 
 template <bool CAUSAL, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
-    int bh, g;
-    map_group_bwd(a.ngroups, a.BH, false, bh, g);
+    // the wave index as a uniform value, so everything per wave (block,
+    // range, scale loads, the step guard) stays scalar
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, h = lane / 32,
+              l32 = lane % 32;
     const int T = a.T;
-    const int qblk = 2 * g + wave / 2, qh = wave % 2;
-    if (qblk >= T) return;                                    // waves never synchronize
-    const int q = qblk * BLK + 32 * qh + l32;                 // this lane's query
-    const int t_end = CAUSAL ? qblk + 1 : T;
+    int bh, g;
+    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g);
+    const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
+    const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);   // waves past T only help stage K^T
+    const bool live = DQ_BLOCKS_PER_WG * g + wave < T;
+    const int t_end = !live ? 0 : CAUSAL ? qblk + 1 : T;
     const size_t bt = (size_t)bh * T;
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
     const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
-    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + qh * 64 + lane;
+    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + lane;
     const float* dss = a.ds_scale + tile0;
-    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096) + lane;
+    const v4i* ktg_wave = (const v4i*)(a.k_t + bt * 4096) + 64 * wave + lane;
     const float* skg = a.sk + bt;
 
     // INT8 identity as the B operand: column n = l32 has its one at k
@@ -564,70 +602,89 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     v4i eye = v4i{0, 0, 0, 0};
     if (h == (l32 % 8) / 4) eye[l32 / 8] = 1 << (8 * (l32 % 4));
 
-    // the dS codes (read once, from HBM) are prefetched DQ_DEPTH key blocks
-    // ahead; the K^T codes (L2 hits) are loaded at their step
-    auto load = [&](int t, DqStep& s) {
-        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);
-        s.ds[1] = __builtin_nontemporal_load(dsg + (size_t)t * 256 + 128);
-        s.sds = dss[t];
-        s.sk = skg[t];
+    const int wg_end = CAUSAL ? min(qblk_wg_last, T - 1) + 1 : T;   // steps of the workgroup's longest wave
+    // chunk (kh * 2 + qs) * 64 + lane of a tile: key 32 kh + l32, 16 queries of
+    // half qs.  Every step loads (past the wave's own range it re-reads its
+    // last tile), so the wait counts before each use are fixed.
+    auto load = [&](int t, DqStep& s) {   // seven untracked loads per slot
+        const int td = min(t, max(t_end - 1, 0));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) s.ds[qs][kh] = gload_nt(dsg + (size_t)td * 256 + (kh * 2 + qs) * 64);
+        s.kq = gload(ktg_wave + (size_t)min(t, wg_end - 1) * 256);
+        s.sds = gload1(dss + td);
+        s.sk = gload1(skg + td);
     };
-    v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, regs = channels
-    auto step = [&](int t, const DqStep& s) {
+    v16f dq[2][2] = {{v16f{}, v16f{}}, {v16f{}, v16f{}}};   // [qs][db]: lane = query, regs = channels
+    auto step = [&](int t, const DqStep& s, const v4i* kts) {
         v4i kt[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = ktg[(size_t)t * 256 + j * 64];
-        v4i dc[2];
-        v16i tr[2];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            tr[kh] = mfma_i8(s.ds[kh], eye, v16i{});
-            dc[kh] = v4i{(int)pack4(tr[kh][0], tr[kh][1], tr[kh][2], tr[kh][3]),
-                         (int)pack4(tr[kh][4], tr[kh][5], tr[kh][6], tr[kh][7]),
-                         (int)pack4(tr[kh][8], tr[kh][9], tr[kh][10], tr[kh][11]),
-                         (int)pack4(tr[kh][12], tr[kh][13], tr[kh][14], tr[kh][15])};
-        }
+        for (int j = 0; j < 4; ++j) kt[j] = kts[j * 64 + lane];
         const float wq = s.sds * s.sk;
         const bool dump_here = DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t;
-        if (dump_here) {
-            uint8_t* dp = a.dump;
-            if (lane == 0 && qh == 0) dump_at<float>(dp, dumpoff::SC)[0] = s.sds;
+        if (dump_here && lane == 0) dump_at<float>(a.dump, dumpoff::SC)[0] = s.sds;
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+        for (int qs = 0; qs < 2; ++qs) {
+            v4i dc[2];
+            v16i tr[2];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    dp[dumpoff::C1 + (q % 64) * 64 + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4)] = (uint8_t)tr[kh][r];
-        }
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            v16i acc = mfma_i8(kt[db * 2 + 0], dc[0], v16i{});
-            acc = mfma_i8(kt[db * 2 + 1], dc[1], acc);
+            for (int kh = 0; kh < 2; ++kh) {
+                tr[kh] = mfma_i8(s.ds[qs][kh], eye, v16i{});
+                dc[kh] = v4i{(int)pack4(tr[kh][0], tr[kh][1], tr[kh][2], tr[kh][3]),
+                             (int)pack4(tr[kh][4], tr[kh][5], tr[kh][6], tr[kh][7]),
+                             (int)pack4(tr[kh][8], tr[kh][9], tr[kh][10], tr[kh][11]),
+                             (int)pack4(tr[kh][12], tr[kh][13], tr[kh][14], tr[kh][15])};
+            }
             if (dump_here) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    dump_at<int>(a.dump, dumpoff::ACC1)[(q % 64) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc[r];
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        a.dump[dumpoff::C1 + (32 * qs + l32) * 64 + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4)] =
+                            (uint8_t)tr[kh][r];
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
+            for (int db = 0; db < 2; ++db) {
+                v16i acc = mfma_i8(kt[db * 2 + 0], dc[0], v16i{});
+                acc = mfma_i8(kt[db * 2 + 1], dc[1], acc);
+                if (dump_here) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(a.dump, dumpoff::ACC1)[(32 * qs + l32) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] =
+                            acc[r];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dq[qs][db][r] = __builtin_fmaf((float)acc[r], wq, dq[qs][db][r]);
+            }
         }
     };
 
+    // the K^T block of each step is shared by the workgroup's four waves:
+    // each wave stages one quarter (loaded with its dS codes, through
+    // registers so no LDS DMA forces a full wait) into a double-buffered LDS
+    // tile
+    __shared__ v4i kts[2][256];
     DqStep ring[DQ_DEPTH];
 #pragma unroll
-    for (int j = 0; j < DQ_DEPTH; ++j)
-        if (j < t_end) load(j, ring[j]);
-    for (int t0 = 0; t0 < t_end; t0 += DQ_DEPTH) {
+    for (int j = 0; j < DQ_DEPTH; ++j) load(j, ring[j]);
+    for (int t0 = 0; t0 < wg_end; t0 += DQ_DEPTH) {
 #pragma unroll
         for (int j = 0; j < DQ_DEPTH; ++j) {
             const int t = t0 + j;
-            if (t < t_end) {
-                step(t, ring[j]);
-                if (t + DQ_DEPTH < t_end) load(t + DQ_DEPTH, ring[j]);
+            if (t < wg_end) {
+                dq_wait<7 * (DQ_DEPTH - 1)>(ring[j]);   // this slot's loads have landed
+                kts[t & 1][64 * wave + lane] = ring[j].kq;
+                lds_barrier();   // LDS only: the prefetch stays in flight
+                if (t < t_end) step(t, ring[j], kts[t & 1]);
+                load(t + DQ_DEPTH, ring[j]);
             }
         }
     }
-
-    dq_epilogue(a, dq, bh, q, h, rowbase);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's last, unused loads
+    if (!live) return;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) dq_epilogue(a, dq[qs], bh, qblk * BLK + 32 * qs + l32, h, rowbase);
 }
 
 // ------------------------------------------------------------------ MXFP8
@@ -876,22 +933,24 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
 // codes, the block exponents applied inside the instruction.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq_mx(BwdArgs a) {
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
-    int bh, g;
-    map_group_bwd(a.ngroups, a.BH, false, bh, g);
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, h = lane / 32,
+              l32 = lane % 32;
     const int T = a.T;
-    const int qblk = 2 * g + wave / 2, qh = wave % 2;
-    if (qblk >= T) return;
-    const int q = qblk * BLK + 32 * qh + l32;
-    const int t_end = CAUSAL ? qblk + 1 : T;
+    int bh, g;
+    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g);
+    const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
+    const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);
+    const bool live = DQ_BLOCKS_PER_WG * g + wave < T;
+    const int t_end = !live ? 0 : CAUSAL ? qblk + 1 : T;
+    const int wg_end = CAUSAL ? min(qblk_wg_last, T - 1) + 1 : T;
     const size_t bt = (size_t)bh * T;
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
     const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
-    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + qh * 64 + lane;
-    const uint32_t* dss = (const uint32_t*)(a.ds_scale + tile0);
-    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096) + lane;
-    const uint32_t* skg = (const uint32_t*)a.sk + bt;
+    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + lane;
+    const float* dss = a.ds_scale + tile0;            // exponent words, loaded as their bit patterns
+    const v4i* ktg_wave = (const v4i*)(a.k_t + bt * 4096) + 64 * wave + lane;
+    const float* skg = a.sk + bt;
 
     // E4M3 identity (B operand): column n = l32 has 1.0 at k position n,
     // which lies in half (n % 8) / 4, byte 4 (n / 8) + n % 4
@@ -899,48 +958,61 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_mx(BwdArgs a) {
     if (h == (l32 % 8) / 4) eye[l32 / 8] = E4M3_ONE << (8 * (l32 % 4));
     const int e_one = opaque(E8M0_ONE);
 
-    auto load = [&](int t, DqStep& s) {
-        s.ds[0] = __builtin_nontemporal_load(dsg + (size_t)t * 256);
-        s.ds[1] = __builtin_nontemporal_load(dsg + (size_t)t * 256 + 128);
-        s.sds = __uint_as_float(dss[t]);
-        s.sk = __uint_as_float(skg[t]);
+    auto load = [&](int t, DqStep& s) {   // seven untracked loads per slot, as in the INT8 kernel
+        const int td = min(t, max(t_end - 1, 0));
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) s.ds[qs][kh] = gload_nt(dsg + (size_t)td * 256 + (kh * 2 + qs) * 64);
+        s.kq = gload(ktg_wave + (size_t)min(t, wg_end - 1) * 256);
+        s.sds = gload1(dss + td);
+        s.sk = gload1(skg + td);
     };
-    v16f dq[2] = {v16f{}, v16f{}};
-    auto step = [&](int t, const DqStep& s) {
+    v16f dq[2][2] = {{v16f{}, v16f{}}, {v16f{}, v16f{}}};
+    auto step = [&](const DqStep& s, const v4i* kts) {
         v8i kt[2];
 #pragma unroll
-        for (int db = 0; db < 2; ++db) kt[db] = cat8(ktg[(size_t)t * 256 + (db * 2 + 0) * 64], ktg[(size_t)t * 256 + (db * 2 + 1) * 64]);
-        v4i dc[2];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const v16f tr = mfma_fp8(cat8(s.ds[kh], v4i{}), eye, v16f{}, e_one, e_one);
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = tr[r];
-            dc[kh] = fp8_block_codes(x, 1.0f);
-        }
+        for (int db = 0; db < 2; ++db) kt[db] = cat8(kts[(db * 2 + 0) * 64 + lane], kts[(db * 2 + 1) * 64 + lane]);
         const uint32_t ds_w = __float_as_uint(s.sds), sk_w = __float_as_uint(s.sk);
-        const v8i db8 = cat8(dc[0], dc[1]);
-        const int de = ebyte(ds_w, 2 * h + qh);   // key half h, this wave's query half
 #pragma unroll
-        for (int db = 0; db < 2; ++db) dq[db] = mfma_fp8(kt[db], db8, dq[db], ebyte(sk_w, 2 * h + db), de);
+        for (int qs = 0; qs < 2; ++qs) {
+            v4i dc[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const v16f tr = mfma_fp8(cat8(s.ds[qs][kh], v4i{}), eye, v16f{}, e_one, e_one);
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = tr[r];
+                dc[kh] = fp8_block_codes(x, 1.0f);
+            }
+            const v8i db8 = cat8(dc[0], dc[1]);
+            const int de = ebyte(ds_w, 2 * h + qs);   // key half h, query half qs
+#pragma unroll
+            for (int db = 0; db < 2; ++db) dq[qs][db] = mfma_fp8(kt[db], db8, dq[qs][db], ebyte(sk_w, 2 * h + db), de);
+        }
     };
 
+    __shared__ v4i kts[2][256];
     DqStep ring[DQ_DEPTH];
 #pragma unroll
-    for (int j = 0; j < DQ_DEPTH; ++j)
-        if (j < t_end) load(j, ring[j]);
-    for (int t0 = 0; t0 < t_end; t0 += DQ_DEPTH) {
+    for (int j = 0; j < DQ_DEPTH; ++j) load(j, ring[j]);
+    for (int t0 = 0; t0 < wg_end; t0 += DQ_DEPTH) {
 #pragma unroll
         for (int j = 0; j < DQ_DEPTH; ++j) {
             const int t = t0 + j;
-            if (t < t_end) {
-                step(t, ring[j]);
-                if (t + DQ_DEPTH < t_end) load(t + DQ_DEPTH, ring[j]);
+            if (t < wg_end) {
+                dq_wait<7 * (DQ_DEPTH - 1)>(ring[j]);
+                kts[t & 1][64 * wave + lane] = ring[j].kq;
+                lds_barrier();
+                if (t < t_end) step(ring[j], kts[t & 1]);
+                load(t + DQ_DEPTH, ring[j]);
             }
         }
     }
-    dq_epilogue(a, dq, bh, q, h, rowbase);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!live) return;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) dq_epilogue(a, dq[qs], bh, qblk * BLK + 32 * qs + l32, h, rowbase);
 }
 
 // Instantiation by (causal, Q-smoothing, all-INT8 dO V^T, tile dump).
@@ -985,7 +1057,7 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
 #undef SAGEBWD_LAUNCH_BWD
 
 int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump) {
-    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
+    dim3 grid(((a.T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG) * BH), block(64 * BWD_WAVES);
     if (mx) {
         if (causal) hipLaunchKernelGGL((k_bwd_dq_mx<true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((k_bwd_dq_mx<false>), grid, block, 0, st, a);
