@@ -141,20 +141,36 @@ template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float brow,
                                            int i, int key, int N, int lane, int h, float (&p)[2][16],
                                            uint8_t* dp = nullptr) {
+    // all operands first (the LSE row is read by every lane, so no divergent
+    // branch splits the reads from the MFMAs), then both query halves' MFMAs
+    v4i qa[2][2];
+    float lv[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        v16i s = mfma_i8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], kop[0], v16i{});
-        s = mfma_i8(sm.q_r[buf][(qb * 2 + 1) * 64 + lane], kop[1], s);
-        const float arow = h == 0 ? -sm.lse2[buf][32 * qb + lane % 32] : 1.0f;
-        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
+        qa[qb][0] = sm.q_r[buf][(qb * 2 + 0) * 64 + lane];
+        qa[qb][1] = sm.q_r[buf][(qb * 2 + 1) * 64 + lane];
+        lv[qb] = sm.lse2[buf][32 * qb + lane % 32];
+        asm volatile("" : "+v"(lv[qb]));
+    }
+    v16i s[2];
+    v16f corr[2];
+    s[0] = mfma_i8(qa[0][0], kop[0], v16i{});
+    s[1] = mfma_i8(qa[1][0], kop[0], v16i{});
+    s[0] = mfma_i8(qa[0][1], kop[1], s[0]);
+    s[1] = mfma_i8(qa[1][1], kop[1], s[1]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+        corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
         if (dp) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dump_at<int>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = s[r];
+                dump_at<int>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = s[qb][r];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[r], sc, corr[r]));
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[qb][r], sc, corr[qb][r]));
             if (MASK) {
                 const int q = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
                 if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
@@ -167,7 +183,8 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
 template <bool CAUSAL, bool SMOOTHQ, bool INT8DP, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     __shared__ DkdvSmem sm;
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
     int bh, g;
     map_group_bwd(a.ngroups, a.BH, true, bh, g);
     const int T = a.T;
@@ -721,15 +738,27 @@ template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i kop, uint32_t q_w, int sk_e,
                                               float brow, int i, int key, int N, int lane, int h,
                                               float (&p)[2][16]) {
+    // all operands first (the LSE row is read by every lane, so no divergent
+    // branch splits the reads from the MFMAs), then both query halves' MFMAs
+    v8i qa[2];
+    float lv[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        const v16f sx = mfma_fp8(cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]),
-                                 kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
-        const float arow = h == 0 ? -sm.lse2[buf][32 * qb + lane % 32] : 1.0f;
-        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(arow, brow, v16f{}, 0, 0, 0);
+        qa[qb] = cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]);
+        lv[qb] = sm.lse2[buf][32 * qb + lane % 32];
+        asm volatile("" : "+v"(lv[qb]));
+    }
+    v16f sx[2], corr[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) sx[qb] = mfma_fp8(qa[qb], kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+        corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], SCORE_SCALE_LOG2, corr[r]));
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[qb][r], SCORE_SCALE_LOG2, corr[qb][r]));
             if (MASK) {
                 const int qq = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
                 if (key >= N || (CAUSAL && key > qq)) pv = 0.0f;
@@ -742,7 +771,8 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
 template <bool CAUSAL, bool SMOOTHQ>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
     __shared__ DkdvMxSmem sm;
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
     int bh, g;
     map_group_bwd(a.ngroups, a.BH, true, bh, g);
     const int T = a.T;
