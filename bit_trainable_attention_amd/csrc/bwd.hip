@@ -137,9 +137,13 @@ struct DkdvSmem {
 // B[l/32][l%32]) in the accumulator layout of the score product, so each score
 // costs one FMA before its exp.  MASK only on the causal diagonal tile and the
 // ragged last key block, so the common path carries no per-element selects.
-template <bool CAUSAL, bool MASK>
+// dP - Delta (the same layout) is formed here too: it does not depend on P, so
+// its MFMAs are scheduled one by one between groups of the score arithmetic
+// instead of stalling the wave later.
+template <bool CAUSAL, bool MASK, bool INT8DP>
 __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float brow,
                                            int i, int key, int N, int lane, int h, float (&p)[2][16],
+                                           v16f (&dpd)[2], const v8h (&vh)[4], const v4i (&vop)[2], float sV,
                                            uint8_t* dp = nullptr) {
     // all operands first (the LSE row is read by every lane, so no divergent
     // branch splits the reads from the MFMAs), then both query halves' MFMAs
@@ -161,6 +165,36 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
         corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
+    if (!INT8DP) __builtin_amdgcn_sched_barrier(0);   // score MFMAs issue before everything below
+    // dP - Delta = dO V^T + (-Delta) on the FP16 MFMA with -Delta as the
+    // accumulator input (all-INT8: s_dO s_V (dO codes V codes^T) + (-Delta))
+    const int l32 = lane % 32;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int row = 32 * qb + l32;
+        v16f nd;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
+            nd[4 * r4 + 0] = d4.x;
+            nd[4 * r4 + 1] = d4.y;
+            nd[4 * r4 + 2] = d4.z;
+            nd[4 * r4 + 3] = d4.w;
+        }
+        if (INT8DP) {
+            const v4i* dor = (const v4i*)sm.do16[buf];
+            v16i ai = mfma_i8(dor[(qb * 2 + 0) * 64 + lane], vop[0], v16i{});
+            ai = mfma_i8(dor[(qb * 2 + 1) * 64 + lane], vop[1], ai);
+            const float wdp = sm.qs[buf][1] * sV;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dpd[qb][r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
+        } else {
+            v16f d = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
+            d = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], d);
+            d = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], d);
+            dpd[qb] = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], d);
+        }
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         if (dp) {
@@ -176,6 +210,15 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
                 if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
             }
             p[qb][r] = pv;
+        }
+    }
+    if (!INT8DP) {
+        // the score MFMAs first, then each dP MFMA between groups of exps
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
         }
     }
 }
@@ -277,9 +320,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         const float sQ = sm.qs[buf][0];
         const float sc = tile_scale(sQ, sK);
         uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
+        v16f dpe[2];
         if (active) {
-            if (masked) dkdv_probs<CAUSAL, true>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
-            else dkdv_probs<CAUSAL, false>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+            if (masked)
+                dkdv_probs<CAUSAL, true, INT8DP>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
+                                                 DUMP ? dp : nullptr);
+            else
+                dkdv_probs<CAUSAL, false, INT8DP>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
+                                                  DUMP ? dp : nullptr);
             if (DUMP && dp) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -337,38 +385,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
             }
-            // dP - Delta = dO V^T + (-Delta) (FP16 MFMA, -Delta as the
-            // accumulator input), dS = P * (dP - Delta) in place of P
+            // dS = P * (dP - Delta) in place of P
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int row = 32 * qb + l32;
-                v16f nd;
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
-                    nd[4 * r4 + 0] = d4.x;
-                    nd[4 * r4 + 1] = d4.y;
-                    nd[4 * r4 + 2] = d4.z;
-                    nd[4 * r4 + 3] = d4.w;
-                }
-                v16f dpd;
-                if (INT8DP) {
-                    // dP - Delta = s_dO s_V (dO codes V codes^T) + (-Delta)
-                    const v4i* dor = (const v4i*)sm.do16[buf];
-                    v16i ai = mfma_i8(dor[(qb * 2 + 0) * 64 + lane], vop[0], v16i{});
-                    ai = mfma_i8(dor[(qb * 2 + 1) * 64 + lane], vop[1], ai);
-                    const float wdp = sm.qs[buf][1] * sV;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dpd[r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
-                } else {
-                    dpd = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
-                    dpd = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dpd);
-                    dpd = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dpd);
-                    dpd = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dpd);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpd[r];
-            }
+                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpe[qb][r];
             {
                 float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
