@@ -174,6 +174,25 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         u0 = *(const uint4*)src;
         u1 = *(const uint4*)(src + 8);
     }
+    // this thread's 16 channels of the centring mean and of the mean its side
+    // output needs (Q: mu_K for the LSE correction; K: mu_Q for the score
+    // bias), loaded as vectors together with the tokens (loads of single
+    // elements behind the pointer tests were waited for one after another)
+    float mc[16], mo[16];
+    const float* mo_src = tensor == 0 ? (a.smooth_k ? a.mu_k : nullptr) : tensor == 1 ? a.mu_q : nullptr;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 c4 = mu ? ((const float4*)(mu + (size_t)bh * HD + 16 * g))[j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 o4 = mo_src ? ((const float4*)(mo_src + (size_t)bh * HD + 16 * g))[j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        mc[4 * j4 + 0] = c4.x;
+        mc[4 * j4 + 1] = c4.y;
+        mc[4 * j4 + 2] = c4.z;
+        mc[4 * j4 + 3] = c4.w;
+        mo[4 * j4 + 0] = o4.x;
+        mo[4 * j4 + 1] = o4.y;
+        mo[4 * j4 + 2] = o4.z;
+        mo[4 * j4 + 3] = o4.w;
+    }
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     const float* rn = tensor == 0 ? a.rq : tensor == 1 ? a.rk : nullptr;   // QK-norm: x_n = bf16(fp32(x r))
     if (rn) {
@@ -193,7 +212,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        x[j] = mu ? raw[j] - mu[(size_t)bh * HD + 16 * g + j] : raw[j];
+        x[j] = mu ? raw[j] - mc[j] : raw[j];
         if (!valid) x[j] = 0.0f;
         amax = fmaxf(amax, fabsf(x[j]));
     }
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         for (int j = 0; j < 16; ++j) {
             const int byte = (cw[j / 4] >> (8 * (j % 4))) & 0xFF;
             codes[r][16 * g + j] = (int8_t)byte;
-            if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], fp8_value(cw[j / 4], j % 4), mu_dot);
+            if (tensor == 1) mu_dot = __builtin_fmaf(mo[j], fp8_value(cw[j / 4], j % 4), mu_dot);
         }
         s = sc;
     } else {
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
             const int cq = code_int(x[j], inv);
             codes[r][16 * g + j] = (int8_t)cq;
             cw[j / 4] |= (uint32_t)(uint8_t)cq << (8 * (j % 4));
-            if (tensor == 1) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], (float)cq, mu_dot);
+            if (tensor == 1) mu_dot = __builtin_fmaf(mo[j], (float)cq, mu_dot);
         }
     }
     int8_t* rdst = tensor == 0 ? a.q_r : tensor == 1 ? a.k_r : nullptr;
@@ -239,7 +258,7 @@ __global__ __launch_bounds__(256) void k_quantize(QuantArgs a) {
         float cd = 0.0f;
         if (a.smooth_k) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], a.mu_k[(size_t)bh * HD + 16 * g + j], cd);
+            for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], mo[j], cd);
         }
         cd += __shfl_xor(cd, 1, 64);
         cd += __shfl_xor(cd, 2, 64);
@@ -285,6 +304,25 @@ __global__ __launch_bounds__(256) void k_quantize_fp4(QuantArgs a) {
         u0 = *(const uint4*)src;
         u1 = *(const uint4*)(src + 8);
     }
+    // this thread's 16 channels of the centring mean and of the mean its side
+    // output needs (Q: mu_K for the LSE correction; K: mu_Q for the score
+    // bias), loaded as vectors together with the tokens (loads of single
+    // elements behind the pointer tests were waited for one after another)
+    float mc[16], mo[16];
+    const float* mo_src = tensor == 0 ? (a.smooth_k ? a.mu_k : nullptr) : tensor == 1 ? a.mu_q : nullptr;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 c4 = mu ? ((const float4*)(mu + (size_t)bh * HD + 16 * g))[j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 o4 = mo_src ? ((const float4*)(mo_src + (size_t)bh * HD + 16 * g))[j4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        mc[4 * j4 + 0] = c4.x;
+        mc[4 * j4 + 1] = c4.y;
+        mc[4 * j4 + 2] = c4.z;
+        mc[4 * j4 + 3] = c4.w;
+        mo[4 * j4 + 0] = o4.x;
+        mo[4 * j4 + 1] = o4.y;
+        mo[4 * j4 + 2] = o4.z;
+        mo[4 * j4 + 3] = o4.w;
+    }
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     const float* rn = tensor == 0 ? a.rq : tensor == 1 ? a.rk : nullptr;
     if (rn) {
@@ -304,7 +342,7 @@ __global__ __launch_bounds__(256) void k_quantize_fp4(QuantArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        x[j] = mu ? raw[j] - mu[(size_t)bh * HD + 16 * g + j] : raw[j];
+        x[j] = mu ? raw[j] - mc[j] : raw[j];
         if (!valid) x[j] = 0.0f;
         amax = fmaxf(amax, fabsf(x[j]));
     }
@@ -323,7 +361,7 @@ __global__ __launch_bounds__(256) void k_quantize_fp4(QuantArgs a) {
             float cd = 0.0f;
             if (a.smooth_k) {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], a.mu_k[(size_t)bh * HD + 16 * g + j], cd);
+                for (int j = 0; j < 16; ++j) cd = __builtin_fmaf(raw[j], mo[j], cd);
             }
             cd += __shfl_xor(cd, 1, 64);
             cd += __shfl_xor(cd, 2, 64);
@@ -332,7 +370,7 @@ __global__ __launch_bounds__(256) void k_quantize_fp4(QuantArgs a) {
             // Q-smoothing bias from the centred float K (not its 4-bit codes)
             float mu_dot = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) mu_dot = __builtin_fmaf(a.mu_q[(size_t)bh * HD + 16 * g + j], x[j], mu_dot);
+            for (int j = 0; j < 16; ++j) mu_dot = __builtin_fmaf(mo[j], x[j], mu_dot);
             mu_dot += __shfl_xor(mu_dot, 1, 64);
             mu_dot += __shfl_xor(mu_dot, 2, 64);
             if (g == 0) a.bias[(size_t)bh * a.T * BLK + tok] = (valid && a.smooth_q) ? mu_dot * SCORE_SCALE_LOG2 : 0.0f;
