@@ -64,24 +64,31 @@ __global__ __launch_bounds__(256) void k_colsum(const uint16_t* __restrict__ q,
     const int tr = threadIdx.x / 8;           // 32 token rows
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const int t0 = chunk * SUM_CHUNK;
-    for (int s = 0; s < SUM_CHUNK / 32; ++s) {
+    // all of this thread's rows in flight at once, then the sums in row order
+    constexpr int ROWS = SUM_CHUNK / 32;
+    uint4 u[ROWS];
+    float rr[ROWS];
+#pragma unroll
+    for (int s = 0; s < ROWS; ++s) {
         const int tok = t0 + tr + 32 * s;
-        if (tok < N) {
-            const uint4 u = *(const uint4*)(src + (size_t)tok * HD + 8 * g);
-            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-            if (rn) {
-                const float rr = rn[rbase + tok];
+        u[s] = tok < N ? *(const uint4*)(src + (size_t)tok * HD + 8 * g) : make_uint4(0, 0, 0, 0);
+        rr[s] = (rn && tok < N) ? rn[rbase + tok] : 0.0f;
+    }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] += (double)qk_normed(w[j] & 0xFFFFu, rr);
-                    acc[2 * j + 1] += (double)qk_normed(w[j] >> 16, rr);
-                }
-            } else {
+    for (int s = 0; s < ROWS; ++s) {
+        if (t0 + tr + 32 * s >= N) continue;   // past the last token: nothing added (not even +0)
+        const uint32_t w[4] = {u[s].x, u[s].y, u[s].z, u[s].w};
+        if (rn) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[2 * j] += (double)bf16_to_f32(w[j] & 0xFFFFu);
-                    acc[2 * j + 1] += (double)bf16_to_f32(w[j] >> 16);
-                }
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += (double)qk_normed(w[j] & 0xFFFFu, rr[s]);
+                acc[2 * j + 1] += (double)qk_normed(w[j] >> 16, rr[s]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] += (double)bf16_to_f32(w[j] & 0xFFFFu);
+                acc[2 * j + 1] += (double)bf16_to_f32(w[j] >> 16);
             }
         }
     }
