@@ -113,7 +113,16 @@ __global__ __launch_bounds__(128) void k_means(const double* __restrict__ sums, 
     if (on) {
         double s = 0.0;
         const double* p = sums + ((size_t)bh * 2 + tensor) * nchunk * HD + c;
-        for (int i = 0; i < nchunk; ++i) s += p[(size_t)i * HD];
+        // sixteen partial sums in flight at a time, added in chunk order
+        constexpr int BATCH = 16;
+        for (int i0 = 0; i0 < nchunk; i0 += BATCH) {
+            double v[BATCH];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) v[j] = i0 + j < nchunk ? p[(size_t)(i0 + j) * HD] : 0.0;
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j)
+                if (i0 + j < nchunk) s += v[j];
+        }
         m = (float)(s / (double)N);
     }
     (tensor == 0 ? mu_k : mu_q)[(size_t)bh * HD + c] = m;
