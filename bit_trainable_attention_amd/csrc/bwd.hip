@@ -206,8 +206,10 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
         for (int r = 0; r < 16; ++r) {
             float pv = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[qb][r], sc, corr[qb][r]));
             if (MASK) {
+                // a select, not a branch around each exp
+                asm volatile("" : "+v"(pv));
                 const int q = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
-                if (key >= N || (CAUSAL && key > q)) pv = 0.0f;
+                pv = (key >= N || (CAUSAL && key > q)) ? 0.0f : pv;
             }
             p[qb][r] = pv;
         }
@@ -354,7 +356,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         float dsm = 0.0f;
         if (active) {
             float sP, invP;
-            block_scale(__builtin_fmaxf(sm.red[0][wave], sm.red[0][wave ^ 1]), sP, invP);
+            // both partial maxima are >= 0: the larger is the larger bit pattern
+            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[0][wave]), __float_as_uint(sm.red[0][wave ^ 1]))),
+                        sP, invP);
             // dV += s_P s_dO (P codes^T dO codes)
             v4i pc[2];
 #pragma unroll
@@ -411,7 +415,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         lds_barrier();
         if (active) {
             float sdS, invdS;
-            block_scale(__builtin_fmaxf(sm.red[1][wave], sm.red[1][wave ^ 1]), sdS, invdS);
+            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[1][wave]), __float_as_uint(sm.red[1][wave ^ 1]))),
+                        sdS, invdS);
             if (DUMP && dp) {
                 if (lane == 0 && kh == 0) dump_at<float>(dp, dumpoff::SC)[1] = sdS;
 #pragma unroll
@@ -781,8 +786,9 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
         for (int r = 0; r < 16; ++r) {
             float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[qb][r], SCORE_SCALE_LOG2, corr[qb][r]));
             if (MASK) {
+                asm volatile("" : "+v"(pv));   // a select, not a branch around each exp
                 const int qq = i * BLK + 32 * qb + 8 * (r / 4) + 4 * h + (r % 4);
-                if (key >= N || (CAUSAL && key > qq)) pv = 0.0f;
+                pv = (key >= N || (CAUSAL && key > qq)) ? 0.0f : pv;
             }
             p[qb][r] = pv;
         }
