@@ -100,14 +100,21 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// Workgroup -> (head, group) as in the forward: the groups of a head share an
-// XCD when the head count allows.  first_small selects the order of groups
-// within a head (smallest index first for the key-block kernel, whose causal
-// work is largest at small key blocks).
-__device__ __forceinline__ void map_group_bwd(int ngroups, int BH, bool first_small, int& bh, int& g) {
+// Workgroup -> (head, group) as in the forward: causal grids deal the
+// longest group of every head first (longest_first), others keep the groups
+// of a head on one XCD when the head count allows.  first_small selects which
+// groups are longest (smallest index first for the key-block kernel, whose
+// causal work is largest at small key blocks).
+__device__ __forceinline__ void map_group_bwd(int ngroups, int BH, bool first_small, int& bh, int& g,
+                                              bool longest_first = false) {
     const int L = blockIdx.x;
     int s_in_head;
-    if ((BH & 7) == 0) {
+    if (longest_first) {
+        // every head's largest group first, then the next: the longest
+        // causal work starts earliest; head bh still runs on XCD bh % 8
+        bh = L % BH;
+        s_in_head = L / BH;
+    } else if ((BH & 7) == 0) {
         const int xcd = L & 7, s = L >> 3;
         bh = (s / ngroups) * 8 + xcd;
         s_in_head = s % ngroups;
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
     int bh, g;
-    map_group_bwd(a.ngroups, a.BH, true, bh, g);
+    map_group_bwd(a.ngroups, a.BH, true, bh, g, CAUSAL);
     const int T = a.T;
     const int kvb = 2 * g + wave / 2, kh = wave % 2;
     const bool live = kvb < T;
@@ -626,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
               l32 = lane % 32;
     const int T = a.T;
     int bh, g;
-    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g);
+    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g, CAUSAL);
     const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
     const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);   // waves past T only help stage K^T
     const bool live = DQ_BLOCKS_PER_WG * g + wave < T;
@@ -801,7 +808,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
     int bh, g;
-    map_group_bwd(a.ngroups, a.BH, true, bh, g);
+    map_group_bwd(a.ngroups, a.BH, true, bh, g, CAUSAL);
     const int T = a.T;
     const int kvb = 2 * g + wave / 2, kh = wave % 2;
     const bool live = kvb < T;
@@ -994,7 +1001,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_mx(BwdArgs a) {
               l32 = lane % 32;
     const int T = a.T;
     int bh, g;
-    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g);
+    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g, CAUSAL);
     const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
     const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);
     const bool live = DQ_BLOCKS_PER_WG * g + wave < T;

@@ -31,11 +31,18 @@ struct FwdSmem {
 };
 
 // Workgroup -> (head, query group).  Consecutive workgroup ids are dealt to
-// the 8 XCDs in turn; when the head count allows, all groups of a head go to
-// the same XCD.  Within a head the longest causal rows come first.
-__device__ __forceinline__ void map_group(int ngroups, int BH, int& bh, int& g) {
+// the 8 XCDs in turn.  Causal (longest_first): the longest group of every
+// head, then the next longest of every head, and so on, so that the longest
+// work starts first across the whole grid (head bh stays on XCD bh % 8 when
+// the head count is a multiple of 8); dispatching head by head left some of
+// the longest groups to start near the end.  Otherwise all groups of a head
+// go to the same XCD when the head count allows.
+__device__ __forceinline__ void map_group(int ngroups, int BH, int& bh, int& g, bool longest_first = false) {
     const int L = blockIdx.x;
-    if ((BH & 7) == 0) {
+    if (longest_first) {
+        bh = L % BH;
+        g = ngroups - 1 - L / BH;
+    } else if ((BH & 7) == 0) {
         const int xcd = L & 7, s = L >> 3;
         bh = (s / ngroups) * 8 + xcd;
         g = ngroups - 1 - (s % ngroups);
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
-    map_group(a.ngroups, a.BH, bh, g);
+    map_group(a.ngroups, a.BH, bh, g, CAUSAL);
     const int T = a.T;
     const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
     const bool live = qblk < T;
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
-    map_group(a.ngroups, a.BH, bh, g);
+    map_group(a.ngroups, a.BH, bh, g, CAUSAL);
     const int T = a.T;
     const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
     const bool live = qblk < T;
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     __shared__ FwdFp4Smem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
-    map_group(a.ngroups, a.BH, bh, g);
+    map_group(a.ngroups, a.BH, bh, g, CAUSAL);
     const int T = a.T;
     const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
     const bool live = qblk < T;
