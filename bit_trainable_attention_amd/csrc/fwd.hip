@@ -22,6 +22,12 @@
 namespace sagebwd {
 
 constexpr int FWD_WAVES = 4;
+// Compile-time flag passed to the loop-step lambdas below.
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
 constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 units; O and L may grow by up to 2^8
 
 struct FwdSmem {
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     float L = 0.0f;                // sum over tiles of exp2(m_t - M) * (code sum of this half-wave)
     v16f O[2] = {v16f{}, v16f{}};  // [db]: lane = query, registers = channels
 
-    for (int t = 0; t <= t_last_wg; ++t) {
+    auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
         if (more) {
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
             const float sc = tile_scale(sQ, a.sk[bt + t]);
             const float sv = a.sv[bt + t];
             uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
-            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+            if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
                 fwd_tile<CAUSAL, SMOOTHQ, true, DUMP>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O, dp,
                                                       32 * qhalf + l32);
             else
@@ -230,7 +236,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
             if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
         }
         __syncthreads();
-    }
+    };
+    // Only the last two steps can hold a masked tile (the causal diagonal
+    // and the ragged last key block come last), so they run in a loop of
+    // their own: the main loop then carries one form of the tile and the
+    // compiler keeps O in the same registers across it (with both forms in
+    // the loop it copied O between them on every step).
+    const int t_tail = t_last_wg > 1 ? t_last_wg - 1 : 0;
+    int t = 0;
+    for (; t < t_tail; ++t) step(t, Flag<false>{});
+    for (; t <= t_last_wg; ++t) step(t, Flag<true>{});
 
     // epilogue: O / L in bf16; LSE in natural log of the un-smoothed scores
     if (live && q < a.N) {
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     v16f O[2] = {v16f{}, v16f{}};  // [db]: lane = query, registers = channels
     v16f Lacc = v16f{};            // register 0: the row sum of the dequantized P~
 
-    for (int t = 0; t <= t_last_wg; ++t) {
+    auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
         if (more) {
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
         }
         if (live && t <= t_last) {
             const uint32_t sk_w = skw[t], sv_w = svw[t];
-            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+            if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
                 fwd_tile_mx<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O, Lacc,
                                                    ones, e_one, e_pt);
             else
@@ -417,7 +432,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
             if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
         }
         __syncthreads();
-    }
+    };
+    // Only the last two steps can hold a masked tile (the causal diagonal
+    // and the ragged last key block come last), so they run in a loop of
+    // their own: the main loop then carries one form of the tile and the
+    // compiler keeps O in the same registers across it (with both forms in
+    // the loop it copied O between them on every step).
+    const int t_tail = t_last_wg > 1 ? t_last_wg - 1 : 0;
+    int t = 0;
+    for (; t < t_tail; ++t) step(t, Flag<false>{});
+    for (; t <= t_last_wg; ++t) step(t, Flag<true>{});
 
     if (live && q < a.N) {
         const float Lt = Lacc[0];
@@ -577,7 +601,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     v16f O[2] = {v16f{}, v16f{}};
     v16f Lacc = v16f{};
 
-    for (int t = 0; t <= t_last_wg; ++t) {
+    auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
         if (more && loader) {
@@ -586,7 +610,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
         }
         if (more && SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
         if (live && t <= t_last) {
-            if ((CAUSAL && t == qblk) || (ragged && t == T - 1))
+            if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
                 fwd_tile_fp4<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
             else
                 fwd_tile_fp4<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
@@ -599,7 +623,16 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
             if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
         }
         __syncthreads();
-    }
+    };
+    // Only the last two steps can hold a masked tile (the causal diagonal
+    // and the ragged last key block come last), so they run in a loop of
+    // their own: the main loop then carries one form of the tile and the
+    // compiler keeps O in the same registers across it (with both forms in
+    // the loop it copied O between them on every step).
+    const int t_tail = t_last_wg > 1 ? t_last_wg - 1 : 0;
+    int t = 0;
+    for (; t < t_tail; ++t) step(t, Flag<false>{});
+    for (; t <= t_last_wg; ++t) step(t, Flag<true>{});
 
     if (live && q < a.N) {
         const float Lt = Lacc[0];
