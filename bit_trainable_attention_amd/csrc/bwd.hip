@@ -14,9 +14,10 @@
 //               so P and dS codes leave the accumulator as the A operand of
 //               P^T dO and dS^T Q (contraction over queries).  It also stores
 //               every tile's dS codes and scale in the workspace.
-//   k_bwd_dq    each wave owns 32 queries and streams the stored dS codes of
-//               its query block: dQ = sum_t s_dS s_K (dS codes K codes), with
-//               no recomputation of S, P or dS.
+//   k_bwd_dq    each wave owns one 64-query block and streams its stored dS
+//               codes: dQ = sum_t s_dS s_K (dS codes K codes), with no
+//               recomputation of S, P or dS; the four waves of a workgroup
+//               share each key block's K^T codes through LDS.
 // A 64x64 quantization tile of P or dS is held by a pair of waves, which
 // exchange their partial maxima through LDS.  The streamed operand tiles go
 // through double-buffered LDS, fetched one step ahead; FP16 rows are stored
@@ -143,7 +144,8 @@ struct DkdvSmem {
 // formed on the FP32 MFMA (32x32x2: lane l carries A[l%32][l/32] and
 // B[l/32][l%32]) in the accumulator layout of the score product, so each score
 // costs one FMA before its exp.  MASK only on the causal diagonal tile and the
-// ragged last key block, so the common path carries no per-element selects.
+// ragged last key block, so the common path carries no per-element selects
+// (a masked P is a select after its exp, not a branch around it).
 // dP - Delta (the same layout) is formed here too: it does not depend on P, so
 // its MFMAs are scheduled one by one between groups of the score arithmetic
 // instead of stalling the wave later.

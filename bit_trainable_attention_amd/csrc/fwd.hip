@@ -13,10 +13,12 @@
 // from there (16 bytes per lane per 32x32 operand).  Computing S^T rather than
 // S puts one query per lane column, so every softmax row statistic lives in
 // one lane and its partner in the other half-wave, and the P~ codes leave the
-// accumulator already in the B-operand layout of V^T P~^T.  At most 256
-// registers per wave keep two waves resident per SIMD.  Workgroups of one
-// head are dealt to one XCD (its K/V codes then stay in that XCD's L2),
-// longest causal rows first.
+// accumulator already in the B-operand layout of V^T P~^T.  Every kernel
+// stays within 256 registers per wave (at least two waves per SIMD; the
+// causal INT8 kernel needs 126, so four fit).  Causal grids start the longest
+// query groups of all heads first; non-causal ones deal the workgroups of one
+// head to one XCD when the head count allows (its K/V codes then stay in
+// that XCD's L2).
 #include "attn.h"
 
 namespace sagebwd {
