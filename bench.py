@@ -124,7 +124,7 @@ def main():
                     help="run one plain device copy of this size before timing (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "heads shard across GPUs without communication, but no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
 
