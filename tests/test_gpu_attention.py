@@ -184,6 +184,30 @@ def test_qk_norm_parity(w):
             assert np.linalg.norm(a) <= 1e-2 * max(np.linalg.norm(g[2]), 1e-30), name
 
 
+@pytest.mark.parametrize("w", QK_SMALL[:2], ids=_ids(QK_SMALL[:2]))
+def test_qk_norm_int8_dp_parity(w):
+    """The two options together: fused QK-norm with the all-INT8 dO V^T, end
+    to end against the oracle with both (same bars)."""
+    print(f"[qk_norm int8_dp] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, w.smooth_q, w.smooth_k, qk_norm=True, int8_dp=True)
+    torch.cuda.synchronize()
+    g = [G.host_f32(t) for t in (dq, dk, dv)]
+    o_f, lse_f = F.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k, qk_norm=True)
+    ref = F.bwd(f32["q"], f32["k"], f32["v"], _bf16(o_f), lse_f.astype(np.float32), f32["do"], w.causal,
+                w.smooth_q, w.smooth_k, qk_norm=True, int8_dp=True)
+    ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal, qk_norm=True)
+    for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
+        assert np.all(np.isfinite(a)), name
+        print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
+        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
+        if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+
+
 def test_zero_inputs():
     z = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16, device="cuda")
     for causal in (False, True):
