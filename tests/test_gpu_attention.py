@@ -220,16 +220,17 @@ def test_zero_inputs():
         assert torch.allclose(lse[0, 0], torch.log(n), atol=1e-5)
 
 
-@pytest.mark.parametrize("qk_norm", [False, True], ids=["plain", "qknorm"])
-def test_autograd_wrapper(qk_norm):
+@pytest.mark.parametrize("qk_norm,mxfp8", [(False, False), (True, False), (False, True)],
+                         ids=["plain", "qknorm", "mxfp8"])
+def test_autograd_wrapper(qk_norm, mxfp8):
     w = W.custom(1, 1, 96, True, True, True, "rowscale" if qk_norm else "kbias", 59)
     x = W.make_inputs(w)
     q, k, v = (G.dev(x[n]).requires_grad_(True) for n in ("q", "k", "v"))
-    o = sb.SageBwdAttention.apply(q, k, v, True, True, True, qk_norm)
+    o = sb.SageBwdAttention.apply(q, k, v, True, True, True, qk_norm, mxfp8)
     o.backward(G.dev(x["do"]))
     dq, dk, dv = sb.bwd(q.detach(), k.detach(), v.detach(),
-                        *sb.fwd(q.detach(), k.detach(), v.detach(), True, True, True, qk_norm=qk_norm),
-                        G.dev(x["do"]), True, True, True, qk_norm=qk_norm)
+                        *sb.fwd(q.detach(), k.detach(), v.detach(), True, True, True, qk_norm=qk_norm, mxfp8=mxfp8),
+                        G.dev(x["do"]), True, True, True, qk_norm=qk_norm, mxfp8=mxfp8)
     torch.cuda.synchronize()
     for a, b in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
         assert torch.equal(a, b)
