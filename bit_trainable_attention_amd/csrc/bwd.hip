@@ -53,20 +53,23 @@ __device__ __forceinline__ float half_sum32(float v) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Maximum over the 64 lanes of a wave of non-negative floats, returned in
-// every lane.  Non-negative floats order like their bit patterns, so the
-// reduction runs on unsigned integers: DPP within each 16-lane row, then the
-// row-pair and half-wave swaps.
+// Maximum over the 64 lanes of a wave of non-negative floats, returned as a
+// uniform value.  Non-negative floats order like their bit patterns, so the
+// reduction runs on unsigned integers: DPP within each 16-lane row, then two
+// DPP row broadcasts that leave the maximum in lane 63, read once.
 __device__ __forceinline__ float wave_max64(float f) {
     uint32_t v = __float_as_uint(f);
     v = umax(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
     v = umax(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
     v = umax(v, dppu<0x141>(v));   // row_half_mirror
     v = umax(v, dppu<0x140>(v));   // row_mirror
-    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    v = umax(v, umax(s[0], s[1]));
-    const auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return __uint_as_float(umax(v, umax(t[0], t[1])));
+    // every lane of a row holds the row's maximum; row_bcast:15 folds row 0
+    // into row 1 and row 2 into row 3, row_bcast:31 row 1 into rows 2 and 3,
+    // so lane 63 ends with the wave's maximum (rows outside the row mask keep
+    // their own value)
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    return __uint_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
 // Four signed codes rne(x * inv) packed into one dword.
