@@ -112,8 +112,10 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
     }
     float mx = max3f(m0, m1, m1);
     {
+        // after the swap the two registers hold, in every lane, this lane's
+        // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
     }
     // tile-row max in log2 units; the code is rne(127 * exp2(score - max))
     const float mt = SMOOTHQ ? mx : mx * sc;
@@ -326,8 +328,10 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
     }
     float mx = max3f(m0, m1, m1);
     {
+        // after the swap the two registers hold, in every lane, this lane's
+        // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
     }
     // running maximum (log2 units); O and l follow it.  The rescale runs for
     // the whole wave when any of its rows rises (factor 1 for the others), so
@@ -521,8 +525,10 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
     }
     float mx = max3f(m0, m1, m1);
     {
+        // after the swap the two registers hold, in every lane, this lane's
+        // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(mx, __uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
     }
     const float mt = mx;
     const bool rise = mt > M;
