@@ -67,8 +67,8 @@ __device__ __forceinline__ float wave_max64(float f) {
     // into row 1 and row 2 into row 3, row_bcast:31 row 1 into rows 2 and 3,
     // so lane 63 ends with the wave's maximum (rows outside the row mask keep
     // their own value)
-    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
-    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
     return __uint_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 

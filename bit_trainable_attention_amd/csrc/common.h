@@ -213,7 +213,6 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
-__device__ __forceinline__ float half_swap(float v) { return __shfl_xor(v, 32, 64); }
 
 // Byte offsets of element (token r, channel c) inside a 64x64 code block.
 __host__ __device__ constexpr int row_operand_offset(int r, int c) {
