@@ -28,10 +28,10 @@ CASES = [
 ]
 
 
-def _run(w, heads, int8_dp=False, qk_norm=False):
+def _run(w, heads, int8_dp=False, qk_norm=False, x=None):
     print(f"[prepare] {w.name} B{w.B} H{w.H} N{w.N} causal={w.causal} sq={w.smooth_q} sk={w.smooth_k} "
           f"int8_dp={int8_dp} qk_norm={qk_norm}", flush=True)
-    x = W.make_inputs(w)
+    x = W.make_inputs(w) if x is None else x
     r = np.random.default_rng(5)
     o_bits = W.f32_to_bf16_bits(r.standard_normal(x["q"].shape).astype(np.float32))
     lse = (r.standard_normal(x["q"].shape[:3]) * 3 + 5).astype(np.float32)
@@ -154,3 +154,27 @@ def test_prepare_zero_inputs():
         assert np.all(G.region(wsh, p, n, np.float32) == 0)
     for n in ("Q_R", "K_R", "V_T", "Q_T", "K_T", "DO_T"):
         assert np.all(G.region(wsh, p, n, np.int8) == 0)
+
+
+def test_prepare_extreme_block_magnitudes():
+    """Blocks of Q and K whose absmax a runs from below the all-zero
+    threshold 2^-100 up past 2^126 (where the reciprocal of a is subnormal),
+    each block scaled by its own power of two: codes and scales (s = a
+    fp32(1/127), inv = fp32(127/a)) bit-exact with the oracle at every
+    magnitude.  V goes as low but stops at 2^10 (its FP16 copy stays finite),
+    and dO stays at unit scale, so Delta stays finite."""
+    exps = [125, 124, 100, 31, 0, -17, -64, -98, -100, -101, -103, 3]
+    N = 64 * len(exps) - 20                                  # ragged last block
+    w = W.custom(1, 1, N, False, False, False, "normal", 46)
+    r = np.random.default_rng(46)
+    scale = np.repeat(np.exp2(np.asarray(exps, np.float64)), 64)[:N, None]
+    x = {}
+    for n in ("q", "k", "v"):
+        v = r.standard_normal((1, 1, N, 64)) * (np.minimum(scale, 2.0 ** 10) if n == "v" else scale)
+        x[n] = W.f32_to_bf16_bits(np.clip(v, -3.0e38, 3.0e38).astype(np.float32))
+    x["do"] = W.f32_to_bf16_bits(r.standard_normal((1, 1, N, 64)).astype(np.float32))
+    f = W.bf16_bits_to_f32(x["q"])[0, 0]
+    amax = np.array([np.abs(f[i:i + 64]).max() for i in range(0, N, 64)])
+    assert np.isfinite(f).all() and amax.max() >= 2.0 ** 126                # the pre-scaled range is reached
+    assert (amax < 2.0 ** -100).any() and ((amax >= 2.0 ** -100) & (amax < 2.0 ** -99)).any()
+    _run(w, None, x=x)
