@@ -21,7 +21,8 @@ with its reason, in the design notes that ship with the library):
   F2  centring         x~ = fp32(x - mu)                (IEEE float32)
   F3  block quantizer  per block of 64 tokens x 64 channels, valid rows only:
                          a = max|x~|;  a < 2^-100 -> s = 0, all codes 0;
-                         else s = fp32(a * fp32(1/127)), inv = fp32(127 / a),
+                         else s = fp32(a / 127), inv = fp32(127 / a) (both
+                         correctly rounded quotients),
                          code = round_half_even(x~ * inv)  (exact product)
       giving codes in [-127, 127] and one float32 scale per block.
   F4  Q-smoothing bias b_j = mu_q . (s_K,t K_code_j): with it the score is the
@@ -77,7 +78,6 @@ D = 64                   # head dimension
 SCALE = 1.0 / 8.0        # 1/sqrt(64), exact
 A_MIN = 2.0 ** -100      # absmax below this -> an all-zero block
 _F127 = np.float32(127.0)
-_R127 = np.float32(1.0) / _F127          # correctly rounded float32 of 1/127
 
 
 # ---------------------------------------------------------------- F0
@@ -145,7 +145,8 @@ def block_scale(a, rounding: bool = True):
         a = np.float32(a)
         if not (a >= A_MIN):
             return np.float32(0.0), np.float32(0.0)
-        return np.float32(a * _R127), np.float32(_F127 / a)
+        # IEEE float32 divisions: the correctly rounded a/127 and 127/a
+        return np.float32(a / _F127), np.float32(_F127 / a)
     a = float(a)
     if a == 0.0:
         return 0.0, 0.0

@@ -134,9 +134,16 @@ def quantize_groups(x, rounding: bool = True):
     return codes * np.ldexp(1.0, e)[..., None], e, codes
 
 
-def key_class_order() -> np.ndarray:
-    """[2, 32]: the keys of key class h of a 64-key tile, in increasing order."""
+def key_class_order(partition: str = "class") -> np.ndarray:
+    """[2, 32]: the keys of key class h of a 64-key tile, in increasing order.
+    partition "class": class h = (key mod 8) div 4 (the blocks the GPU forms
+    in its score accumulators); "contiguous": keys 32h .. 32h + 31, kept as a
+    reference partition for the accuracy comparison of the two."""
     k = np.arange(BLK)
+    if partition == "contiguous":
+        return np.stack([k[k // 32 == h] for h in (0, 1)])
+    if partition != "class":
+        raise ValueError(partition)
     return np.stack([k[(k % 8) // 4 == h] for h in (0, 1)])
 
 
@@ -150,14 +157,14 @@ def quantize_rows(x, nrows: int, rounding: bool = True):
     return deq.reshape(x.shape), e
 
 
-def quantize_v(v, nrows: int, rounding: bool = True):
+def quantize_v(v, nrows: int, rounding: bool = True, partition: str = "class"):
     """V [Np, 64]: for each channel, the 32 keys of each key class of each
     64-key tile.  Returns (dequantized [Np, 64], exponents [T, 2, 64] as
     (tile, class, channel))."""
     v = np.array(v, np.float64)
     v[nrows:] = 0.0
     T = v.shape[0] // BLK
-    cls = key_class_order()
+    cls = key_class_order(partition)
     g = v.reshape(T, BLK, D)[:, cls, :]                        # [T, 2, 32, 64]
     deq, e, _ = quantize_groups(np.swapaxes(g, 2, 3), rounding)  # blocks along the 32 keys
     out = np.zeros((T, BLK, D))
@@ -182,9 +189,11 @@ class Prepared:
     b: np.ndarray        # [Np] Q-smoothing bias
     corr: np.ndarray     # [Np]
     rounding: bool
+    partition: str = "class"   # the key partition of the P~ and V blocks (key_class_order)
 
 
-def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_norm: bool = False) -> Prepared:
+def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_norm: bool = False,
+            partition: str = "class") -> Prepared:
     """Y1-Y3 for one head (q, k, v: [N, 64] arrays of bf16 values)."""
     fp = _F.prepare(q, k, v, smooth_q, smooth_k, rounding, qk_norm)    # F0-F2 and the means
     N, T = fp.N, fp.T
@@ -202,9 +211,9 @@ def prepare(q, k, v, smooth_q: bool, smooth_k: bool, rounding: bool = True, qk_n
     qh, eq = quantize_rows(centre(fp.q_raw, fp.mu_q), N, rounding)
     kt = centre(fp.k_in, fp.mu_k)
     kh, ek = quantize_rows(kt, N, rounding)
-    vh, ev = quantize_v(centre(v, np.zeros(D, dt)), N, rounding)
+    vh, ev = quantize_v(centre(v, np.zeros(D, dt)), N, rounding, partition)
     b = np.asarray(kt, np.float64) @ np.asarray(fp.mu_q, np.float64)
-    return Prepared(N, T, fp.mu_q, fp.mu_k, qh, kh, vh, eq, ek, ev, b, fp.corr, rounding)
+    return Prepared(N, T, fp.mu_q, fp.mu_k, qh, kh, vh, eq, ek, ev, b, fp.corr, rounding, partition)
 
 
 # ---------------------------------------------------------------- Y5-Y6
@@ -217,7 +226,7 @@ def fwd_head(pp: Prepared, causal: bool, qblocks=None, chunk_blocks: int = 4, p_
     T = pp.T
     qblocks = list(range(T)) if qblocks is None else list(qblocks)
     cols = np.arange(T * BLK)
-    cls = key_class_order()
+    cls = key_class_order(pp.partition)
     vb = pp.vh.reshape(T, BLK, D)
     oo, ll, pq, ee, mm = [], [], [], [], []
     for c0 in range(0, len(qblocks), chunk_blocks):

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import exact
+from oracle import exact, metrics as M
 
 
 def _rand(n, d, seed, scale=1.0):
@@ -178,3 +178,28 @@ def test_sampled_matches_dense_qk_norm(causal):
     assert np.max(np.abs(dq - g[0][qr])) < 1e-13
     assert np.max(np.abs(dk - g[1][kr])) < 1e-13
     assert np.max(np.abs(dv - g[2][kr])) < 1e-13
+
+
+def test_worst_row_and_tile_metrics():
+    """The local error metrics the GPU parity tests use next to rel-L2: one
+    wrong row among many is invisible in a whole-tensor rel-L2 below 1e-2 but
+    shows as a relative error of 1 in its row and at least 1/8 in its tile;
+    rows that are zero in the reference are measured against the floor."""
+    r = np.random.default_rng(5)
+    ref = r.standard_normal((2, 3, 16384, 64))
+    x = ref * (1 + 1e-3 * r.standard_normal(ref.shape))
+    assert M.rel_l2(x, ref) < 2e-3 and M.worst_row_rel(x, ref) < 1e-2 and M.worst_tile_rel(x, ref) < 4e-3
+    bad = x.copy()
+    bad[1, 2, 777] = 0.0                              # one dropped row
+    assert M.rel_l2(bad, ref) < 1e-2
+    assert M.worst_row_rel(bad, ref) > 0.9 and M.worst_tile_rel(bad, ref) > 0.12
+    z = ref.copy()
+    z[0, 0, 5] = 0.0
+    xz = z.copy()
+    xz[0, 0, 5, 0] = 1e-3                            # residue on a zero reference row
+    assert M.worst_row_rel(xz, z) < 1e-2
+    # ragged tiles: the last tile of 48 rows is its own tile
+    a = r.standard_normal((112, 64))
+    b = a.copy()
+    b[100:] += 1.0
+    assert M.worst_tile_rel(b, a) > 0.45 and M.worst_tile_rel(b[:64], a[:64]) == 0.0

@@ -83,29 +83,97 @@ def _f32_round(fr: Fraction) -> Fraction:
 
 def test_quantizer_matches_exact_rationals():
     """Scale, inverse and codes re-derived with exact rationals, with float32
-    rounding done by hand, agree bit for bit with the float32 route.  The
-    scale is absmax times the float32 of 1/127 (one rounded multiply), which
-    stays within one float32 ulp of absmax/127; the inverse is the correctly
-    rounded 127/absmax."""
-    r127 = _f32_round(Fraction(1, 127))
+    rounding done by hand, agree bit for bit with the float32 route: the scale
+    is the correctly rounded absmax/127 and the inverse the correctly rounded
+    127/absmax (the SageBwd reading of "absmax/127 scales")."""
     r = np.random.default_rng(7)
     n_checked = 0
+    n_shortcut_differs = 0
+    r127 = _f32_round(Fraction(1, 127))
     for trial in range(2000):
         scale = float(np.exp(r.uniform(-12, 6)))
         x = (r.standard_normal(512) * scale).astype(np.float32)
         a = np.max(np.abs(x))
         s, inv = F.block_scale(a)
         fa = Fraction(float(a))
-        s_ref = _f32_round(fa * r127)
+        s_ref = _f32_round(fa / 127)
         inv_ref = _f32_round(Fraction(127) / fa)
         assert Fraction(float(s)) == s_ref
-        assert abs(s_ref - fa / 127) <= fa / 127 * Fraction(1, 2 ** 23)
         assert Fraction(float(inv)) == inv_ref
+        # a planted mistake, the one-multiply a * fp32(1/127), differs from the
+        # quotient on some of these blocks, so this check would catch it
+        n_shortcut_differs += _f32_round(fa * r127) != s_ref
         codes = F.block_codes(x, inv)
         for xi, ci in zip(x.tolist(), codes.tolist()):
             assert ci == max(-127, min(127, _rne(Fraction(xi) * inv_ref)))
             n_checked += 1
     assert n_checked == 2000 * 512        # 1 024 000 values
+    assert n_shortcut_differs > 20
+
+
+def test_block_scale_quotient_exhaustive_binade():
+    """s = fp32(a/127) for every float32 a in [1, 2) (all 2^23 mantissas),
+    against the quotient rounded by hand from an exact integer division: with
+    a = m 2^-23, a/127 = m / (127 2^23); its float32 rounding is read off the
+    integer quotient and remainder of m 2^k / 127.  Division by 127 commutes
+    with scaling by powers of two, so this covers every normal a."""
+    m = np.arange(2 ** 23, dtype=np.int64) + 2 ** 23          # a = m 2^-23 in [1, 2)
+    a = m.astype(np.float32) * np.float32(2.0 ** -23)
+    s = np.array([F.block_scale(v)[0] for v in a[:: 4099]])  # the oracle's route on a sample
+    # exact: a/127 lies in [2^-7, 2^-6) (float32 ulp 2^-30, quotient m 2^7 / 127
+    # in ulps) for m < 127 2^17, else in [2^-6, 2^-5) (ulp 2^-29, m 2^6 / 127)
+    hi = m >= 127 * 2 ** 17
+    sh = np.where(hi, 6, 7)
+    num = m << sh
+    q, rem = num // 127, num % 127
+    up = (2 * rem > 127) | ((2 * rem == 127) & (q % 2 == 1))
+    ref = ((q + up).astype(np.float64) * np.where(hi, 2.0 ** -29, 2.0 ** -30)).astype(np.float32)
+    assert np.array_equal(s, ref[:: 4099])
+    got = (a / np.float32(127.0)).astype(np.float32)          # the oracle's float32 division, all of them
+    assert np.array_equal(got, ref)
+
+
+def _tile_loop(x, rounding=True):
+    """B3/B7 written as a loop over 64x64 tiles of the pinned block_scale and
+    block_codes (a second formulation of quantize_tiles)."""
+    I, J = x.shape[0] // 64, x.shape[1] // 64
+    codes = np.zeros(x.shape)
+    scales = np.zeros((I, J), np.float32)
+    for i in range(I):
+        for j in range(J):
+            t = np.asarray(x[64 * i:64 * i + 64, 64 * j:64 * j + 64], np.float32)
+            s, inv = F.block_scale(np.max(np.abs(t)))
+            scales[i, j] = s
+            codes[64 * i:64 * i + 64, 64 * j:64 * j + 64] = F.block_codes(t, inv)
+    return codes, scales
+
+
+def _planted_per_row(x):
+    """A plausible mistake: one absmax per row of each tile instead of per tile."""
+    codes = np.zeros(x.shape)
+    for r0 in range(0, x.shape[0]):
+        for j in range(x.shape[1] // 64):
+            t = np.asarray(x[r0, 64 * j:64 * j + 64], np.float32)
+            _, inv = F.block_scale(np.max(np.abs(t)))
+            codes[r0, 64 * j:64 * j + 64] = F.block_codes(t, inv)
+    return codes
+
+
+def test_quantize_tiles_against_tile_loop():
+    """quantize_tiles (B3, B7, with rounding) equals the per-tile loop over the
+    pinned scalar quantizer, on signed dS-like and non-negative P-like tiles
+    with exact ties and zero tiles; a per-row absmax would not."""
+    r = np.random.default_rng(11)
+    x = (r.standard_normal((192, 128)) * np.exp(r.uniform(-6, 3, (192, 1)))).astype(np.float32)
+    x[64:128, 64:128] = 0.0                                   # an all-zero tile
+    x[0:64, 0:64] = np.abs(x[0:64, 0:64])                     # a P-like tile
+    x[5, 3] = np.max(np.abs(x[0:64, 0:64])) * 2.5 / 127       # exact-ish ties near 2.5 codes
+    c, s = F.quantize_tiles(x)
+    c_ref, s_ref = _tile_loop(x)
+    assert np.array_equal(s, s_ref)
+    assert np.array_equal(c, c_ref)
+    assert np.max(np.abs(c)) == 127 and np.all(np.abs(c) <= 127)
+    assert not np.array_equal(_planted_per_row(x), c_ref)
 
 
 def test_quantizer_hand_cases():

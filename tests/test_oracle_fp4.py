@@ -162,3 +162,31 @@ def test_accuracy_orderings():
             pp.b = pp.kh @ np.asarray(pp.mu_q, np.float64)                # mu_q . K^ (the 8-bit modes' F4)
             assert M.cos_sim(Y.fwd_head(pp, w.causal)[0][:N], oe) < cos["fp4"] - 0.02, (name, cos)
         print(name, {k: round(v, 5) for k, v in cos.items()})
+
+
+@pytest.mark.slow
+def test_key_class_partition_matches_contiguous_blocks():
+    """Reading Y2/Y5 takes the P~ and V blocks of a 64-key tile as the two key
+    classes (key mod 8) div 4, the keys a half-wave holds in its score
+    accumulators, rather than two contiguous runs of 32 keys.  Both are
+    partitions of the contraction index into blocks of 32; this study shows
+    they are equally accurate: on 1024-token prefixes of three heads each of
+    llama8k, video and pretrain, the cosine to exact attention of the two
+    partitions differs by less than 2e-3 per head, and neither is better on
+    average by more than 1e-3."""
+    diffs = []
+    for name, heads in (("llama8k", ((0, 3), (0, 17), (0, 30))), ("video", ((1, 3), (0, 11), (1, 22))),
+                        ("pretrain", ((0, 0), (3, 7), (7, 15)))):
+        w = W.WORKLOADS[name]
+        for bh in heads:
+            N = 1024
+            f = {k: W.bf16_bits_to_f32(v)[:N] for k, v in W.make_head(w, *bh).items()}
+            oe, _ = exact.fwd(f["q"], f["k"], f["v"], w.causal)
+            c = {}
+            for part in ("class", "contiguous"):
+                pp = Y.prepare(f["q"], f["k"], f["v"], w.smooth_q, w.smooth_k, partition=part)
+                c[part] = M.cos_sim(Y.fwd_head(pp, w.causal)[0][:N], oe)
+            print(name, bh, {k: round(v, 5) for k, v in c.items()})
+            assert abs(c["class"] - c["contiguous"]) < 2e-3, (name, bh, c)
+            diffs.append(c["class"] - c["contiguous"])
+    assert abs(float(np.mean(diffs))) < 1e-3, diffs
