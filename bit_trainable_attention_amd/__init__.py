@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["debug_tile", "DUMP_BYTES", "fwd", "bwd", "fwd_stage", "bwd_stage", "STAGES", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
+__all__ = ["check_block_scale", "debug_tile", "DUMP_BYTES", "fwd", "bwd", "fwd_stage", "bwd_stage", "STAGES", "prepare", "ws_region", "workspace_size", "Params", "SageBwdAttention",
            "SageBwdError", "REGIONS", "load_library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +78,8 @@ def load_library() -> ctypes.CDLL:
         lib.sagebwd_prepare.restype = ctypes.c_int
         lib.sagebwd_ws_region.argtypes = [_P, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
         lib.sagebwd_ws_region.restype = ctypes.c_int
+        lib.sagebwd_check_block_scale.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp]
+        lib.sagebwd_check_block_scale.restype = ctypes.c_int
         lib.sagebwd_status_string.argtypes = [ctypes.c_int]
         lib.sagebwd_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -222,11 +224,12 @@ DEBUG_KERNELS = {"fwd": 0, "dkdv": 1, "dq": 2}
 
 
 def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=False, smooth_q=False,
-               smooth_k=True, int8_dp=False, qk_norm=False, mxfp8=False):
+               smooth_k=True, int8_dp=False, qk_norm=False, mxfp8=False, return_grads=False):
     """Run one attention kernel's debug instantiation and return the raw
     SAGEBWD_DUMP_BYTES dump of tile (bh, qblock, kblock) as a CPU uint8
     tensor (see include/sagebwd.h for the layout).  kernel: "fwd" writes into
-    o and lse; "dkdv" and "dq" read o, lse and do."""
+    o and lse; "dkdv" and "dq" read o, lse and do.  With return_grads, also
+    the (dQ, dK, dV) buffers the backward kernels wrote (None for "fwd")."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
     p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
@@ -240,7 +243,26 @@ def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=Fals
                                 _ptr(dump), DUMP_BYTES, _ptr(ws), ws.numel(), _stream())
     _check(rc, "sagebwd_debug_tile")
     torch.cuda.synchronize()
+    if return_grads:
+        return dump.cpu(), grads
     return dump.cpu()
+
+
+def check_block_scale(e_lo: int, e_hi: int, keep_first: bool = False):
+    """Run the library's exhaustive block-scale check over the exponents
+    [e_lo, e_hi]; returns (mismatches of a/127, mismatches of 127/a), plus
+    with keep_first the fast quotients (a/127, 127/a) of every mantissa of
+    exponent e_lo as CPU float32 tensors."""
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    outs = [torch.empty(1 << 23, dtype=torch.float32, device="cuda") for _ in range(2)] if keep_first else [None, None]
+    rc = load_library().sagebwd_check_block_scale(int(e_lo), int(e_hi), _ptr(counts), _ptr(outs[0]), _ptr(outs[1]),
+                                                  _stream())
+    _check(rc, "sagebwd_check_block_scale")
+    torch.cuda.synchronize()
+    res = tuple(int(c) for c in counts.cpu().tolist())
+    if keep_first:
+        return res + (outs[0].cpu(), outs[1].cpu())
+    return res
 
 
 def ws_region(params: Params, region) -> tuple:

@@ -71,7 +71,7 @@ constexpr double QK_NORM_EPS = 1e-6;
 // up to the largest finite a.  On gfx950 this q equals the correctly rounded
 // quotient for every float32 a in [2^-121, 2^128), which was checked
 // exhaustively (all 2^23 mantissas at every exponent) against the compiled
-// division.
+// division by sagebwd_check_block_scale.
 __device__ __forceinline__ float div127(float a) {
     const float as = a * 0x1p-4f;
     const float y = __builtin_amdgcn_rcpf(as);
@@ -79,12 +79,22 @@ __device__ __forceinline__ float div127(float a) {
     return __builtin_fmaf(__builtin_fmaf(-as, q0, 7.9375f), y, q0);
 }
 
-// Per-block scale from an absmax: s = a * fp32(1/127) (one rounded
-// multiply) and inv = 127/a (correctly rounded float32 division); blocks with
-// a < 2^-100 are all-zero.
+// a/127, correctly rounded, in three VALU instructions: q0 = a RN(1/127),
+// the residual r = a - 127 q0 (exact in one FMA: it is a small multiple of
+// ulp(q0), subnormal near a = 2^-100, which this build keeps), and one fused
+// correction q = q0 + r RN(1/127).  Equal to the correctly rounded quotient
+// for every float32 a in [2^-100, 2^128) (sagebwd_check_block_scale compares
+// all of them with the IEEE division on the GPU).
+__device__ __forceinline__ float quot127(float a) {
+    const float q0 = a * R127;
+    return __builtin_fmaf(__builtin_fmaf(-127.0f, q0, a), R127, q0);
+}
+
+// Per-block scale from an absmax: s = a/127 and inv = 127/a, both the
+// correctly rounded float32 quotients; blocks with a < 2^-100 are all-zero.
 __device__ __forceinline__ void block_scale(float a, float& s, float& inv) {
     if (a >= A_MIN) {
-        s = a * R127;
+        s = quot127(a);
         inv = div127(a);
     } else {
         s = 0.0f;
@@ -203,24 +213,16 @@ constexpr uint32_t E2M1_ONES = 0x22222222u;   // eight E2M1 codes of 1.0
 constexpr int FP4_EXP_OFF = 2048;             // exponent bytes after the codes of an FP4 block
 
 
-// max(a, b, c) and max(a, |b|, |c|) as one v_max3_f32.  fmaxf in IEEE mode
-// makes the compiler quiet every operand it cannot prove canonical (one extra
-// v_max_f32 per value); the operands here are arithmetic results, never
-// signaling NaNs, so the raw instruction gives the same maximum.
-// The compiler does not look inside inline assembly when it inserts the wait
-// states a result needs before a VALU instruction may read it, so operands
-// must never come straight from an MFMA accumulator or from a transcendental
-// instruction (v_exp_f32 and the like): pass them through an ordinary VALU
-// operation first, or reduce with compiler-visible instructions.
+// max(a, b, c) and max(a, |b|, |c|), written so the compiler sees them (it
+// forms v_max3_f32 itself and inserts the wait states an MFMA or
+// transcendental result needs before a VALU instruction reads it).  The
+// operands are arithmetic results, never signaling NaNs, so no quieting is
+// needed; the compiler knows this of the results it can see.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-    float d;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 __device__ __forceinline__ float max_abs2f(float a, float b, float c) {
-    float d;
-    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
+    return __builtin_fmaxf(__builtin_fmaxf(a, __builtin_fabsf(b)), __builtin_fabsf(c));
 }
 
 // Wave-wide reductions (wave64).

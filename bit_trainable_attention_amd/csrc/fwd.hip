@@ -38,6 +38,27 @@ struct FwdSmem {
     float bias[2][64];   // Q-smoothing key bias (log2 domain)
 };
 
+// Maximum of a lane's 32 scores: one chain the compiler turns into v_max3_f32
+// (15 of them and one v_max_f32), starting from the first score.
+__device__ __forceinline__ float row_max32(const float (&z)[2][16]) {
+    float m = __builtin_fmaxf(z[0][0], z[0][1]);
+#pragma unroll
+    for (int i = 2; i < 32; ++i) m = __builtin_fmaxf(m, z[i / 16][i % 16]);
+    return m;
+}
+
+// max of two row maxima that come out of a lane swap (bit patterns of
+// non-NaN floats): the median of (x, y, +inf) is max(x, y) and, unlike
+// fmaxf on values the compiler cannot prove canonical, needs no quieting.
+// (+inf goes through an empty asm so the compiler does not turn the median
+// back into a maximum that it would then quiet; the asm has no side effects
+// and is hoisted out of the loops.)
+__device__ __forceinline__ float max2_swapped(uint32_t x, uint32_t y) {
+    float inf = __builtin_inff();
+    asm("" : "+v"(inf));
+    return __builtin_amdgcn_fmed3f(__uint_as_float(x), __uint_as_float(y), inf);
+}
+
 // Workgroup -> (head, query group).  Consecutive workgroup ids are dealt to
 // the 8 XCDs in turn.  Causal (longest_first): the longest group of every
 // head, then the next longest of every head, and so on, so that the longest
@@ -104,18 +125,12 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
             }
         }
     }
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        m0 = max3f(m0, z[0][r], z[0][r + 1]);
-        m1 = max3f(m1, z[1][r], z[1][r + 1]);
-    }
-    float mx = max3f(m0, m1, m1);
+    float mx = row_max32(z);
     {
         // after the swap the two registers hold, in every lane, this lane's
         // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        mx = max2_swapped(sw[0], sw[1]);
     }
     // tile-row max in log2 units; the code is rne(127 * exp2(score - max))
     const float mt = SMOOTHQ ? mx : mx * sc;
@@ -320,18 +335,12 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
             }
         }
     }
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        m0 = max3f(m0, z[0][r], z[0][r + 1]);
-        m1 = max3f(m1, z[1][r], z[1][r + 1]);
-    }
-    float mx = max3f(m0, m1, m1);
+    float mx = row_max32(z);
     {
         // after the swap the two registers hold, in every lane, this lane's
         // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        mx = max2_swapped(sw[0], sw[1]);
     }
     // running maximum (log2 units); O and l follow it.  The rescale runs for
     // the whole wave when any of its rows rises (factor 1 for the others), so
@@ -517,18 +526,12 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
             }
         }
     }
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        m0 = max3f(m0, z[0][r], z[0][r + 1]);
-        m1 = max3f(m1, z[1][r], z[1][r + 1]);
-    }
-    float mx = max3f(m0, m1, m1);
+    float mx = row_max32(z);
     {
         // after the swap the two registers hold, in every lane, this lane's
         // value and its partner's (lane l ^ 32): their maximum is the row's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        mx = max2_swapped(sw[0], sw[1]);
     }
     const float mt = mx;
     const bool rise = mt > M;

@@ -271,6 +271,20 @@ int sagebwd_prepare(const sagebwd_params* p,
                     void* ws, size_t ws_bytes, void* stream);
 int sagebwd_ws_region(const sagebwd_params* p, int region, size_t* offset, size_t* bytes);
 
+/* sagebwd_check_block_scale checks the quantizers' block-scale arithmetic
+ * (the absmax/127 scale and its inverse of every INT8 block; SageBwd
+ * abstract): for every float32 a = m 2^e, e in [e_lo, e_hi], and all 2^23
+ * mantissas m, it compares the kernels' fast quotients a/127 and 127/a with
+ * the compiled IEEE float32 divisions on the GPU, and adds the numbers of
+ * mismatches to counts[0] (a/127) and counts[1] (127/a), a device array of
+ * two uint64 that the caller zeroes.  With out_s and out_inv (device arrays
+ * of 2^23 floats each, or both NULL) it also writes the two fast quotients
+ * of every mantissa of exponent e_lo, for a check on the host.  Requires
+ * -126 <= e_lo <= e_hi <= 127 (SAGEBWD_ERR_INVALID_ARG otherwise).  The
+ * kernels use these quotients for absmax >= 2^-100 only. */
+int sagebwd_check_block_scale(int e_lo, int e_hi, unsigned long long* counts, float* out_s, float* out_inv,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,3 +51,26 @@ def decode_codes(ws_host, params, name, kind, BH, T) -> np.ndarray:
 def assert_perms_are_bijections():
     for p in _PERMS.values():
         assert np.array_equal(np.sort(p), np.arange(4096))
+
+
+# Bars of the element-wise parity checks (HIP against the oracle of the same
+# mode): whole-tensor relative L2 (the stated tolerance), and the worst single
+# row and worst 64-row tile, so that one wrong row or block cannot hide in the
+# whole-tensor norm.  The 8-bit-float and FP4 modes allow more per row: one P~
+# code that lands on the neighbouring E4M3 / E2M1 value (the two sides round
+# scores differently) moves that key's weight by up to 1/16 (1/4).
+BARS = {"int8": (1e-2, 3e-2, 1.5e-2), "mxfp8": (1e-2, 0.15, 0.05), "fp4": (1e-2, 0.3, 0.1)}
+
+
+def parity(name, got, ref, mode="int8", where=""):
+    """Assert HIP output ``got`` against the oracle's ``ref`` ([..., rows, 64]
+    arrays) within the mode's bars; returns and prints the three measures."""
+    from oracle import metrics as M
+    rel, row, tile = BARS[mode]
+    r = {"rel_l2": M.rel_l2(got, ref), "worst_row": M.worst_row_rel(got, ref), "worst_tile": M.worst_tile_rel(got, ref)}
+    print(f"  {name}{where}: rel-L2 {r['rel_l2']:.2e}  worst row {r['worst_row']:.2e}  worst tile "
+          f"{r['worst_tile']:.2e}", flush=True)
+    assert r["rel_l2"] <= rel, (name, r)
+    assert r["worst_row"] <= row, (name, r)
+    assert r["worst_tile"] <= tile, (name, r)
+    return r

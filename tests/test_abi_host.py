@@ -231,3 +231,13 @@ def test_backward_head_groups(lib, B, H, N, causal):
     if count > 1:
         assert b(3) == UNSUPPORTED and b(4) == UNSUPPORTED
     assert (count > 1) == ((B, H, N) in ((2, 30, 17776), (1, 4, 1 << 18)))
+
+
+def test_block_scale_check_validation(lib):
+    """The block-scale self-check rejects exponent ranges outside the normal
+    float32 range, reversed ranges, a null counter array and a single output
+    pointer before launching anything."""
+    for lo, hi in ((-127, 0), (0, 128), (5, 4)):
+        assert lib.sagebwd_check_block_scale(lo, hi, FAKE, None, None, None) == INVALID
+    assert lib.sagebwd_check_block_scale(0, 0, None, None, None, None) == INVALID
+    assert lib.sagebwd_check_block_scale(0, 0, FAKE, FAKE, None, None) == INVALID

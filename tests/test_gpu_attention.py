@@ -59,7 +59,7 @@ def test_forward_parity(w):
     assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
     print(f"  O: rel-L2 vs faithful {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}, "
           f"LSE max err {np.max(np.abs(lse_g - lse_f)):.2e}")
-    assert M.rel_l2(o_g, o_f) <= REL_L2, M.rel_l2(o_g, o_f)
+    G.parity("O", o_g, o_f)
     assert np.max(np.abs(lse_g - lse_f)) <= LSE_ATOL
     assert M.cos_sim(o_g, o_e) >= COS_O
     assert np.max(np.abs(lse_g - lse_e)) <= 0.05
@@ -84,10 +84,11 @@ def test_backward_parity(w):
     for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
         assert np.all(np.isfinite(a)), name
         print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
-        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
         if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            G.parity(name, a, b)
             assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
         else:
+            assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
             # degenerate case (one token: dS = 0 exactly, so dQ = dK = 0): the
             # kernel's residue must stay at the size of the O quantization noise
             assert np.linalg.norm(a) <= 1e-2 * max(np.linalg.norm(g[2]), 1e-30), name
@@ -113,9 +114,11 @@ def test_backward_parity_int8_dp(w):
     for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
         assert np.all(np.isfinite(a)), name
         print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
-        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
         if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            G.parity(name, a, b)
             assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+        else:
+            assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
 
 
 @pytest.mark.parametrize("w", SMALL[:4], ids=_ids(SMALL[:4]))
@@ -139,8 +142,8 @@ def test_end_to_end_parity_and_determinism(w):
     o_b = _bf16(o_f)
     ref = F.bwd(f32["q"], f32["k"], f32["v"], o_b, lse_f.astype(np.float32), f32["do"], w.causal,
                 w.smooth_q, w.smooth_k)
-    for a, b in zip(outs[0][1:4], ref):
-        assert M.rel_l2(W.bf16_bits_to_f32(a), b) <= REL_L2
+    for name, a, b in zip(("dQ", "dK", "dV"), outs[0][1:4], ref):
+        G.parity(name, W.bf16_bits_to_f32(a), b)
 
 
 QK_SMALL = [
@@ -171,16 +174,17 @@ def test_qk_norm_parity(w):
     o_e, lse_e = exact.fwd_bh(f32["q"], f32["k"], f32["v"], w.causal, qk_norm=True)
     ex = exact.bwd_bh(f32["q"], f32["k"], f32["v"], f32["do"], w.causal, qk_norm=True)
     print(f"  O: rel-L2 vs faithful {M.rel_l2(o_g, o_f):.2e}, cos vs exact {M.cos_sim(o_g, o_e):.6f}")
-    assert M.rel_l2(o_g, o_f) <= REL_L2
+    G.parity("O", o_g, o_f)
     assert np.max(np.abs(lse_g - lse_f)) <= LSE_ATOL
     assert M.cos_sim(o_g, o_e) >= COS_O
     for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
         assert np.all(np.isfinite(a)), name
         print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
-        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
         if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            G.parity(name, a, b)
             assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
         else:
+            assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
             assert np.linalg.norm(a) <= 1e-2 * max(np.linalg.norm(g[2]), 1e-30), name
 
 
@@ -203,9 +207,11 @@ def test_qk_norm_int8_dp_parity(w):
     for name, a, b, e in zip(("dQ", "dK", "dV"), g, ref, ex):
         assert np.all(np.isfinite(a)), name
         print(f"  {name}: rel-L2 vs faithful {M.rel_l2(a, b):.2e}, cos vs exact {M.cos_sim(a, e):.6f}")
-        assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
         if np.linalg.norm(e) > 1e-9 * max(1.0, np.linalg.norm(b)):
+            G.parity(name, a, b)
             assert M.cos_sim(a, e) >= COS_G, (name, M.cos_sim(a, e))
+        else:
+            assert M.rel_l2(a, b) <= REL_L2, (name, M.rel_l2(a, b))
 
 
 def test_zero_inputs():

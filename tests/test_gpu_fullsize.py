@@ -2,12 +2,16 @@
 times (the whole forward and backward over every head on the GPU, the
 backward reusing the forward's quantized Q and K).
 
-The oracle cannot afford every head of these workloads, so it is run on one
-sampled head per workload: its forward over all query rows of that head (the
-backward of a key block needs every row's O, LSE and Delta), then its
-backward for sampled query blocks (dQ) and key blocks (dK, dV): first, middle
-and last, which covers the causal diagonal and the ragged tail.  Each side
-feeds its own forward into its own backward (end to end)."""
+The oracle cannot afford every head of these workloads, so it runs on sampled
+heads: its forward over all query rows of a head (the backward of a key block
+needs every row's O, LSE and Delta), then its backward for eight sampled
+query blocks (dQ) and key blocks (dK, dV): the first two, four spread over
+the sequence and the last two, which covers causal diagonals, the ragged
+tail and blocks of every length.  Each side feeds its own forward into its
+own backward (end to end).  Every output is checked element-wise: relative L2
+over the sampled rows, and the worst single row and 64-row tile.  The
+headline workload (llama16k) is checked on four heads, one on each of four
+different XCDs (head index mod 8)."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +28,9 @@ CASES = [
     ("pretrain", None, (7, 15), False),
     ("llama8k", None, (0, 17), False),
     ("llama16k", None, (0, 29), False),
+    ("llama16k", None, (0, 2), False),
+    ("llama16k", None, (0, 12), False),
+    ("llama16k", None, (0, 23), False),
     ("video", None, (1, 3), False),
     ("video", False, (0, 11), False),   # the same layer with Q-smoothing off
     ("llama8k", None, (0, 17), True),   # the all-INT8 dO V^T ablation, same head as above
@@ -31,52 +38,52 @@ CASES = [
 
 
 def _blocks(T):
-    return sorted({0, T // 2, T - 1})
+    return sorted({0, min(1, T - 1), T // 5, (2 * T) // 5, (3 * T) // 5, (4 * T) // 5, max(T - 2, 0), T - 1})
 
 
-@pytest.mark.parametrize("name,smooth_q,head,int8_dp", CASES,
-                         ids=[f"{c[0]}{'' if c[1] is None else '_q' + str(int(c[1]))}{'_int8dp' if c[3] else ''}"
-                              for c in CASES])
-def test_fullsize_sampled_parity(name, smooth_q, head, int8_dp):
-    w = W.WORKLOADS[name]
-    sq = w.smooth_q if smooth_q is None else smooth_q
-    b, h = head
-    print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head} int8_dp={int8_dp}",
-          flush=True)
+def _run_gpu(w, sq, int8_dp=False):
     x = W.make_inputs(w)
     tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
     fws = torch.empty(sb.workspace_size(w.B, w.H, w.N, w.causal, sq, w.smooth_k), dtype=torch.uint8, device="cuda")
     o, lse = sb.fwd(tq, tk, tv, w.causal, sq, w.smooth_k, workspace=fws)
     dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, w.causal, sq, w.smooth_k, fwd_workspace=fws, int8_dp=int8_dp)
     torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("name,smooth_q,head,int8_dp", CASES,
+                         ids=[f"{c[0]}_h{c[2][0]}.{c[2][1]}{'' if c[1] is None else '_q' + str(int(c[1]))}"
+                              f"{'_int8dp' if c[3] else ''}" for c in CASES])
+def test_fullsize_sampled_parity(name, smooth_q, head, int8_dp):
+    w = W.WORKLOADS[name]
+    sq = w.smooth_q if smooth_q is None else smooth_q
+    b, h = head
+    print(f"[fullsize] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} smooth_q={sq} head={head} int8_dp={int8_dp}",
+          flush=True)
+    o, lse, dq, dk, dv = _run_gpu(w, sq, int8_dp)
     o_g = G.host_f32(o[b, h])
     lse_g = lse[b, h].cpu().numpy()
     dq_g, dk_g, dv_g = (G.host_f32(t[b, h]) for t in (dq, dk, dv))
     for t in (o_g, lse_g, dq_g, dk_g, dv_g):
         assert np.all(np.isfinite(t))
-    del x, tq, tk, tv, tdo, o, lse, dq, dk, dv, fws
+    del o, lse, dq, dk, dv
 
     f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
     N, T = w.N, (w.N + 63) // 64
     pp = F.prepare(f["q"], f["k"], f["v"], sq, w.smooth_k)
     o_f, lse_f = F.fwd_head(pp, w.causal)
     o_f, lse_f = o_f[:N], lse_f[:N]
+    G.parity("O", o_g, o_f, where=" (all rows)")
+    assert np.max(np.abs(lse_g - lse_f)) <= 2e-3
     blocks = _blocks(T)
     rows = np.concatenate([np.arange(i * 64, min(N, i * 64 + 64)) for i in blocks])
-    assert M.rel_l2(o_g[rows], o_f[rows]) <= 1e-2, M.rel_l2(o_g[rows], o_f[rows])
-    assert M.rel_l2(o_g, o_f) <= 1e-2
-    assert np.max(np.abs(lse_g - lse_f)) <= 2e-3
     # end to end: the oracle's backward takes the oracle's O (bf16) and LSE
     o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
     bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"], int8_dp)
     dq_f, dk_f, dv_f = F.bwd_head(bp, w.causal, blocks, blocks)
     sel = np.concatenate([np.arange(j * 64, j * 64 + min(64, N - i * 64)) for j, i in enumerate(blocks)])
-    errs = {"dQ": M.rel_l2(dq_g[rows], dq_f[sel]), "dK": M.rel_l2(dk_g[rows], dk_f[sel]),
-            "dV": M.rel_l2(dv_g[rows], dv_f[sel])}
-    print("  rel-L2 vs faithful:", {k: f"{v:.2e}" for k, v in errs.items()},
-          f"O {M.rel_l2(o_g, o_f):.2e}", flush=True)
-    for k, v in errs.items():
-        assert v <= 1e-2, (k, v)
+    for k, a, r in (("dQ", dq_g, dq_f), ("dK", dk_g, dk_f), ("dV", dv_g, dv_f)):
+        G.parity(k, a[rows], r[sel], where=f" (blocks {blocks})")
     # against exact attention, on the same sampled rows
     oe, le, dqe, dke, dve = exact.sampled(f["q"], f["k"], f["v"], f["do"], w.causal, rows, rows)
     cos = {"O": M.cos_sim(o_g[rows], oe), "dQ": M.cos_sim(dq_g[rows], dqe), "dK": M.cos_sim(dk_g[rows], dke),
@@ -87,11 +94,41 @@ def test_fullsize_sampled_parity(name, smooth_q, head, int8_dp):
         assert cos[k] >= 0.99, (k, cos[k])
 
 
+QSMOOTH = [("video", (1, 3)), ("video", (0, 11)), ("llama16k", (0, 29))]
+
+
+@pytest.mark.parametrize("name,head", QSMOOTH, ids=[f"{c[0]}_h{c[1][0]}.{c[1][1]}" for c in QSMOOTH])
+def test_q_smoothing_comparison(name, head):
+    """The same heads with Q-smoothing on and off (SageBwd abstract, insight
+    (iv): Q-smoothing is optional and of limited benefit in pretraining; the
+    SageAttention3 summary's table lists "Add Q smoothing" among its measured
+    effects): cosine similarity, relative L1 and relative L2 against exact
+    attention of O, dQ, dK, dV on the sampled blocks, for both modes.  Both
+    must meet the bars (cosine >= 0.999 for O, >= 0.99 for the gradients)."""
+    w = W.WORKLOADS[name]
+    b, h = head
+    f = {n: W.bf16_bits_to_f32(a) for n, a in W.make_head(w, b, h).items()}
+    N, T = w.N, (w.N + 63) // 64
+    blocks = _blocks(T)
+    rows = np.concatenate([np.arange(i * 64, min(N, i * 64 + 64)) for i in blocks])
+    ex = dict(zip(("O", "LSE", "dQ", "dK", "dV"), exact.sampled(f["q"], f["k"], f["v"], f["do"], w.causal, rows, rows)))
+    for sq in (True, False):
+        o, lse, dq, dk, dv = _run_gpu(w, sq)
+        got = {"O": G.host_f32(o[b, h])[rows], "dQ": G.host_f32(dq[b, h])[rows], "dK": G.host_f32(dk[b, h])[rows],
+               "dV": G.host_f32(dv[b, h])[rows]}
+        del o, lse, dq, dk, dv
+        res = {k: (M.cos_sim(a, ex[k]), M.l1(a, ex[k]), M.rel_l2(a, ex[k])) for k, a in got.items()}
+        print(f"[q-smoothing {'on ' if sq else 'off'}] {name} head={head}: " +
+              ", ".join(f"{k} cos {c:.6f} L1 {l:.3e} relL2 {r:.3e}" for k, (c, l, r) in res.items()), flush=True)
+        assert res["O"][0] >= 0.999
+        for k in ("dQ", "dK", "dV"):
+            assert res[k][0] >= 0.99, (sq, k, res[k])
+
+
 def test_fullsize_qk_norm_sampled_parity():
     """The fused QK-norm at the pretraining shape (B8 H16 N2048 causal) on raw
     rows of very different sizes: one sampled head, forward over all rows and
-    the backward's first, middle and last blocks, with gradients through the
-    norm."""
+    the backward's sampled blocks, with gradients through the norm."""
     w = W.custom(8, 16, 2048, True, True, False, "rowscale", 95)
     b, h = 5, 9
     print(f"[fullsize qk_norm] B{w.B} H{w.H} N{w.N} head=({b}, {h})", flush=True)
@@ -110,17 +147,16 @@ def test_fullsize_qk_norm_sampled_parity():
     pp = F.prepare(f["q"], f["k"], f["v"], False, True, qk_norm=True)
     o_f, lse_f = F.fwd_head(pp, True)
     o_f, lse_f = o_f[:N], lse_f[:N]
-    assert M.rel_l2(o_g, o_f) <= 1e-2 and np.max(np.abs(lse_g - lse_f)) <= 2e-3
+    G.parity("O", o_g, o_f)
+    assert np.max(np.abs(lse_g - lse_f)) <= 2e-3
     blocks = _blocks(T)
     rows = np.concatenate([np.arange(i * 64, i * 64 + 64) for i in blocks])
     o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_f.astype(np.float32)))
     bp = F.prepare_bwd(pp, f["v"], o_b, lse_f.astype(np.float32), f["do"])
     dq_f, dk_f, dv_f = F.bwd_head(bp, True, blocks, blocks)
     dq_f, dk_f = F.norm_grads(pp, dq_f, dk_f, rows, rows)
-    errs = {"dQ": M.rel_l2(dq_g[rows], dq_f), "dK": M.rel_l2(dk_g[rows], dk_f), "dV": M.rel_l2(dv_g[rows], dv_f)}
-    print("  rel-L2 vs faithful:", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    for k, v in errs.items():
-        assert v <= 1e-2, (k, v)
+    for k, a, r in (("dQ", dq_g, dq_f), ("dK", dk_g, dk_f), ("dV", dv_g, dv_f)):
+        G.parity(k, a[rows], r)
     oe, le, dqe, dke, dve = exact.sampled(f["q"], f["k"], f["v"], f["do"], True, rows, rows, qk_norm=True)
     cos = {"O": M.cos_sim(o_g[rows], oe), "dQ": M.cos_sim(dq_g[rows], dqe), "dK": M.cos_sim(dk_g[rows], dke),
            "dV": M.cos_sim(dv_g[rows], dve)}

@@ -14,8 +14,14 @@ values exactly:
          s_dS, dS codes = F3 of the dumped dS; dS^T Q = codes^T Q_code
   dq     the dS codes and scale the dK/dV kernel stored, after its
          transposition (bit for bit); dS K = codes K_code
-The codes the oracle forms from its own float64 P and dS agree except at
-rounding boundaries; that rate is reported and bounded."""
+The codes the oracle forms from its own float64 P~, P and dS agree except at
+rounding boundaries; that rate is reported and bounded.
+
+The debug instantiations differ from the production kernels only by their
+dump stores, which move instructions; so the production forward and
+backward are also run on the same inputs and their outputs (O, LSE, dQ, dK,
+dV) must equal the debug instantiations' outputs bit for bit: the replayed
+codes and products are then those of the production kernels."""
 import numpy as np
 import pytest
 import torch
@@ -67,6 +73,12 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
     o_b = W.bf16_bits_to_f32(W.f32_to_bf16_bits(o_all[b, h]))
     bp = F.prepare_bwd(pp, f["v"], o_b, lse_all[b, h], f["do"], int8_dp)
     fresh_total, fresh_diff = 0, 0
+    fwd_total, fwd_diff = 0, 0
+    # the production kernels on the same inputs (the backward re-quantizes, as
+    # the debug path does)
+    po, plse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k)
+    pgrads = sb.bwd(tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k, int8_dp=int8_dp)
+    torch.cuda.synchronize()
     for (i, t) in tiles:
         rows = slice(64 * i, 64 * i + 64)
         cols = slice(64 * t, 64 * t + 64)
@@ -81,9 +93,22 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         assert np.array_equal(codes.astype(np.int64), np.rint(v.astype(np.float64)).astype(np.int64)), ("fwd codes", i, t)
         assert np.array_equal(_blk(d, ACC1, np.int32).astype(np.int64),
                               (codes.astype(np.float64) @ pp.vc[cols]).astype(np.int64)), ("fwd PV", i, t)
+        assert torch.equal(fo.view(torch.int16), po.view(torch.int16)) and torch.equal(fl, plse), ("fwd prod", i, t)
+        _, _, fc, _ = F.fwd_head(pp, w.causal, qblocks=[i], return_codes=True)
+        fcode = fc[:, cols]
+        keep = np.ones((64, 64), bool)
+        if w.causal:
+            keep &= (np.arange(64 * t, 64 * t + 64)[None, :] <= np.arange(64 * i, 64 * i + 64)[:, None])
+        keep &= (np.arange(64 * i, 64 * i + 64)[:, None] < N) & (np.arange(64 * t, 64 * t + 64)[None, :] < N)
+        nd = int(np.sum((fcode != codes) & keep))
+        fwd_total += int(np.sum(keep))
+        fwd_diff += nd
         # ---- dK/dV kernel
-        d1 = sb.debug_tile("dkdv", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
-                           int8_dp).numpy().tobytes()
+        d1, g1 = sb.debug_tile("dkdv", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
+                               int8_dp, return_grads=True)
+        d1 = d1.numpy().tobytes()
+        for name, a, pr in (("dK", g1[1], pgrads[1]), ("dV", g1[2], pgrads[2])):
+            assert torch.equal(a.view(torch.int16), pr.view(torch.int16)), (name + " prod", i, t)
         assert np.array_equal(_blk(d1, A, np.int32), a_ref.astype(np.int32)), ("dkdv A", i, t)
         P = _blk(d1, F1, np.float32)
         sP, invP = F.block_scale(np.max(np.abs(P)))
@@ -102,8 +127,10 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
                               (cdS.T @ pp.qc[rows]).astype(np.int64)), ("dS^T Q", i, t)
         # ---- dQ kernel: the dK/dV kernel's dS codes and scale, read back and
         # transposed, bit for bit
-        d2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
-                           int8_dp).numpy().tobytes()
+        d2, g2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
+                               int8_dp, return_grads=True)
+        d2 = d2.numpy().tobytes()
+        assert torch.equal(g2[0].view(torch.int16), pgrads[0].view(torch.int16)), ("dQ prod", i, t)
         assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32)
         assert np.array_equal(_blk(d2, C1, np.int8), _blk(d1, C2, np.int8)), ("dq codes", i, t)
         assert np.array_equal(_blk(d2, ACC1, np.int32).astype(np.int64),
@@ -112,6 +139,8 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         tl = F.bwd_tiles(bp, [i], [t], w.causal)
         fresh_total += 2 * 4096
         fresh_diff += int(np.sum(tl["cP"] != cP)) + int(np.sum(tl["cdS"] != cdS))
-        print(f"  tile ({i},{t}): bit-exact; fresh-code differences P {int(np.sum(tl['cP'] != cP))} "
-              f"dS {int(np.sum(tl['cdS'] != cdS))} of 4096", flush=True)
+        print(f"  tile ({i},{t}): bit-exact, production outputs equal; fresh-code differences P~ {nd} of "
+              f"{int(np.sum(keep))}, P {int(np.sum(tl['cP'] != cP))} dS {int(np.sum(tl['cdS'] != cdS))} of 4096",
+              flush=True)
     assert fresh_diff <= 0.02 * fresh_total, (fresh_diff, fresh_total)
+    assert fwd_diff <= 0.02 * max(fwd_total, 1), (fwd_diff, fwd_total)
