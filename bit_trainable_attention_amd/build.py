@@ -4,7 +4,10 @@ Each .hip source under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into bit_trainable_attention_amd/libsagebwd.so.
 Flags: gfx950 only, -O3, packed-FP32 VALU instructions disabled (the compiler
 otherwise emits v_pk_*_f32 by itself), no fast-math (the quantizer's float32
-divisions and roundings must be the IEEE ones the tests check bit for bit).
+divisions and roundings must be the IEEE ones the tests check bit for bit),
+and no floating-point contraction: every fused multiply-add is written out,
+so each template instantiation of a kernel (the debug ones that dump a tile
+included) rounds exactly the same operations.
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsagebwd.so")
 SOURCES = ["prepare.hip", "fwd.hip", "bwd.hip", "api.hip", "selftest.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -20,8 +20,11 @@ rounding boundaries; that rate is reported and bounded.
 The debug instantiations differ from the production kernels only by their
 dump stores, which move instructions; so the production forward and
 backward are also run on the same inputs and their outputs (O, LSE, dQ, dK,
-dV) must equal the debug instantiations' outputs bit for bit: the replayed
-codes and products are then those of the production kernels."""
+dV of the dumped head) must equal the debug instantiations' outputs bit for
+bit: the replayed codes and products are then those of the production
+kernels.  (The library is built without floating-point contraction, so the
+compiler cannot fuse a multiply and an add in one instantiation and not in
+the other.)"""
 import numpy as np
 import pytest
 import torch
@@ -93,7 +96,8 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         assert np.array_equal(codes.astype(np.int64), np.rint(v.astype(np.float64)).astype(np.int64)), ("fwd codes", i, t)
         assert np.array_equal(_blk(d, ACC1, np.int32).astype(np.int64),
                               (codes.astype(np.float64) @ pp.vc[cols]).astype(np.int64)), ("fwd PV", i, t)
-        assert torch.equal(fo.view(torch.int16), po.view(torch.int16)) and torch.equal(fl, plse), ("fwd prod", i, t)
+        assert torch.equal(fo[b, h].view(torch.int16), po[b, h].view(torch.int16)), ("fwd prod O", i, t)
+        assert torch.equal(fl[b, h], plse[b, h]), ("fwd prod LSE", i, t)
         _, _, fc, _ = F.fwd_head(pp, w.causal, qblocks=[i], return_codes=True)
         fcode = fc[:, cols]
         keep = np.ones((64, 64), bool)
@@ -108,7 +112,7 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
                                int8_dp, return_grads=True)
         d1 = d1.numpy().tobytes()
         for name, a, pr in (("dK", g1[1], pgrads[1]), ("dV", g1[2], pgrads[2])):
-            assert torch.equal(a.view(torch.int16), pr.view(torch.int16)), (name + " prod", i, t)
+            assert torch.equal(a[b, h].view(torch.int16), pr[b, h].view(torch.int16)), (name + " prod", i, t)
         assert np.array_equal(_blk(d1, A, np.int32), a_ref.astype(np.int32)), ("dkdv A", i, t)
         P = _blk(d1, F1, np.float32)
         sP, invP = F.block_scale(np.max(np.abs(P)))
@@ -130,7 +134,7 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         d2, g2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
                                int8_dp, return_grads=True)
         d2 = d2.numpy().tobytes()
-        assert torch.equal(g2[0].view(torch.int16), pgrads[0].view(torch.int16)), ("dQ prod", i, t)
+        assert torch.equal(g2[0][b, h].view(torch.int16), pgrads[0][b, h].view(torch.int16)), ("dQ prod", i, t)
         assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32)
         assert np.array_equal(_blk(d2, C1, np.int8), _blk(d1, C2, np.int8)), ("dq codes", i, t)
         assert np.array_equal(_blk(d2, ACC1, np.int32).astype(np.int64),
