@@ -27,8 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libsagebwd.so")
 
 REGIONS = {"MU_Q": 0, "MU_K": 1, "Q_R": 2, "K_R": 3, "V_T": 4, "Q_T": 5, "K_T": 6, "DO_T": 7,
            "S_Q": 8, "S_K": 9, "S_V": 10, "S_DO": 11, "CORR": 12, "BIAS": 13, "NDELTA": 14,
-           "LSE2": 15, "DO16": 16, "V16": 17, "DO_R": 18, "V_R": 19, "RQ": 20, "RK": 21,
-           "DS": 22, "DS_SCALE": 23}
+           "LSE2": 15, "DO16": 16, "V16": 17, "DO_R": 18, "V_R": 19, "RQ": 20, "RK": 21}
 
 
 STAGES = {"FWD_PREPARE": 0, "FWD_ATTN": 1, "BWD_PREPARE": 2, "BWD_DKDV": 3, "BWD_DQ": 4, "BWD_ATTN": 5}

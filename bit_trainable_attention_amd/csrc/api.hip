@@ -15,7 +15,7 @@ using namespace sagebwd;
 enum Region {
     R_MU_Q = 0, R_MU_K, R_Q_R, R_K_R, R_V_T, R_Q_T, R_K_T, R_DO_T,
     R_S_Q, R_S_K, R_S_V, R_S_DO, R_CORR, R_BIAS, R_DELTA, R_LSE2, R_DO16, R_V16,
-    R_DO_R, R_V_R, R_RQ, R_RK, R_DS, R_DS_SCALE, R_SUMS, R_COUNT
+    R_DO_R, R_V_R, R_RQ, R_RK, R_SUMS, R_COUNT
 };
 
 struct Layout {
@@ -26,27 +26,8 @@ struct Layout {
 
 constexpr int32_t MAX_N = 1 << 18;
 constexpr int64_t MAX_BH = 65535;
-// The backward keeps the INT8 dS codes of every tile of a group of heads
-// (4 KB per 64x64 tile) between its two attention kernels; a group holds as
-// many heads as fit in this many bytes, and at least one.
-constexpr size_t DS_CAP_BYTES = (size_t)16 << 30;
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Heads per backward group and the number of groups (equal-sized but the last).
-struct Groups {
-    int heads, count;
-    size_t ntiles;   // dS tiles per head
-};
-Groups head_groups(const sagebwd_params& p) {
-    const int BH = p.B * p.H;
-    const int T = (p.N + BLK - 1) / BLK;
-    const size_t nt = ds_tiles_per_head(p.causal, T);
-    size_t hmax = DS_CAP_BYTES / (nt * 4096);
-    if (hmax < 1) hmax = 1;
-    const int count = (int)((BH + hmax - 1) / hmax);
-    return Groups{(BH + count - 1) / count, count, nt};
-}
 
 // Which regions a pass uses: the forward needs Q/K row codes and V
 // transposed codes; the backward needs Q/K in both layouts and its own
@@ -84,9 +65,6 @@ Layout make_layout(const sagebwd_params& p, Pass pass) {
     sz[R_V_R] = i8dp ? BH * T * 4096 : 0;
     sz[R_RQ] = p.qk_norm ? BH * Np * 4 : 0;         // QK-norm factors of Q and K tokens
     sz[R_RK] = p.qk_norm ? BH * Np * 4 : 0;
-    const Groups G = head_groups(p);
-    sz[R_DS] = bwd ? (size_t)G.heads * G.ntiles * 4096 : 0;     // dS codes of one head group
-    sz[R_DS_SCALE] = bwd ? (size_t)G.heads * G.ntiles * 4 : 0;
     sz[R_SUMS] = BH * 2 * nchunk * HD * 8;
     size_t o = 0;
     for (int r = 0; r < R_COUNT; ++r) {
@@ -261,9 +239,6 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     a.dq = (uint16_t*)dQ;
     a.dk = (uint16_t*)dK;
     a.dv = (uint16_t*)dV;
-    a.ds_codes = region<int8_t>(ws, L, R_DS);
-    a.ds_scale = region<float>(ws, L, R_DS_SCALE);
-    a.ntiles = head_groups(p).ntiles;
     a.N = p.N;
     a.T = (p.N + BLK - 1) / BLK;
     a.ngroups = (a.T + 1) / 2;
@@ -273,52 +248,14 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
     return a;
 }
 
-// The same arguments restricted to heads [bh0, bh0 + nbh): every per-head
-// pointer moves by bh0 heads, the dS buffers stay (they hold one group).
-template <class P>
-P* adv(P* ptr, size_t n) { return ptr ? ptr + n : ptr; }
-BwdArgs group_args(const BwdArgs& a, int bh0, int nbh) {
-    BwdArgs c = a;
-    const size_t T = (size_t)a.T, Np = T * BLK, codes = (size_t)bh0 * T * 4096, blocks = (size_t)bh0 * T,
-                 rows = (size_t)bh0 * Np, toks = (size_t)bh0 * a.N * HD;
-    c.q_r = adv(a.q_r, codes);
-    c.k_r = adv(a.k_r, codes);
-    c.q_t = adv(a.q_t, codes);
-    c.k_t = adv(a.k_t, codes);
-    c.do_t = adv(a.do_t, codes);
-    c.do_r = adv(a.do_r, codes);
-    c.v_r = adv(a.v_r, codes);
-    c.sq = adv(a.sq, blocks);
-    c.sk = adv(a.sk, blocks);
-    c.sdo = adv(a.sdo, blocks);
-    c.sv = adv(a.sv, blocks);
-    c.bias = adv(a.bias, rows);
-    c.delta = adv(a.delta, rows);
-    c.lse2 = adv(a.lse2, rows);
-    c.rq = adv(a.rq, rows);
-    c.rk = adv(a.rk, rows);
-    c.do16 = adv(a.do16, rows * HD);
-    c.v16 = adv(a.v16, rows * HD);
-    c.mu_q = adv(a.mu_q, (size_t)bh0 * HD);
-    c.q_in = adv(a.q_in, toks);
-    c.k_in = adv(a.k_in, toks);
-    c.dq = adv(a.dq, toks);
-    c.dk = adv(a.dk, toks);
-    c.dv = adv(a.dv, toks);
-    c.BH = nbh;
-    c.dump_bh = a.dump_bh >= 0 ? a.dump_bh - bh0 : -1;
-    return c;
-}
-
-// The two attention kernels of the backward over one head group.  kernel_dump
-// selects which of them (1: dK/dV, 2: dQ) runs its debug instantiation.
-void run_bwd_group(const sagebwd_params& p, const BwdArgs& a, int grp, int which, int kernel_dump,
-                   hipStream_t st) {
-    const Groups G = head_groups(p);
-    const int bh0 = grp * G.heads, nbh = std::min(G.heads, p.B * p.H - bh0);
-    const BwdArgs c = group_args(a, bh0, nbh);
-    if (which & 1) launch_bwd_dkdv(c, nbh, p.causal, p.smooth_q, p.int8_dp, p.mxfp8, st, kernel_dump == 1);
-    if (which & 2) launch_bwd_dq(c, nbh, p.causal, p.mxfp8, st, kernel_dump == 2);
+// The two attention kernels of the backward.  which: 1 the dK/dV kernel, 2
+// the dQ kernel, 3 both; kernel_dump selects which of them (1: dK/dV, 2: dQ)
+// runs its debug instantiation.  The two are independent: each recomputes
+// the scores, P and dS it needs.
+void run_bwd_attn(const sagebwd_params& p, const BwdArgs& a, int which, int kernel_dump, hipStream_t st) {
+    const int BH = p.B * p.H;
+    if (which & 1) launch_bwd_dkdv(a, BH, p.causal, p.smooth_q, p.int8_dp, p.mxfp8, st, kernel_dump == 1);
+    if (which & 2) launch_bwd_dq(a, BH, p.causal, p.mxfp8, st, kernel_dump == 2);
 }
 
 }  // namespace
@@ -404,20 +341,11 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const v
         return hip_status();
     }
     const BwdArgs a = bwd_args(*p, L, qk, ws, Q, K, dQ, dK, dV);
-    const int groups = head_groups(*p).count;
-    if (stage == SAGEBWD_STAGE_BWD_ATTN) {
-        for (int g = 0; g < groups; ++g) run_bwd_group(*p, a, g, 3, 0, st);
-        return hip_status();
-    }
-    // the two attention stages on their own hand the dS codes of all heads
-    // from one to the other, which needs a single head group
-    if (groups != 1) return SAGEBWD_ERR_UNSUPPORTED;
-    run_bwd_group(*p, a, 0, stage == SAGEBWD_STAGE_BWD_DKDV ? 1 : 2, 0, st);
+    run_bwd_attn(*p, a, stage == SAGEBWD_STAGE_BWD_ATTN ? 3 : stage == SAGEBWD_STAGE_BWD_DKDV ? 1 : 2, 0, st);
     return hip_status();
 }
 
-// The whole backward: preparation, then for each head group the dK/dV kernel
-// followed by the dQ kernel (which reads the group's dS codes).
+// The whole backward: preparation, then the dK/dV kernel and the dQ kernel.
 static int bwd_pass(const sagebwd_params* p, const void* Q, const void* K, const void* V, const void* O,
              const float* LSE, const void* dO, void* dQ, void* dK, void* dV, const void* fwd_ws,
              size_t fwd_ws_bytes, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -465,9 +393,8 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
     a.dump_bh = bh;
     a.dump_i = qblock;
     a.dump_t = kblock;
-    // the head group holding the dumped head: its dK/dV kernel (which the dQ
-    // kernel reads), and for kernel 2 its dQ kernel
-    run_bwd_group(*p, a, bh / head_groups(*p).heads, kernel == 1 ? 1 : 3, kernel, (hipStream_t)stream);
+    // kernel 1: the dK/dV kernel; kernel 2: both (the dQ kernel dumps)
+    run_bwd_attn(*p, a, kernel == 1 ? 1 : 3, kernel, (hipStream_t)stream);
     return hip_status();
 }
 

@@ -6,11 +6,11 @@ namespace sagebwd {
 
 // Tile dump of the debug instantiations (row-major [row][col] blocks):
 //   A     i32 [64][64]  score accumulator Q_code K_code^T       [query][key]
-//   F1    f32 [64][64]  fwd: 127 P^ before rounding; dkdv: P; dq: dS
+//   F1    f32 [64][64]  fwd: 127 P^ before rounding; dkdv: P
 //   C1    u8  [64][64]  fwd: P~ codes; dkdv: P codes; dq: dS codes
 //   ACC1  i32 [64][64]  fwd: P~ V_code [query][ch]; dkdv: P^T dO [key][ch];
 //                       dq: dS K [query][ch]
-//   F2    f32 [64][64]  dkdv: dS
+//   F2    f32 [64][64]  dkdv, dq: dS
 //   C2    u8  [64][64]  dkdv: dS codes
 //   ACC2  i32 [64][64]  dkdv: dS^T Q [key][ch]
 //   SC    f32 [4]       dkdv: s_P, s_dS; dq: s_dS
@@ -18,6 +18,12 @@ namespace dumpoff {
 constexpr int A = 0, F1 = 16384, C1 = 32768, ACC1 = 36864, F2 = 53248, C2 = 69632, ACC2 = 73728, SC = 90112,
               BYTES = 90368;
 }
+
+// Compile-time flag passed to the loop-step lambdas of the attention kernels.
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
 
 struct FwdArgs {
     const int8_t *q_r, *k_r, *v_t;     // code blocks [BH][T][4096]
@@ -40,9 +46,6 @@ struct BwdArgs {
     const uint16_t *q_in, *k_in;       // bf16 Q, K as passed in [BH][N][64] (QK-norm gradient)
     const float *rq, *rk;              // QK-norm factors [BH][Np], or null (no QK-norm)
     uint16_t *dq, *dk, *dv;            // bf16 [BH][N][64]
-    int8_t* ds_codes;                  // dS codes of every computed tile [BH][ntiles][4096] (see ds_tile_index)
-    float* ds_scale;                   // their block scales [BH][ntiles] (MX: 4 exponent bytes per tile)
-    size_t ntiles;                     // tiles per head: T (T + 1) / 2 causal, T^2 otherwise
     int N, T, ngroups, BH;             // ngroups = ceil(T / 2): two 64-row blocks per workgroup
     uint8_t* dump;                     // tile dump (debug instantiation only)
     int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
@@ -55,16 +58,6 @@ int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hi
 int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, bool mx, hipStream_t st,
                     bool dump = false);
 int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump = false);
-
-// Position of the dS tile (query block i, key block t) among the tiles of
-// its head: query-block major, so the tiles of one query block are
-// contiguous; causal heads keep only t <= i.
-__host__ __device__ inline size_t ds_tile_index(bool causal, int i, int t, int T) {
-    return causal ? (size_t)i * (i + 1) / 2 + t : (size_t)i * T + t;
-}
-__host__ __device__ inline size_t ds_tiles_per_head(bool causal, int T) {
-    return causal ? (size_t)T * (T + 1) / 2 : (size_t)T * T;
-}
 
 template <class T>
 __device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }

@@ -77,6 +77,13 @@ __device__ __forceinline__ int pack_codes(float x0, float x1, float x2, float x3
     return (int)pack4(code_bits(x0, inv), code_bits(x1, inv), code_bits(x2, inv), code_bits(x3, inv));
 }
 
+// Codes of a 32x32 block held as 16 registers x 64 lanes (E4M3(x / 2^e)),
+// packed four registers to a dword in register order.
+__device__ __forceinline__ v4i fp8_block_codes(const float (&x)[16], float scale) {
+    return v4i{(int)fp8_quad(x[0], x[1], x[2], x[3], scale), (int)fp8_quad(x[4], x[5], x[6], x[7], scale),
+               (int)fp8_quad(x[8], x[9], x[10], x[11], scale), (int)fp8_quad(x[12], x[13], x[14], x[15], scale)};
+}
+
 // FP16 rows of 8 chunks of 16 bytes in LDS: chunk c of row r sits at slot
 // c ^ ((r / 2) % 8), so any 16 consecutive rows read at one chunk cover all
 // 64 banks (with c ^ (r % 8), rows r and r + 8 would collide).
@@ -306,21 +313,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
     float gsum = 0.0f;                                          // sum_i s_dS colsum(dS codes), this half
 
-    // the dS codes of the previous query block: stored just after the next
-    // block's DMA has been waited for, so that the stores complete during
-    // the following compute instead of delaying that wait
-    v4i dc_prev[2] = {v4i{}, v4i{}};
-    float sds_prev = 0.0f;
-    size_t tix_prev = 0;
-    bool have_prev = false;
-    auto store_prev = [&]() {
-        // streaming stores: the codes are read once, by the dQ kernel
-        v4i* dst = (v4i*)(a.ds_codes + tix_prev * 4096) + kh * 128 + lane;
-        __builtin_nontemporal_store(dc_prev[0], dst);
-        __builtin_nontemporal_store(dc_prev[1], dst + 64);
-        if (lane == 0) a.ds_scale[tix_prev] = sds_prev;   // both waves of the tile write the same value
-    };
-
     fetch(i0, 0);
     wait_vmem();
     lds_barrier();
@@ -363,8 +355,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         if (more) fetch(i + 1, buf ^ 1);
         wait_vmem();
         lds_barrier();
-        if (have_prev) store_prev();
-        have_prev = false;
         float dsm = 0.0f;
         if (active) {
             float sP, invP;
@@ -445,14 +435,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                              pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invdS),
                              pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invdS),
                              pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invdS)};
-            // hand the tile's codes and scale to the dQ kernel: 16-byte chunk
-            // (kh * 2 + qs) * 64 + lane of the tile holds this lane's key with
-            // the 16 queries of dc[qs] (the A-operand layout of dS^T Q)
-            dc_prev[0] = dc[0];
-            dc_prev[1] = dc[1];
-            sds_prev = sdS;
-            tix_prev = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, i, kvb, T);
-            have_prev = true;
             if (SMOOTHQ) {
                 int cs = 0;
 #pragma unroll
@@ -477,7 +459,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         }
         lds_barrier();
     }
-    if (have_prev) store_prev();
 
     // epilogue: dK (x 1/8, plus colsum(dS) mu_q for Q-smoothing) and dV in bf16;
     // lane = channel, registers = keys of this wave's half block
@@ -528,61 +509,37 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 
 // ------------------------------------------------------------------ dQ
 
-// dQ from the dS codes and scales the key-block kernel stored: for each key
-// block t, dQ_i += s_dS(i,t) s_K,t (dS codes(i,t) K codes_t), so nothing is
-// recomputed.  The stored codes hold, per lane, one key and 16 queries (the
-// layout in which the key-block kernel contracts over queries); dQ contracts
-// over keys, so each 32x32 code block is first transposed on the MFMA
-// itself, as the product with an INT8 identity matrix: D = A I puts query n
-// in lane n and keys 8(r/4) + 4h + r%4 in register r, exact small integers
-// whose low bytes are the codes in the B-operand layout of K^T dS^T.
+// dQ recomputes each tile's scores, P, dP - Delta and dS in the forward's
+// layout, S^T = K Q^T (lane = query, registers = keys), so that the dS codes
+// leave the accumulator as the B operand of dQ^T = K^T dS^T (contraction
+// over keys) with no transposition, and nothing of size N^2 is kept between
+// the two backward kernels.  Every product is formed from the key-block
+// kernel's operands in the same k order (the rank-2 score correction sums
+// -lse2_i and bias_j in the same order, the FP16 dO V^T MFMAs take the same
+// channel chunks in the same sequence from the same -Delta input, and the
+// FMAs are written out), so its P, dS, tile maxima, scales and codes are
+// bitwise the key-block kernel's; the tile replay test checks this.
 //
-// Each wave owns one 64-query block: per key block it streams the 4 KB dS
-// code tile of its block (HBM, read once, prefetched DQ_DEPTH key blocks
-// ahead) and reads the 4 KB K^T code block of the key block, which every
-// query block of the head needs.  The K^T reads from L2, not the dS stream,
-// bounded an earlier form with 32 queries per wave and one K^T read per wave;
-// here each K^T block serves 64 queries, and the four waves of a workgroup
-// (four consecutive query blocks, so nearly the same key-block range) share
-// one copy staged through LDS, loaded a quarter per wave.
+// Work split as in the forward: a workgroup of 4 waves owns 128 query rows
+// (two query blocks), each wave 32 of them, and walks the key blocks; a
+// 64x64 quantization tile of dS is held by the pair of waves of one query
+// block, which exchange their partial maxima through LDS.  Each key block's
+// K codes (both layouts), FP16 V rows, key bias and block scale go global ->
+// LDS by DMA into one of three buffers: the DMA for step t + 2 is issued
+// right after step t's barrier (the buffer it overwrites was last read in
+// step t - 1, which every wave has finished by then), so each step waits at
+// its one barrier for a DMA issued a whole step earlier.
 
-constexpr int DQ_DEPTH = 3;
-constexpr int DQ_BLOCKS_PER_WG = 4;   // one query block per wave
+constexpr int DQ_BUFS = 3;
 
-struct DqStep {
-    v4i ds[2][2];  // [qs][kh]: dS codes of query half qs, key half kh (A operand, lane = key)
-    v4i kq;        // this wave's quarter of the K^T code block (INT8 kernel)
-    float sds, sk; // s_dS(i, t) and s_K,t (MXFP8 kernel: their exponent words)
+struct DqSmem {
+    v4i k[DQ_BUFS][256];     // K row-operand codes (A operand of K Q^T)
+    v4i kt[DQ_BUFS][256];    // K transposed codes (A operand of K^T dS^T)
+    v8h v16[DQ_BUFS][512];   // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
+    float bias[DQ_BUFS][64]; // Q-smoothing key bias (log2 domain; 0 without Q-smoothing)
+    float sk[DQ_BUFS][4];    // [0]: K block scale (MXFP8: its four exponent bytes)
+    float red[2][4];         // partial |dS| maxima per wave, by step parity (INT8)
 };
-
-// Vector loads the compiler does not track (inline assembly): the INT8 dQ
-// kernel waits for them itself with dq_wait, which names the registers of a
-// ring slot as operands so that no use of them can move above the wait.
-// (The compiler's own wait counts lose precision around the prefetch loop and
-// fall back to waiting for every load in flight.)
-__device__ __forceinline__ v4i gload_nt(const v4i* p) {
-    v4i r;
-    asm volatile("global_load_dwordx4 %0, %1, off nt" : "=v"(r) : "v"(p));
-    return r;
-}
-__device__ __forceinline__ v4i gload(const v4i* p) {
-    v4i r;
-    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p));
-    return r;
-}
-__device__ __forceinline__ float gload1(const float* p) {
-    float r;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p));
-    return r;
-}
-// Wait until at most N of this wave's vector loads are outstanding.
-template <int N>
-__device__ __forceinline__ void dq_wait(DqStep& s) {
-    asm volatile("s_waitcnt vmcnt(%7)"
-                 : "+v"(s.ds[0][0]), "+v"(s.ds[0][1]), "+v"(s.ds[1][0]), "+v"(s.ds[1][1]), "+v"(s.kq), "+v"(s.sds),
-                   "+v"(s.sk)
-                 : "n"(N));
-}
 
 // dQ (x 1/8) in bf16; with QK-norm dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
 // other 32 channels of this lane's query being in the other half of the wave.
@@ -630,116 +587,241 @@ __device__ __forceinline__ void dq_epilogue(const BwdArgs& a, v16f (&dq)[2], int
     }
 }
 
-template <bool CAUSAL, bool DUMP>
+// The persistent operands of one wave's 32 queries.
+struct DqQuery {
+    v4i qop[2];       // Q row-operand codes (B operand of K Q^T)
+    v8h dob[4];       // dO in FP16, channels 16 ks + 8 h .. + 7 (B operand of V dO^T)
+    v16f nd;          // -Delta of this lane's query in every register (accumulator input of V dO^T)
+    float brow;       // B operand of the rank-2 score correction: -lse2 (h = 0) or 1 (h = 1)
+    uint32_t qw;      // Q block scale (MXFP8: exponent word)
+};
+
+// One key-block step of one wave up to the dS values: scores, P, dP - Delta
+// and dS = P (dP - Delta) for 32 queries x 64 keys (lane = query, registers
+// = keys 32 kb + 8 (r/4) + 4 h + r%4).  MASK only for the causal diagonal
+// tile and the ragged last key block.
+template <bool CAUSAL, bool MASK, bool MX>
+__device__ __forceinline__ void dq_scores(const DqSmem& sm, int buf, const DqQuery& qd, int t, int q, int N, int lane,
+                                          int h, float (&ds)[2][16], int (&sdump)[2][16], bool dump) {
+    const int l32 = lane % 32;
+    v16f corr[2], dpd[2];
+    v16i s[2];
+    v16f sx[2];
+    const uint32_t kw = __float_as_uint(sm.sk[buf][0]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (MX) {
+            const v8i ka = cat8(sm.k[buf][(kb * 2 + 0) * 64 + lane], sm.k[buf][(kb * 2 + 1) * 64 + lane]);
+            sx[kb] = mfma_fp8(ka, cat8(qd.qop[0], qd.qop[1]), v16f{}, ebyte(kw, 2 * kb + h), ebyte(qd.qw, h));
+        } else {
+            s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qd.qop[0], v16i{});
+            s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qd.qop[1], s[kb]);
+        }
+    }
+    // bias_j - lse2_i as [1 | bias] [-lse2 | 1]^T on the FP32 MFMA (32x32x2:
+    // lane l carries A[l%32][l/32] and B[l/32][l%32])
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        corr[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow, v16f{},
+                                                        0, 0, 0);
+    // dP^T - Delta = V dO^T + (-Delta): the key-block kernel's four FP16
+    // MFMAs with the operands swapped (the same channel chunk per k step)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + l32;
+        v16f d = mfma_f16(sm.v16[buf][swz(row, 0 + h)], qd.dob[0], qd.nd);
+        d = mfma_f16(sm.v16[buf][swz(row, 2 + h)], qd.dob[1], d);
+        d = mfma_f16(sm.v16[buf][swz(row, 4 + h)], qd.dob[2], d);
+        dpd[kb] = mfma_f16(sm.v16[buf][swz(row, 6 + h)], qd.dob[3], d);
+    }
+    const float sc = MX ? SCORE_SCALE_LOG2 : tile_scale(__uint_as_float(qd.qw), sm.sk[buf][0]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if (!MX && dump) sdump[kb][r] = s[kb][r];
+            const float sv = MX ? sx[kb][r] : (float)s[kb][r];
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc, corr[kb][r]));
+            if (MASK) {
+                asm volatile("" : "+v"(pv));   // a select, not a branch around each exp
+                const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+                pv = (key >= N || (CAUSAL && key > q)) ? 0.0f : pv;
+            }
+            ds[kb][r] = pv * dpd[kb][r];
+        }
+    }
+}
+
+template <bool CAUSAL, bool MX, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
-    // the wave index as a uniform value, so everything per wave (block,
-    // range, scale loads, the step guard) stays scalar
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, h = lane / 32,
-              l32 = lane % 32;
-    const int T = a.T;
+    __shared__ DqSmem sm;
+    const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
     int bh, g;
-    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g, CAUSAL);
-    const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
-    const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);   // waves past T only help stage K^T
-    const bool live = DQ_BLOCKS_PER_WG * g + wave < T;
-    const int t_end = !live ? 0 : CAUSAL ? qblk + 1 : T;
+    map_group_bwd(a.ngroups, a.BH, false, bh, g, CAUSAL);
+    const int T = a.T;
+    const int qblk = 2 * g + wave / 2, qhalf = wave % 2;
+    const bool live = qblk < T;
+    const int t_last_wg = CAUSAL ? min(2 * g + 1, T - 1) : T - 1;   // steps of the workgroup
+    const int t_last = !live ? -1 : CAUSAL ? qblk : T - 1;          // steps this wave computes
+    const bool ragged = (a.N & (BLK - 1)) != 0;
     const size_t bt = (size_t)bh * T;
     const size_t np = (size_t)T * BLK;
     const size_t rowbase = bh * np;
-    const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
-    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + lane;
-    const float* dss = a.ds_scale + tile0;
-    const v4i* ktg_wave = (const v4i*)(a.k_t + bt * 4096) + 64 * wave + lane;
-    const float* skg = a.sk + bt;
+    const int q = qblk * BLK + 32 * qhalf + l32;                    // this lane's query (padded index)
 
-    // INT8 identity as the B operand: column n = l32 has its one at k
-    // position n, which lies in half (n % 8) / 4, byte 4 (n / 8) + n % 4
-    v4i eye = v4i{0, 0, 0, 0};
-    if (h == (l32 % 8) / 4) eye[l32 / 8] = 1 << (8 * (l32 % 4));
+    DqQuery qd;
+    qd.qop[0] = qd.qop[1] = v4i{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qd.dob[ks] = v8h{};
+    float ndl = 0.0f, lse2 = 0.0f;
+    qd.qw = 0;
+    if (live) {
+        const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
+        qd.qop[0] = src[(qhalf * 2 + 0) * 64 + lane];
+        qd.qop[1] = src[(qhalf * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qd.dob[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+        ndl = a.delta[rowbase + q];
+        lse2 = a.lse2[rowbase + q];
+        const uint32_t w = ((const uint32_t*)a.sq)[bt + qblk];
+        qd.qw = MX ? (uint32_t)ebyte(w, 2 * qhalf + 0) | ((uint32_t)ebyte(w, 2 * qhalf + 1) << 8) : w;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) qd.nd[r] = ndl;
+    qd.brow = h == 0 ? -lse2 : 1.0f;
 
-    const int wg_end = CAUSAL ? min(qblk_wg_last, T - 1) + 1 : T;   // steps of the workgroup's longest wave
-    // chunk (kh * 2 + qs) * 64 + lane of a tile: key 32 kh + l32, 16 queries of
-    // half qs.  Every step loads (past the wave's own range it re-reads its
-    // last tile), so the wait counts before each use are fixed.
-    auto load = [&](int t, DqStep& s) {   // seven untracked loads per slot
-        const int td = min(t, max(t_end - 1, 0));
+    const v4i* kg = (const v4i*)(a.k_r + bt * 4096);
+    const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
+    auto fetch = [&](int t, int b) {
+        dma16_to_lds(kg + (size_t)t * 256 + tid, &sm.k[b][64 * wave]);
+        dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.kt[b][64 * wave]);
+        // LDS slot s of the FP16 V tile holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
+        const v4i* hs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) s.ds[qs][kh] = gload_nt(dsg + (size_t)td * 256 + (kh * 2 + qs) * 64);
-        s.kq = gload(ktg_wave + (size_t)min(t, wg_end - 1) * 256);
-        s.sds = gload1(dss + td);
-        s.sk = gload1(skg + td);
+        for (int j = 0; j < 2; ++j) {
+            const int s = 256 * j + tid, row = s / 8;
+            dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+        }
+        if (wave == 2 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
+        if (wave == 3 && lane == 0) dma4_to_lds(a.sk + bt + t, &sm.sk[b][0]);
     };
-    v16f dq[2][2] = {{v16f{}, v16f{}}, {v16f{}, v16f{}}};   // [qs][db]: lane = query, regs = channels
-    auto step = [&](int t, const DqStep& s, const v4i* kts) {
-        v4i kt[4];
+
+    v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, registers = channels 32 db + 8 (r/4) + 4 h + r%4
+    uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
+    const int qloc = 32 * qhalf + l32;
+
+    auto step = [&](int t, auto maybe_masked) {
+        const int buf = t % DQ_BUFS;
+        const bool active = t <= t_last;
+        float ds[2][16];
+        int sd[2][16];
+        uint8_t* dp = (DUMP && dp_sel && t == a.dump_t) ? dp_sel : nullptr;
+        if (active) {
+            if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
+                dq_scores<CAUSAL, true, MX>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
+            else
+                dq_scores<CAUSAL, false, MX>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
+            if (DUMP && dp) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kt[j] = kts[j * 64 + lane];
-        const float wq = s.sds * s.sk;
-        const bool dump_here = DUMP && bh == a.dump_bh && qblk == a.dump_i && t == a.dump_t;
-        if (dump_here && lane == 0) dump_at<float>(a.dump, dumpoff::SC)[0] = s.sds;
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
+                    for (int r = 0; r < 16; ++r) {
+                        const int kk = 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
+                        dump_at<int>(dp, dumpoff::A)[qloc * 64 + kk] = sd[kb][r];
+                        dump_at<float>(dp, dumpoff::F2)[qloc * 64 + kk] = ds[kb][r];
+                    }
+            }
+            if (!MX) {
+                float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
+                    m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
+                }
+                const float dsm = wave_max64(__builtin_fmaxf(m0, m1));
+                if (lane == 0) sm.red[t & 1][wave] = dsm;
+            }
+        }
+        // this wave's DMA of step t + 1 (issued a step ago) has landed; after
+        // the barrier every wave's has, and every partial maximum is visible
+        wait_vmem();
+        lds_barrier();
+        if (t + 2 <= t_last_wg) fetch(t + 2, (t + 2) % DQ_BUFS);
+        if (!active) return;
+        const uint32_t kw = __float_as_uint(sm.sk[buf][0]);
+        if (MX) {
+            // 32x32 blocks (this wave's queries x key half kb) lie within the wave
+            int eS[2];
             v4i dc[2];
-            v16i tr[2];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                tr[kh] = mfma_i8(s.ds[qs][kh], eye, v16i{});
-                dc[kh] = v4i{(int)pack4(tr[kh][0], tr[kh][1], tr[kh][2], tr[kh][3]),
-                             (int)pack4(tr[kh][4], tr[kh][5], tr[kh][6], tr[kh][7]),
-                             (int)pack4(tr[kh][8], tr[kh][9], tr[kh][10], tr[kh][11]),
-                             (int)pack4(tr[kh][12], tr[kh][13], tr[kh][14], tr[kh][15])};
+            for (int kb = 0; kb < 2; ++kb) {
+                float m = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) m = max_abs2f(m, ds[kb][r], ds[kb][r + 1]);
+                eS[kb] = mx_exponent(wave_max64(m));
+                dc[kb] = fp8_block_codes(ds[kb], pow2f(eS[kb]));
             }
-            if (dump_here) {
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        a.dump[dumpoff::C1 + (32 * qs + l32) * 64 + 32 * kh + 8 * (r / 4) + 4 * h + (r % 4)] =
-                            (uint8_t)tr[kh][r];
-            }
+            // dQ^T += K^T dS^T: B = the codes (k block h = key half h, scale
+            // of this lane's query for key half h)
+            const v8i db8 = cat8(dc[0], dc[1]);
+            const int de = (h ? eS[1] : eS[0]) + 127;
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(kt[db * 2 + 0], dc[0], v16i{});
-                acc = mfma_i8(kt[db * 2 + 1], dc[1], acc);
-                if (dump_here) {
+                const v8i ka = cat8(sm.kt[buf][(db * 2 + 0) * 64 + lane], sm.kt[buf][(db * 2 + 1) * 64 + lane]);
+                dq[db] = mfma_fp8(ka, db8, dq[db], ebyte(kw, 2 * h + db), de);
+            }
+        } else {
+            float sdS, invdS;
+            // both partial maxima are >= 0: the larger is the larger bit pattern
+            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[t & 1][wave]),
+                                             __float_as_uint(sm.red[t & 1][wave ^ 1]))),
+                        sdS, invdS);
+            v4i dc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                dc[kb] = v4i{pack_codes(ds[kb][0], ds[kb][1], ds[kb][2], ds[kb][3], invdS),
+                             pack_codes(ds[kb][4], ds[kb][5], ds[kb][6], ds[kb][7], invdS),
+                             pack_codes(ds[kb][8], ds[kb][9], ds[kb][10], ds[kb][11], invdS),
+                             pack_codes(ds[kb][12], ds[kb][13], ds[kb][14], ds[kb][15], invdS)};
+            if (DUMP && dp) {
+                if (lane == 0 && qhalf == 0) dump_at<float>(dp, dumpoff::SC)[0] = sdS;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        dump_at<int>(a.dump, dumpoff::ACC1)[(32 * qs + l32) * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] =
-                            acc[r];
+                        dp[dumpoff::C1 + qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] =
+                            (uint8_t)code_bits(ds[kb][r], invdS);
+            }
+            const float wq = sdS * __uint_as_float(kw);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                v16i acc = mfma_i8(sm.kt[buf][(db * 2 + 0) * 64 + lane], dc[0], v16i{});
+                acc = mfma_i8(sm.kt[buf][(db * 2 + 1) * 64 + lane], dc[1], acc);
+                if (DUMP && dp) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(dp, dumpoff::ACC1)[qloc * 64 + 32 * db + 8 * (r / 4) + 4 * h + (r % 4)] = acc[r];
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dq[qs][db][r] = __builtin_fmaf((float)acc[r], wq, dq[qs][db][r]);
+                for (int r = 0; r < 16; ++r) dq[db][r] = __builtin_fmaf((float)acc[r], wq, dq[db][r]);
             }
         }
     };
 
-    // the K^T block of each step is shared by the workgroup's four waves:
-    // each wave stages one quarter (loaded with its dS codes, through
-    // registers so no LDS DMA forces a full wait) into a double-buffered LDS
-    // tile
-    __shared__ v4i kts[2][256];
-    DqStep ring[DQ_DEPTH];
-#pragma unroll
-    for (int j = 0; j < DQ_DEPTH; ++j) load(j, ring[j]);
-    for (int t0 = 0; t0 < wg_end; t0 += DQ_DEPTH) {
-#pragma unroll
-        for (int j = 0; j < DQ_DEPTH; ++j) {
-            const int t = t0 + j;
-            if (t < wg_end) {
-                dq_wait<7 * (DQ_DEPTH - 1)>(ring[j]);   // this slot's loads have landed
-                kts[t & 1][64 * wave + lane] = ring[j].kq;
-                lds_barrier();   // LDS only: the prefetch stays in flight
-                if (t < t_end) step(t, ring[j], kts[t & 1]);
-                load(t + DQ_DEPTH, ring[j]);
-            }
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the ring's last, unused loads
+    fetch(0, 0);
+    if (t_last_wg >= 1) fetch(1, 1);
+    wait_vmem();
+    lds_barrier();
+    // Only the last two steps can hold a masked tile (the causal diagonal and
+    // the ragged last key block come last), so they run in a loop of their
+    // own and the main loop carries one form of the step.
+    const int t_tail = t_last_wg > 1 ? t_last_wg - 1 : 0;
+    int t = 0;
+    for (; t < t_tail; ++t) step(t, Flag<false>{});
+    for (; t <= t_last_wg; ++t) step(t, Flag<true>{});
     if (!live) return;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) dq_epilogue(a, dq[qs], bh, qblk * BLK + 32 * qs + l32, h, rowbase);
+    dq_epilogue(a, dq, bh, q, h, rowbase);
 }
 
 // ------------------------------------------------------------------ MXFP8
@@ -761,13 +843,6 @@ struct DkdvMxSmem {
     float lse2[2][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta
     uint32_t qs[2][4];   // [0]: Q block exponents, [1]: dO block exponents
 };
-
-// Codes of a 32x32 block held as 16 registers x 64 lanes (E4M3(x / 2^e)),
-// packed four registers to a dword in register order.
-__device__ __forceinline__ v4i fp8_block_codes(const float (&x)[16], float scale) {
-    return v4i{(int)fp8_quad(x[0], x[1], x[2], x[3], scale), (int)fp8_quad(x[4], x[5], x[6], x[7], scale),
-               (int)fp8_quad(x[8], x[9], x[10], x[11], scale), (int)fp8_quad(x[12], x[13], x[14], x[15], scale)};
-}
 
 // S = Q K^T (dequantized in the MFMA) and P = exp2(S log2(e)/8 + bias_j -
 // lse2_i) for one 64-query x 32-key tile (lane = key, registers = queries);
@@ -863,17 +938,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
     v16f csum = v16f{};   // Q-smoothing: every column holds sum over queries of dS^ for key (row)
 
-    v4i dc_prev[2] = {v4i{}, v4i{}};
-    uint32_t e_prev = 0;
-    size_t tix_prev = 0;
-    bool have_prev = false;
-    auto store_prev = [&]() {
-        v4i* dst = (v4i*)(a.ds_codes + tix_prev * 4096) + kh * 128 + lane;
-        __builtin_nontemporal_store(dc_prev[0], dst);
-        __builtin_nontemporal_store(dc_prev[1], dst + 64);
-        if (lane == 0) ((uint16_t*)(a.ds_scale + tix_prev))[kh] = (uint16_t)e_prev;   // bytes 2 kh, 2 kh + 1
-    };
-
     fetch(i0, 0);
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
     for (int i = i0; i < T; ++i) {
@@ -883,8 +947,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         wait_vmem();
         lds_barrier();
         if (i + 1 < T) fetch(i + 1, buf ^ 1);
-        if (have_prev) store_prev();
-        have_prev = false;
         if (!live || (CAUSAL && i < kvb)) continue;
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
         const uint32_t q_w = sm.qs[buf][0], do_w = sm.qs[buf][1];
@@ -951,13 +1013,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
                                   dk[db], de, ebyte(q_w, 2 * h + db));
             if (SMOOTHQ) csum = mfma_fp8(da, ones, csum, de, e_one);
         }
-        dc_prev[0] = dc[0];
-        dc_prev[1] = dc[1];
-        e_prev = (uint32_t)(eS[0] + 127) | ((uint32_t)(eS[1] + 127) << 8);
-        tix_prev = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, i, kvb, T);
-        have_prev = true;
     }
-    if (have_prev) store_prev();
 
     if (!live) return;
 #pragma unroll
@@ -993,95 +1049,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
             }
         }
     }
-}
-
-// dQ from the stored E4M3 dS codes: each 32-key half of a tile is transposed
-// on the MFMA as its product with an E4M3 identity (the codes in the first 32
-// k positions, zeros in the other 32; every output is one exact product),
-// re-coded (exact: the values are E4M3 values), and contracted with the K^T
-// codes, the block exponents applied inside the instruction.
-template <bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void k_bwd_dq_mx(BwdArgs a) {
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, h = lane / 32,
-              l32 = lane % 32;
-    const int T = a.T;
-    int bh, g;
-    map_group_bwd((T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG, a.BH, false, bh, g, CAUSAL);
-    const int qblk_wg_last = DQ_BLOCKS_PER_WG * g + DQ_BLOCKS_PER_WG - 1;
-    const int qblk = min(DQ_BLOCKS_PER_WG * g + wave, T - 1);
-    const bool live = DQ_BLOCKS_PER_WG * g + wave < T;
-    const int t_end = !live ? 0 : CAUSAL ? qblk + 1 : T;
-    const int wg_end = CAUSAL ? min(qblk_wg_last, T - 1) + 1 : T;
-    const size_t bt = (size_t)bh * T;
-    const size_t np = (size_t)T * BLK;
-    const size_t rowbase = bh * np;
-    const size_t tile0 = (size_t)bh * a.ntiles + ds_tile_index(CAUSAL, qblk, 0, T);
-    const v4i* dsg = (const v4i*)(a.ds_codes + tile0 * 4096) + lane;
-    const float* dss = a.ds_scale + tile0;            // exponent words, loaded as their bit patterns
-    const v4i* ktg_wave = (const v4i*)(a.k_t + bt * 4096) + 64 * wave + lane;
-    const float* skg = a.sk + bt;
-
-    // E4M3 identity (B operand): column n = l32 has 1.0 at k position n,
-    // which lies in half (n % 8) / 4, byte 4 (n / 8) + n % 4
-    v8i eye = v8i{};
-    if (h == (l32 % 8) / 4) eye[l32 / 8] = E4M3_ONE << (8 * (l32 % 4));
-    const int e_one = opaque(E8M0_ONE);
-
-    auto load = [&](int t, DqStep& s) {   // seven untracked loads per slot, as in the INT8 kernel
-        const int td = min(t, max(t_end - 1, 0));
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) s.ds[qs][kh] = gload_nt(dsg + (size_t)td * 256 + (kh * 2 + qs) * 64);
-        s.kq = gload(ktg_wave + (size_t)min(t, wg_end - 1) * 256);
-        s.sds = gload1(dss + td);
-        s.sk = gload1(skg + td);
-    };
-    v16f dq[2][2] = {{v16f{}, v16f{}}, {v16f{}, v16f{}}};
-    auto step = [&](const DqStep& s, const v4i* kts) {
-        v8i kt[2];
-#pragma unroll
-        for (int db = 0; db < 2; ++db) kt[db] = cat8(kts[(db * 2 + 0) * 64 + lane], kts[(db * 2 + 1) * 64 + lane]);
-        const uint32_t ds_w = __float_as_uint(s.sds), sk_w = __float_as_uint(s.sk);
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            v4i dc[2];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const v16f tr = mfma_fp8(cat8(s.ds[qs][kh], v4i{}), eye, v16f{}, e_one, e_one);
-                float x[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = tr[r];
-                dc[kh] = fp8_block_codes(x, 1.0f);
-            }
-            const v8i db8 = cat8(dc[0], dc[1]);
-            const int de = ebyte(ds_w, 2 * h + qs);   // key half h, query half qs
-#pragma unroll
-            for (int db = 0; db < 2; ++db) dq[qs][db] = mfma_fp8(kt[db], db8, dq[qs][db], ebyte(sk_w, 2 * h + db), de);
-        }
-    };
-
-    __shared__ v4i kts[2][256];
-    DqStep ring[DQ_DEPTH];
-#pragma unroll
-    for (int j = 0; j < DQ_DEPTH; ++j) load(j, ring[j]);
-    for (int t0 = 0; t0 < wg_end; t0 += DQ_DEPTH) {
-#pragma unroll
-        for (int j = 0; j < DQ_DEPTH; ++j) {
-            const int t = t0 + j;
-            if (t < wg_end) {
-                dq_wait<7 * (DQ_DEPTH - 1)>(ring[j]);
-                kts[t & 1][64 * wave + lane] = ring[j].kq;
-                lds_barrier();
-                if (t < t_end) step(ring[j], kts[t & 1]);
-                load(t + DQ_DEPTH, ring[j]);
-            }
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (!live) return;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) dq_epilogue(a, dq[qs], bh, qblk * BLK + 32 * qs + l32, h, rowbase);
 }
 
 // Instantiation by (causal, Q-smoothing, all-INT8 dO V^T, tile dump).
@@ -1126,18 +1093,18 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
 #undef SAGEBWD_LAUNCH_BWD
 
 int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump) {
-    dim3 grid(((a.T + DQ_BLOCKS_PER_WG - 1) / DQ_BLOCKS_PER_WG) * BH), block(64 * BWD_WAVES);
+    dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
     if (mx) {
-        if (causal) hipLaunchKernelGGL((k_bwd_dq_mx<true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq_mx<false>), grid, block, 0, st, a);
+        if (causal) hipLaunchKernelGGL((k_bwd_dq<true, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<false, true, false>), grid, block, 0, st, a);
         return 0;
     }
     if (causal) {
-        if (dump) hipLaunchKernelGGL((k_bwd_dq<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<true, false>), grid, block, 0, st, a);
+        if (dump) hipLaunchKernelGGL((k_bwd_dq<true, false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<true, false, false>), grid, block, 0, st, a);
     } else {
-        if (dump) hipLaunchKernelGGL((k_bwd_dq<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<false, false>), grid, block, 0, st, a);
+        if (dump) hipLaunchKernelGGL((k_bwd_dq<false, false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<false, false, false>), grid, block, 0, st, a);
     }
     return 0;
 }

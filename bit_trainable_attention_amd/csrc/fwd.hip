@@ -24,11 +24,6 @@
 namespace sagebwd {
 
 constexpr int FWD_WAVES = 4;
-// Compile-time flag passed to the loop-step lambdas below.
-template <bool B>
-struct Flag {
-    static constexpr bool value = B;
-};
 
 constexpr float RESCALE_THRESHOLD = 8.0f;   // log2 units; O and L may grow by up to 2^8
 

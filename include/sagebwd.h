@@ -111,13 +111,10 @@ typedef struct sagebwd_params {
 #define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
 
 /* Workspace bytes needed by sagebwd_fwd / sagebwd_bwd for these params;
- * 0 if the params are invalid.  The forward's grows linearly with B*H*N.
- * The backward's also holds the INT8 dS codes of every computed 64x64 tile
- * of a group of heads (4096 bytes per tile: T(T+1)/2 tiles per head when
- * causal, T^2 otherwise, T = ceil(N/64)), which its dK/dV kernel writes and
- * its dQ kernel reads instead of recomputing them; a group is as many heads
- * as fit in 16 GiB of codes, at least one, the heads split evenly over the
- * groups (e.g. B=1, H=32, N=16384 causal: one group, 4.3 GB). */
+ * 0 if the params are invalid.  Both grow linearly with B*H*N (about 5.2
+ * bytes per element of Q for the forward and 10.3 for the backward: codes,
+ * block scales, per-token rows and FP16 copies); nothing of size N^2 is kept
+ * (e.g. B=1, H=32, N=16384 causal: 174 MB and 346 MB). */
 size_t sagebwd_fwd_workspace_size(const sagebwd_params* p);
 size_t sagebwd_bwd_workspace_size(const sagebwd_params* p);
 
@@ -153,18 +150,18 @@ int sagebwd_bwd(const sagebwd_params* p,
  * stage each, for callers that schedule or time them separately; a stage
  * reads what the earlier stages of its pass wrote into ``ws`` (same params,
  * inputs and workspace), and the full sequence is exactly the pass.
- * BWD_ATTN is BWD_DKDV then BWD_DQ for each head group in turn; BWD_DKDV and
- * BWD_DQ on their own return SAGEBWD_ERR_UNSUPPORTED when the backward has
- * more than one head group.
+ * BWD_ATTN is BWD_DKDV then BWD_DQ; the two are independent of each other
+ * (each recomputes the scores, P and dS it needs from the preparation's
+ * output) and may run in either order.
  *   FWD_PREPARE  smoothing means; Q, K, V block quantization
  *   FWD_ATTN     the fused forward kernel (INT8 QK^T and P~V)
  *   BWD_PREPARE  (without fwd_ws) means and quantization again; then
  *                -Delta, log2 LSE, dO codes, FP16 copies of dO and V
  *                (int8_dp: also row-layout dO codes, V codes and scales)
- *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T); also
- *                stores every tile's dS codes and scale in ws
- *   BWD_DQ       dQ (INT8 dS K from the stored dS codes)
- *   BWD_ATTN     BWD_DKDV and BWD_DQ over every head group */
+ *   BWD_DKDV     dK and dV (INT8 QK^T, P^T dO, dS^T Q; FP16 dO V^T)
+ *   BWD_DQ       dQ (INT8 QK^T and dS K; FP16 dO V^T): the same scores, P,
+ *                dS, tile scales and dS codes as BWD_DKDV, bit for bit
+ *   BWD_ATTN     BWD_DKDV then BWD_DQ */
 #define SAGEBWD_STAGE_FWD_PREPARE 0
 #define SAGEBWD_STAGE_FWD_ATTN    1
 #define SAGEBWD_STAGE_BWD_PREPARE 2
@@ -214,18 +211,10 @@ const char* sagebwd_status_string(int status);
  *   19 V_R    int8  [BH][T][4096]    V codes, row operand layout (int8_dp only)
  *   20 RQ     float32 [BH][Np]       QK-norm factor r of each Q token (qk_norm only; 0 past N)
  *   21 RK     float32 [BH][Np]       likewise for K
- *   22 DS     int8  [G][tiles][4096] dS codes of one head group (G heads), tile
- *                                    (i, t) at i(i+1)/2 + t causal, i T + t
- *                                    otherwise; in a tile, 16-byte chunk
- *                                    (kh*2 + qs)*64 + l holds key 32 kh + l%32
- *                                    and byte b the query
- *                                    32 qs + 8(b/4) + 4(l/32) + b%4
- *   23 DS_SCALE float32 [G][tiles]   their block scales s_dS
  * with T = ceil(N/64), Np = 64 T.  With mxfp8 the code regions hold E4M3
  * code bytes in the same layouts, and each 4-byte block scale (regions 8-11)
  * holds the four biased exponents e + 127 of the block's 32x32 sub-blocks,
- * byte 2*(r/32) + c/32 (token half, channel half); a DS_SCALE entry holds
- * those of its dS tile, byte 2*(key half) + query half.  With fp4 the
+ * byte 2*(r/32) + c/32 (token half, channel half).  With fp4 the
  * regions Q_R, K_R and V_T hold FP4 blocks in their 4096-byte slots: 2048
  * bytes of E2M1 codes (two per byte, the first in the low nibble), then 128
  * exponent bytes e + 127.  Q_R, K_R: 16-byte chunk th*64 + 32h + m holds the
@@ -253,8 +242,8 @@ const char* sagebwd_status_string(int status);
  *     P^T dO i32[k][c] at 36864, dS f32[q][k] at 53248, dS codes u8[q][k] at
  *     69632, dS^T Q i32[k][c] at 73728, s_P and s_dS f32 at 90112
  *   kernel 2 (dQ; runs the backward preparation and the dK/dV kernel first;
- *     writes dK, dV, dQ): the dS codes it read, transposed, u8[q][k] at
- *     32768, dS K i32[q][c] at 36864, s_dS f32 at 90112
+ *     writes dK, dV, dQ): A at 0, dS f32[q][k] at 53248, its dS codes
+ *     u8[q][k] at 32768, dS K i32[q][c] at 36864, s_dS f32 at 90112
  * (q, k: query and key within the blocks; c: channel), so that the INT8
  * codes, block scales and integer tile products can be re-derived exactly
  * from the kernel's own pre-quantization values.  Tiles above the causal

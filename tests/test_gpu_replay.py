@@ -12,8 +12,9 @@ values exactly:
   fwd    P~ codes = rne(127 P^) of the dumped values, P~V = codes V_code
   dkdv   s_P, P codes = F3 of the dumped P; P^T dO = codes^T dO_code;
          s_dS, dS codes = F3 of the dumped dS; dS^T Q = codes^T Q_code
-  dq     the dS codes and scale the dK/dV kernel stored, after its
-         transposition (bit for bit); dS K = codes K_code
+  dq     A, the dS values, s_dS and the dS codes, recomputed in the
+         forward's layout, bit for bit equal to the dK/dV kernel's;
+         dS K = codes K_code
 The codes the oracle forms from its own float64 P~, P and dS agree except at
 rounding boundaries; that rate is reported and bounded.
 
@@ -129,13 +130,16 @@ def test_tile_replay_bitexact(name, w, bh, tiles, int8_dp):
         assert np.array_equal(_blk(d1, C2, np.int8).astype(np.int64), cdS.astype(np.int64)), ("dS codes", i, t)
         assert np.array_equal(_blk(d1, ACC2, np.int32).astype(np.int64),
                               (cdS.T @ pp.qc[rows]).astype(np.int64)), ("dS^T Q", i, t)
-        # ---- dQ kernel: the dK/dV kernel's dS codes and scale, read back and
-        # transposed, bit for bit
+        # ---- dQ kernel: it recomputes the tile in the forward's layout; its
+        # score integers, dS values, scale and codes are bitwise the dK/dV
+        # kernel's, and its dS K product is exact
         d2, g2 = sb.debug_tile("dq", bh, i, t, tq, tk, tv, to, tlse, tdo, w.causal, w.smooth_q, w.smooth_k,
                                int8_dp, return_grads=True)
         d2 = d2.numpy().tobytes()
         assert torch.equal(g2[0][b, h].view(torch.int16), pgrads[0][b, h].view(torch.int16)), ("dQ prod", i, t)
-        assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32)
+        assert np.array_equal(_blk(d2, A, np.int32), a_ref.astype(np.int32)), ("dq A", i, t)
+        assert np.array_equal(_blk(d2, F2, np.uint32), _blk(d1, F2, np.uint32)), ("dq dS values", i, t)
+        assert np.frombuffer(d2, np.float32, 1, SC)[0].view(np.uint32) == sc1[1].view(np.uint32), ("dq s_dS", i, t)
         assert np.array_equal(_blk(d2, C1, np.int8), _blk(d1, C2, np.int8)), ("dq codes", i, t)
         assert np.array_equal(_blk(d2, ACC1, np.int32).astype(np.int64),
                               (cdS @ pp.kc[cols]).astype(np.int64)), ("dS K", i, t)
