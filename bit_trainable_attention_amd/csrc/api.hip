@@ -255,7 +255,7 @@ BwdArgs bwd_args(const sagebwd_params& p, const Layout& L, const QkSource& qk, v
 void run_bwd_attn(const sagebwd_params& p, const BwdArgs& a, int which, int kernel_dump, hipStream_t st) {
     const int BH = p.B * p.H;
     if (which & 1) launch_bwd_dkdv(a, BH, p.causal, p.smooth_q, p.int8_dp, p.mxfp8, st, kernel_dump == 1);
-    if (which & 2) launch_bwd_dq(a, BH, p.causal, p.mxfp8, st, kernel_dump == 2);
+    if (which & 2) launch_bwd_dq(a, BH, p.causal, p.int8_dp, p.mxfp8, st, kernel_dump == 2);
 }
 
 }  // namespace

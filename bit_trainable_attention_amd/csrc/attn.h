@@ -57,7 +57,8 @@ int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hi
 // mx: MXFP8 codes and block exponents (neither int8_dp nor a tile dump)
 int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool int8_dp, bool mx, hipStream_t st,
                     bool dump = false);
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump = false);
+// int8_dp, mx: as launch_bwd_dkdv (the dQ kernel recomputes dS the same way)
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool int8_dp, bool mx, hipStream_t st, bool dump = false);
 
 template <class T>
 __device__ __forceinline__ T* dump_at(uint8_t* d, int off) { return (T*)(d + off); }

@@ -535,9 +535,10 @@ constexpr int DQ_BUFS = 3;
 struct DqSmem {
     v4i k[DQ_BUFS][256];     // K row-operand codes (A operand of K Q^T)
     v4i kt[DQ_BUFS][256];    // K transposed codes (A operand of K^T dS^T)
-    v8h v16[DQ_BUFS][512];   // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T)
+    v8h v16[DQ_BUFS][512];   // V in FP16, [64 rows][8 chunks], swizzled (A operand of V dO^T);
+                             // all-INT8 dO V^T: V row-operand codes in its first 4 KB
     float bias[DQ_BUFS][64]; // Q-smoothing key bias (log2 domain; 0 without Q-smoothing)
-    float sk[DQ_BUFS][4];    // [0]: K block scale (MXFP8: its four exponent bytes)
+    float sk[DQ_BUFS][4];    // [0]: K block scale (MXFP8: its exponent word), [1]: V block scale (all-INT8)
     float red[2][4];         // partial |dS| maxima per wave, by step parity (INT8)
 };
 
@@ -591,69 +592,77 @@ __device__ __forceinline__ void dq_epilogue(const BwdArgs& a, v16f (&dq)[2], int
 struct DqQuery {
     v4i qop[2];       // Q row-operand codes (B operand of K Q^T)
     v8h dob[4];       // dO in FP16, channels 16 ks + 8 h .. + 7 (B operand of V dO^T)
-    v16f nd;          // -Delta of this lane's query in every register (accumulator input of V dO^T)
+    v4i dor[2];       // all-INT8 dO V^T: dO row-operand codes (B operand of V dO^T)
     float brow;       // B operand of the rank-2 score correction: -lse2 (h = 0) or 1 (h = 1)
-    uint32_t qw;      // Q block scale (MXFP8: exponent word)
+    float bnd;        // B operand of the rank-1 product that puts -Delta in every row: -Delta (h = 0) or 0
+    float sdo;        // dO block scale (all-INT8 dO V^T)
+    uint32_t qw;      // Q block scale (MXFP8: the exponent bytes of this half, channel halves 0, 1)
 };
 
 // One key-block step of one wave up to the dS values: scores, P, dP - Delta
 // and dS = P (dP - Delta) for 32 queries x 64 keys (lane = query, registers
-// = keys 32 kb + 8 (r/4) + 4 h + r%4).  MASK only for the causal diagonal
-// tile and the ragged last key block.
-template <bool CAUSAL, bool MASK, bool MX>
+// = keys 32 kb + 8 (r/4) + 4 h + r%4), one 32-key half after the other.
+// MASK only for the causal diagonal tile and the ragged last key block.
+template <bool CAUSAL, bool MASK, bool MX, bool INT8DP>
 __device__ __forceinline__ void dq_scores(const DqSmem& sm, int buf, const DqQuery& qd, int t, int q, int N, int lane,
                                           int h, float (&ds)[2][16], int (&sdump)[2][16], bool dump) {
     const int l32 = lane % 32;
-    v16f corr[2], dpd[2];
-    v16i s[2];
-    v16f sx[2];
     const uint32_t kw = __float_as_uint(sm.sk[buf][0]);
+    const float sc = MX ? SCORE_SCALE_LOG2 : tile_scale(__uint_as_float(qd.qw), sm.sk[buf][0]);
+    const float wdp = INT8DP ? qd.sdo * sm.sk[buf][1] : 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+        v16i s;
+        v16f sx;
         if (MX) {
             const v8i ka = cat8(sm.k[buf][(kb * 2 + 0) * 64 + lane], sm.k[buf][(kb * 2 + 1) * 64 + lane]);
-            sx[kb] = mfma_fp8(ka, cat8(qd.qop[0], qd.qop[1]), v16f{}, ebyte(kw, 2 * kb + h), ebyte(qd.qw, h));
+            sx = mfma_fp8(ka, cat8(qd.qop[0], qd.qop[1]), v16f{}, ebyte(kw, 2 * kb + h), ebyte(qd.qw, h));
         } else {
-            s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qd.qop[0], v16i{});
-            s[kb] = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qd.qop[1], s[kb]);
+            s = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qd.qop[0], v16i{});
+            s = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qd.qop[1], s);
         }
-    }
-    // bias_j - lse2_i as [1 | bias] [-lse2 | 1]^T on the FP32 MFMA (32x32x2:
-    // lane l carries A[l%32][l/32] and B[l/32][l%32])
+        // bias_j - lse2_i as [1 | bias] [-lse2 | 1]^T on the FP32 MFMA
+        // (32x32x2: lane l carries A[l%32][l/32] and B[l/32][l%32]), and
+        // -Delta_i in every row as [1 | 0] [-Delta | 0]^T
+        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow,
+                                                               v16f{}, 0, 0, 0);
+        const v16f nd = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : 0.0f, qd.bnd, v16f{}, 0, 0, 0);
+        // dP^T - Delta: the key-block kernel's products with the operands
+        // swapped, the same channels in the same k steps from the same -Delta
+        v16f dpd;
+        if (INT8DP) {
+            const v4i* vr = (const v4i*)sm.v16[buf];
+            v16i ai = mfma_i8(vr[(kb * 2 + 0) * 64 + lane], qd.dor[0], v16i{});
+            ai = mfma_i8(vr[(kb * 2 + 1) * 64 + lane], qd.dor[1], ai);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-        corr[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow, v16f{},
-                                                        0, 0, 0);
-    // dP^T - Delta = V dO^T + (-Delta): the key-block kernel's four FP16
-    // MFMAs with the operands swapped (the same channel chunk per k step)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int row = 32 * kb + l32;
-        v16f d = mfma_f16(sm.v16[buf][swz(row, 0 + h)], qd.dob[0], qd.nd);
-        d = mfma_f16(sm.v16[buf][swz(row, 2 + h)], qd.dob[1], d);
-        d = mfma_f16(sm.v16[buf][swz(row, 4 + h)], qd.dob[2], d);
-        dpd[kb] = mfma_f16(sm.v16[buf][swz(row, 6 + h)], qd.dob[3], d);
-    }
-    const float sc = MX ? SCORE_SCALE_LOG2 : tile_scale(__uint_as_float(qd.qw), sm.sk[buf][0]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+            for (int r = 0; r < 16; ++r) dpd[r] = __builtin_fmaf((float)ai[r], wdp, nd[r]);
+        } else {
+            const int row = 32 * kb + l32;
+            dpd = mfma_f16(sm.v16[buf][swz(row, 0 + h)], qd.dob[0], nd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 2 + h)], qd.dob[1], dpd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 4 + h)], qd.dob[2], dpd);
+            dpd = mfma_f16(sm.v16[buf][swz(row, 6 + h)], qd.dob[3], dpd);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            if (!MX && dump) sdump[kb][r] = s[kb][r];
-            const float sv = MX ? sx[kb][r] : (float)s[kb][r];
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc, corr[kb][r]));
+            if (!MX && dump) sdump[kb][r] = s[r];
+            const float sv = MX ? sx[r] : (float)s[r];
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc, corr[r]));
             if (MASK) {
                 asm volatile("" : "+v"(pv));   // a select, not a branch around each exp
                 const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
                 pv = (key >= N || (CAUSAL && key > q)) ? 0.0f : pv;
             }
-            ds[kb][r] = pv * dpd[kb][r];
+            ds[kb][r] = pv * dpd[r];
         }
+        // the second half's MFMAs wait until the first half is done, so the
+        // two halves' accumulators are never live at once
+        if (kb == 0) __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <bool CAUSAL, bool MX, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
+template <bool CAUSAL, bool MX, bool INT8DP, bool DUMP>
+__global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     __shared__ DqSmem sm;
     const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: per-wave values live in SGPRs
@@ -671,40 +680,51 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
     const int q = qblk * BLK + 32 * qhalf + l32;                    // this lane's query (padded index)
 
     DqQuery qd;
-    qd.qop[0] = qd.qop[1] = v4i{};
+    qd.qop[0] = qd.qop[1] = qd.dor[0] = qd.dor[1] = v4i{};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qd.dob[ks] = v8h{};
     float ndl = 0.0f, lse2 = 0.0f;
     qd.qw = 0;
+    qd.sdo = 0.0f;
     if (live) {
         const v4i* src = (const v4i*)(a.q_r + (bt + qblk) * 4096);
         qd.qop[0] = src[(qhalf * 2 + 0) * 64 + lane];
         qd.qop[1] = src[(qhalf * 2 + 1) * 64 + lane];
+        if (INT8DP) {
+            const v4i* dsrc = (const v4i*)(a.do_r + (bt + qblk) * 4096);
+            qd.dor[0] = dsrc[(qhalf * 2 + 0) * 64 + lane];
+            qd.dor[1] = dsrc[(qhalf * 2 + 1) * 64 + lane];
+            qd.sdo = a.sdo[bt + qblk];
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qd.dob[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+            for (int ks = 0; ks < 4; ++ks) qd.dob[ks] = *(const v8h*)(a.do16 + (rowbase + q) * HD + 16 * ks + 8 * h);
+        }
         ndl = a.delta[rowbase + q];
         lse2 = a.lse2[rowbase + q];
         const uint32_t w = ((const uint32_t*)a.sq)[bt + qblk];
         qd.qw = MX ? (uint32_t)ebyte(w, 2 * qhalf + 0) | ((uint32_t)ebyte(w, 2 * qhalf + 1) << 8) : w;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) qd.nd[r] = ndl;
     qd.brow = h == 0 ? -lse2 : 1.0f;
+    qd.bnd = h == 0 ? ndl : 0.0f;
 
     const v4i* kg = (const v4i*)(a.k_r + bt * 4096);
     const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
     auto fetch = [&](int t, int b) {
         dma16_to_lds(kg + (size_t)t * 256 + tid, &sm.k[b][64 * wave]);
         dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.kt[b][64 * wave]);
-        // LDS slot s of the FP16 V tile holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
-        const v4i* hs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
+        if (INT8DP) {
+            dma16_to_lds((const v4i*)(a.v_r + bt * 4096) + (size_t)t * 256 + tid, (v4i*)sm.v16[b] + 64 * wave);
+        } else {
+            // LDS slot s of the FP16 V tile holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
+            const v4i* hs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int s = 256 * j + tid, row = s / 8;
-            dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+            for (int j = 0; j < 2; ++j) {
+                const int s = 256 * j + tid, row = s / 8;
+                dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
+            }
         }
         if (wave == 2 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
-        if (wave == 3 && lane == 0) dma4_to_lds(a.sk + bt + t, &sm.sk[b][0]);
+        if (wave == 3 && lane < (INT8DP ? 2 : 1)) dma4_to_lds((lane == 0 ? a.sk : a.sv) + bt + t, &sm.sk[b][0]);
     };
 
     v16f dq[2] = {v16f{}, v16f{}};   // [db]: lane = query, registers = channels 32 db + 8 (r/4) + 4 h + r%4
@@ -719,9 +739,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq(BwdArgs a) {
         uint8_t* dp = (DUMP && dp_sel && t == a.dump_t) ? dp_sel : nullptr;
         if (active) {
             if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
-                dq_scores<CAUSAL, true, MX>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
+                dq_scores<CAUSAL, true, MX, INT8DP>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
             else
-                dq_scores<CAUSAL, false, MX>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
+                dq_scores<CAUSAL, false, MX, INT8DP>(sm, buf, qd, t, q, a.N, lane, h, ds, sd, DUMP && dp);
             if (DUMP && dp) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -1092,19 +1112,22 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
 
 #undef SAGEBWD_LAUNCH_BWD
 
-int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool mx, hipStream_t st, bool dump) {
+int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool int8_dp, bool mx, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
     if (mx) {
-        if (causal) hipLaunchKernelGGL((k_bwd_dq<true, true, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<false, true, false>), grid, block, 0, st, a);
+        if (causal) hipLaunchKernelGGL((k_bwd_dq<true, true, false, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_bwd_dq<false, true, false, false>), grid, block, 0, st, a);
         return 0;
     }
-    if (causal) {
-        if (dump) hipLaunchKernelGGL((k_bwd_dq<true, false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<true, false, false>), grid, block, 0, st, a);
-    } else {
-        if (dump) hipLaunchKernelGGL((k_bwd_dq<false, false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<false, false, false>), grid, block, 0, st, a);
+    switch ((causal ? 4 : 0) | (int8_dp ? 2 : 0) | (dump ? 1 : 0)) {
+        case 0: hipLaunchKernelGGL((k_bwd_dq<false, false, false, false>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((k_bwd_dq<false, false, false, true>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_bwd_dq<false, false, true, false>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((k_bwd_dq<false, false, true, true>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_bwd_dq<true, false, false, false>), grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL((k_bwd_dq<true, false, false, true>), grid, block, 0, st, a); break;
+        case 6: hipLaunchKernelGGL((k_bwd_dq<true, false, true, false>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((k_bwd_dq<true, false, true, true>), grid, block, 0, st, a); break;
     }
     return 0;
 }
