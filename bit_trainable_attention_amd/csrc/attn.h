@@ -24,6 +24,10 @@ template <bool B>
 struct Flag {
     static constexpr bool value = B;
 };
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 struct FwdArgs {
     const int8_t *q_r, *k_r, *v_t;     // code blocks [BH][T][4096]

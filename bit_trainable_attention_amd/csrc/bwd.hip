@@ -317,8 +317,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     wait_vmem();
     lds_barrier();
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
-    for (int i = i0; i < T; ++i) {
-        const int buf = (i - i0) & 1;
+    // the loop runs two query blocks per iteration so that each one's LDS
+    // buffer is a compile-time constant (every LDS address is then a base
+    // register plus an immediate offset)
+    auto step = [&](int i, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const bool more = i + 1 < T;
         const bool active = live && (!CAUSAL || i >= kvb);
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
@@ -458,7 +461,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             }
         }
         lds_barrier();
+    };
+    int i = i0;
+    for (; i + 1 < T; i += 2) {
+        step(i, IntC<0>{});
+        step(i + 1, IntC<1>{});
     }
+    if (i < T) step(i, IntC<0>{});
 
     // epilogue: dK (x 1/8, plus colsum(dS) mu_q for Q-smoothing) and dV in bf16;
     // lane = channel, registers = keys of this wave's half block
@@ -731,8 +740,11 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
     const int qloc = 32 * qhalf + l32;
 
-    auto step = [&](int t, auto maybe_masked) {
-        const int buf = t % DQ_BUFS;
+    // bufc: IntC<b> when the step's LDS buffer b = t % 3 is known at compile
+    // time (the main loop runs three steps per iteration, so every LDS address
+    // is a base register plus an immediate), IntC<-1> otherwise
+    auto step = [&](int t, auto maybe_masked, auto bufc) {
+        const int buf = decltype(bufc)::value >= 0 ? decltype(bufc)::value : t % DQ_BUFS;
         const bool active = t <= t_last;
         float ds[2][16];
         int sd[2][16];
@@ -838,8 +850,13 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
     // own and the main loop carries one form of the step.
     const int t_tail = t_last_wg > 1 ? t_last_wg - 1 : 0;
     int t = 0;
-    for (; t < t_tail; ++t) step(t, Flag<false>{});
-    for (; t <= t_last_wg; ++t) step(t, Flag<true>{});
+    for (; t + 2 < t_tail; t += 3) {
+        step(t, Flag<false>{}, IntC<0>{});
+        step(t + 1, Flag<false>{}, IntC<1>{});
+        step(t + 2, Flag<false>{}, IntC<2>{});
+    }
+    for (; t < t_tail; ++t) step(t, Flag<false>{}, IntC<-1>{});
+    for (; t <= t_last_wg; ++t) step(t, Flag<true>{}, IntC<-1>{});
     if (!live) return;
     dq_epilogue(a, dq, bh, q, h, rowbase);
 }
