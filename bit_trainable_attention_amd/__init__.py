@@ -77,6 +77,8 @@ def load_library() -> ctypes.CDLL:
         lib.sagebwd_prepare.restype = ctypes.c_int
         lib.sagebwd_ws_region.argtypes = [_P, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]
         lib.sagebwd_ws_region.restype = ctypes.c_int
+        lib.sagebwd_fwd_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.sagebwd_fwd_noalloc.restype = ctypes.c_int
         lib.sagebwd_check_block_scale.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp]
         lib.sagebwd_check_block_scale.restype = ctypes.c_int
         lib.sagebwd_status_string.argtypes = [ctypes.c_int]

@@ -4,6 +4,7 @@
 #include "sagebwd.h"
 
 #include <algorithm>
+#include <mutex>
 
 #include "attn.h"
 #include "prep.h"
@@ -110,6 +111,28 @@ T* region(void* ws, const Layout& L, int r) {
 }
 
 int hip_status() { return hipGetLastError() == hipSuccess ? SAGEBWD_OK : SAGEBWD_ERR_HIP; }
+
+// The workspace of sagebwd_fwd_noalloc: one static device array, which each
+// GPU holds at its own address.  Host code never uses the array's name as a
+// device pointer: the address of each device's copy is looked up once, with
+// that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[SAGEBWD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+
+// Address of this device's copy of the scratch array, or null on failure.
+void* scratch_ptr(int device) {
+    static std::mutex mu;
+    static void* ptrs[SCRATCH_MAX_DEVICES] = {};
+    if (device < 0 || device >= SCRATCH_MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[device]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptrs[device] = ptr;
+    }
+    return ptrs[device];
+}
 
 int operand_format(const sagebwd_params& p) { return p.fp4 ? FMT_FP4 : p.mxfp8 ? FMT_MXFP8 : FMT_INT8; }
 
@@ -279,6 +302,7 @@ const char* sagebwd_status_string(int status) {
         case SAGEBWD_ERR_UNSUPPORTED: return "unsupported shape";
         case SAGEBWD_ERR_WORKSPACE: return "workspace too small";
         case SAGEBWD_ERR_HIP: return "HIP launch error";
+        case SAGEBWD_ERR_SCRATCH: return "workspace exceeds the built-in scratch buffer";
         default: return "unknown status";
     }
 }
@@ -309,6 +333,23 @@ int sagebwd_fwd(const sagebwd_params* p, const void* Q, const void* K, const voi
     int rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream);
     if (rc) return rc;
     return sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_ATTN, Q, K, V, O, LSE, ws, ws_bytes, stream);
+}
+
+int sagebwd_fwd_noalloc(const sagebwd_params* p, const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        void* stream) {
+    int rc = check_params(p);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, (const void*)O}) {
+        if ((rc = check_tensor(t))) return rc;
+    }
+    if (!LSE || !aligned(LSE, 4)) return SAGEBWD_ERR_INVALID_ARG;
+    const size_t need = make_layout(*p, PASS_FWD).total;
+    if (need > SAGEBWD_NOALLOC_SCRATCH_BYTES) return SAGEBWD_ERR_SCRATCH;
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) return SAGEBWD_ERR_HIP;
+    void* ws = scratch_ptr(device);
+    if (!ws) return SAGEBWD_ERR_HIP;
+    return sagebwd_fwd(p, Q, K, V, O, LSE, ws, SAGEBWD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int sagebwd_bwd_stage(const sagebwd_params* p, int stage, const void* Q, const void* K, const void* V,

@@ -109,6 +109,8 @@ typedef struct sagebwd_params {
                                           combination or an entry point the modes do not have */
 #define SAGEBWD_ERR_WORKSPACE   (-3)   /* ws_bytes smaller than the required size */
 #define SAGEBWD_ERR_HIP         (-4)   /* the HIP runtime reported a launch error */
+#define SAGEBWD_ERR_SCRATCH     (-5)   /* sagebwd_fwd_noalloc: the problem's workspace exceeds
+                                          SAGEBWD_NOALLOC_SCRATCH_BYTES */
 
 /* Workspace bytes needed by sagebwd_fwd / sagebwd_bwd for these params;
  * 0 if the params are invalid.  Both grow linearly with B*H*N (about 5.2
@@ -178,6 +180,27 @@ int sagebwd_bwd_stage(const sagebwd_params* p, int stage,
                       void* dQ, void* dK, void* dV,
                       const void* fwd_ws, size_t fwd_ws_bytes,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* Forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It is sagebwd_fwd with its workspace taken from a
+ * buffer compiled into the library: a static device array of
+ * SAGEBWD_NOALLOC_SCRATCH_BYTES (256 MiB) that every GPU the library runs on
+ * holds until the process ends.  The call allocates nothing: on its first use
+ * on a device it looks the array's address up once (hipGetSymbolAddress) and
+ * keeps it.  Inputs and outputs are the caller's, as for sagebwd_fwd.
+ * Returns SAGEBWD_ERR_SCRATCH, before any HIP call, when
+ * sagebwd_fwd_workspace_size(p) exceeds the buffer (e.g. B=1, H=32, N=16384
+ * needs 174 MB and fits; B=1, H=32, N=32768 does not).  The buffer is shared
+ * by every call on a GPU and keeps the last call's contents (the forward
+ * overwrites everything it reads), so calls that overlap on one GPU (on
+ * different streams, or from different threads) race; calls in stream order
+ * do not.  A backward cannot reuse this forward's quantization (pass
+ * fwd_ws = NULL to sagebwd_bwd). */
+#define SAGEBWD_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int sagebwd_fwd_noalloc(const sagebwd_params* p,
+                        const void* Q, const void* K, const void* V,
+                        void* O, float* LSE, void* stream);
 
 /* Static description of a status code. */
 const char* sagebwd_status_string(int status);

@@ -164,7 +164,8 @@ def test_ws_regions_layout(lib, int8_dp, qk_norm, mxfp8):
 
 def test_status_strings(lib):
     for rc, s in ((OK, b"ok"), (INVALID, b"invalid argument"), (UNSUPPORTED, b"unsupported shape"),
-                  (WORKSPACE, b"workspace too small"), (HIPERR, b"HIP launch error"), (-99, b"unknown status")):
+                  (WORKSPACE, b"workspace too small"), (HIPERR, b"HIP launch error"),
+                  (-5, b"workspace exceeds the built-in scratch buffer"), (-99, b"unknown status")):
         assert lib.sagebwd_status_string(rc) == s
 
 
@@ -231,3 +232,20 @@ def test_block_scale_check_validation(lib):
         assert lib.sagebwd_check_block_scale(lo, hi, FAKE, None, None, None) == INVALID
     assert lib.sagebwd_check_block_scale(0, 0, None, None, None, None) == INVALID
     assert lib.sagebwd_check_block_scale(0, 0, FAKE, FAKE, None, None) == INVALID
+
+
+def test_noalloc_forward_validation(lib):
+    """sagebwd_fwd_noalloc validates like sagebwd_fwd and rejects a problem
+    whose workspace exceeds the 256 MiB scratch buffer, all before any HIP
+    call."""
+    f = lambda p, *ptrs: lib.sagebwd_fwd_noalloc(ctypes.byref(p) if p is not None else None, *ptrs, None)
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert f(P(), None, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert f(P(), FAKE + 8, FAKE, FAKE, FAKE, FAKE) == INVALID
+    assert f(P(), FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(P(D=32), FAKE, FAKE, FAKE, FAKE, FAKE) == UNSUPPORTED
+    big = P(B=1, H=32, N=32768, causal=1)
+    assert lib.sagebwd_fwd_workspace_size(ctypes.byref(big)) > (256 << 20)
+    assert f(big, FAKE, FAKE, FAKE, FAKE, FAKE) == -5
+    fits = P(B=1, H=32, N=16384, causal=1, smooth_q=1)
+    assert lib.sagebwd_fwd_workspace_size(ctypes.byref(fits)) <= (256 << 20)
