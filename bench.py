@@ -51,9 +51,10 @@ def source_sha(stage: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(stage: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+def load_profile(stage: str, workload: str):
+    """The committed rocprofv3 summary of one kernel on one workload (HBM
+    bytes per launch, the profiled average duration, the shader clock measured
+    under load), if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"counters_{stage.lower()}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -61,7 +62,7 @@ def load_traffic(stage: str, workload: str):
         c = json.load(fh)
     if c.get("source_sha") != source_sha(stage):
         return None
-    return c.get("hbm_bytes_per_launch")
+    return c
 
 
 def cpu_baseline(w, seconds: float, mode: str = "int8"):
@@ -95,10 +96,11 @@ def cpu_baseline(w, seconds: float, mode: str = "int8"):
     el = time.perf_counter() - t0
     ops = done_heads * (4.0 if mode == "fp4" else 14.0) * n * n * 64 * (0.5 if w.causal else 1.0)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": cores, "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{'faithful' if mode == 'int8' else mode} {'fwd' if mode == 'fp4' else 'fwd+bwd'} of {done_heads} whole head(s) of the first {n} tokens of {w.name} "
-                      f"(causal={w.causal}) in {el:.1f} s; {os.cpu_count()} host cores visible, "
-                      f"BLAS threads {threads}"}
+                      f"(causal={w.causal}) in {el:.1f} s; {cores} host cores available to the process "
+                      f"({os.cpu_count()} in the machine), BLAS threads {threads}"}
 
 
 def main():
@@ -197,10 +199,21 @@ def main():
     dom = max((s for s in KERNEL_UNITS if s in stage_ms), key=lambda s: stage_ms[s])
     ach = KERNEL_UNITS[dom] * unit / (stage_ms[dom] * 1e-3) / 1e12
     peak = FP4_PEAK_TOPS if args.fp4 else INT8_PEAK_TOPS
+    prof = None if (args.int8_dp or args.qk_norm or args.no_reuse) else load_profile(dom, w.name + mode_suffix)
     roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(ach / peak, 4),
-            "traffic": None if (args.int8_dp or args.qk_norm) else load_traffic(dom, w.name + mode_suffix),
+            "traffic": prof.get("hbm_bytes_per_launch") if prof else None,
             "avg_launch_ms": round(stage_ms[dom], 4)}
+    if prof:
+        # the same kernel's average duration in the committed rocprofv3 kernel
+        # statistics, and the fraction it gives; the shader clock measured under
+        # load (GRBM_GUI_ACTIVE cycles of one XCD over the kernel's duration)
+        # and the fraction of the peak at that clock (the peak scales with it)
+        ach_p = KERNEL_UNITS[dom] * unit / (prof["avg_ms_profile"] * 1e-3) / 1e12
+        roof["avg_launch_ms_profile"] = round(prof["avg_ms_profile"], 4)
+        roof["frac_profile"] = round(ach_p / peak, 4)
+        roof["sclk_mhz_measured"] = round(prof["sclk_mhz"], 0)
+        roof["frac_at_measured_sclk"] = round(ach / (peak * prof["sclk_mhz"] / 2400.0), 4)
     out = {
         "metric": METRIC_FP4 if args.fp4 else METRIC,
         "value": round(tops, 2),
