@@ -8,21 +8,23 @@
 // findings") keeps dO V^T in FP16 because quantizing it hurts dQ.  The
 // gradient formulas are FlashAttention-2's (under "Builds on").
 //
-// Two kernels, no atomics, bitwise repeatable:
+// Two kernels, no atomics, bitwise repeatable, nothing of size N^2 kept
+// between them:
 //   k_bwd_dkdv  a workgroup of 4 waves owns two 64-key blocks (each wave 32
 //               keys) and walks the query blocks.  It computes S (lane = key),
 //               so P and dS codes leave the accumulator as the A operand of
-//               P^T dO and dS^T Q (contraction over queries).  It also stores
-//               every tile's dS codes and scale in the workspace.
-//   k_bwd_dq    each wave owns one 64-query block and streams its stored dS
-//               codes: dQ = sum_t s_dS s_K (dS codes K codes), with no
-//               recomputation of S, P or dS; the four waves of a workgroup
-//               share each key block's K^T codes through LDS.
+//               P^T dO and dS^T Q (contraction over queries).
+//   k_bwd_dq    a workgroup of 4 waves owns two 64-query blocks (each wave 32
+//               queries) and walks the key blocks.  It recomputes S, P,
+//               dP - Delta and dS in the forward's layout (lane = query), so
+//               the dS codes leave the accumulator as the B operand of
+//               dQ^T = K^T dS^T (contraction over keys); its dS values and
+//               codes are bitwise the key-block kernel's.
 // A 64x64 quantization tile of P or dS is held by a pair of waves, which
 // exchange their partial maxima through LDS.  The streamed operand tiles go
-// through double-buffered LDS, fetched one step ahead; FP16 rows are stored
-// with their 16-byte chunks XOR-swizzled by row so column reads do not
-// collide on LDS banks.
+// global -> LDS by DMA (two buffers in the key-block kernel, three in the dQ
+// kernel); FP16 rows are stored with their 16-byte chunks XOR-swizzled by row
+// so column reads do not collide on LDS banks.
 #include "attn.h"
 
 namespace sagebwd {
@@ -868,9 +870,9 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
 // multiply).  A 32x32 block of P or dS (32 queries of one half of the query
 // block x the 32 keys of one wave) lies within one wave, so the block maxima
 // need no exchange between waves, and the key-block kernel synchronizes once
-// per query block (double-buffered operand tiles).  The dS codes handed to
-// the dQ kernel carry four exponent bytes per tile (byte 2 * key half + query
-// half) in the slot of the INT8 block scale.
+// per query block (double-buffered operand tiles).  The dQ kernel is the
+// INT8 one's recomputing kernel instantiated for E4M3 codes: its 32x32 dS
+// blocks (32 queries of a wave x one 32-key half) also lie within one wave.
 
 struct DkdvMxSmem {
     v4i q_r[2][256];     // Q row-operand codes (A operand of Q K^T)
