@@ -152,30 +152,26 @@ struct DkdvSmem {
 
 // P for one 64-query x 32-key half tile in the S layout (lane = key,
 // registers = queries): P = exp2(sc A + (bias_j - lse2_i)), log2 domain.  The
-// outer difference bias_j - lse2_i is the rank-2 product [-lse2 | 1] [1 | bias]^T,
-// formed on the FP32 MFMA (32x32x2: lane l carries A[l%32][l/32] and
-// B[l/32][l%32]) in the accumulator layout of the score product, so each score
-// costs one FMA before its exp.  MASK only on the causal diagonal tile and the
-// ragged last key block, so the common path carries no per-element selects
-// (a masked P is a select after its exp, not a branch around it).
+// outer difference bias_j - lse2_i is one subtraction per score (this lane's
+// key bias minus the query's lse2, read from LDS while the score MFMAs run;
+// as an FP32 rank-2 MFMA it sat in the score's dependency chain and was
+// slower), then one FMA before the exp.  MASK only on the causal diagonal tile
+// and the ragged last key block, so the common path carries no per-element
+// selects (a masked P is a select after its exp, not a branch around it).
 // dP - Delta (the same layout) is formed here too: it does not depend on P, so
 // its MFMAs are scheduled one by one between groups of the score arithmetic
 // instead of stalling the wave later.
 template <bool CAUSAL, bool MASK, bool INT8DP>
-__device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float brow,
+__device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4i (&kop)[2], float sc, float kbias,
                                            int i, int key, int N, int lane, int h, float (&p)[2][16],
                                            v16f (&dpd)[2], const v8h (&vh)[4], const v4i (&vop)[2], float sV,
                                            uint8_t* dp = nullptr) {
-    // all operands first (the LSE row is read by every lane, so no divergent
-    // branch splits the reads from the MFMAs), then both query halves' MFMAs
+    // the score operands first, then both query halves' MFMAs
     v4i qa[2][2];
-    float lv[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         qa[qb][0] = sm.q_r[buf][(qb * 2 + 0) * 64 + lane];
         qa[qb][1] = sm.q_r[buf][(qb * 2 + 1) * 64 + lane];
-        lv[qb] = sm.lse2[buf][32 * qb + lane % 32];
-        asm volatile("" : "+v"(lv[qb]));
     }
     v16i s[2];
     v16f corr[2];
@@ -183,9 +179,17 @@ __device__ __forceinline__ void dkdv_probs(const DkdvSmem& sm, int buf, const v4
     s[1] = mfma_i8(qa[1][0], kop[0], v16i{});
     s[0] = mfma_i8(qa[0][1], kop[1], s[0]);
     s[1] = mfma_i8(qa[1][1], kop[1], s[1]);
+    // bias_j - lse2_i for queries 32 qb + 8 (r/4) + 4 h + r%4
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
-        corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
+            corr[qb][4 * r4 + 0] = kbias - l4.x;
+            corr[qb][4 * r4 + 1] = kbias - l4.y;
+            corr[qb][4 * r4 + 2] = kbias - l4.z;
+            corr[qb][4 * r4 + 3] = kbias - l4.w;
+        }
     if (!INT8DP) __builtin_amdgcn_sched_barrier(0);   // score MFMAs issue before everything below
     // dP - Delta = dO V^T + (-Delta) on the FP16 MFMA with -Delta as the
     // accumulator input (all-INT8: s_dO s_V (dO codes V codes^T) + (-Delta))
@@ -284,7 +288,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         if (SMOOTHQ) kbias = a.bias[rowbase + key];
         sK = a.sk[bt + kvb];
     }
-    const float brow = h == 0 ? 1.0f : kbias;   // B operand of the rank-2 score correction
 
     const int i0 = CAUSAL ? min(2 * g, T - 1) : 0;
     // query block i -> LDS buffer b by DMA; LDS slot s of the FP16 dO tile
@@ -334,10 +337,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
         v16f dpe[2];
         if (active) {
             if (masked)
-                dkdv_probs<CAUSAL, true, INT8DP>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
+                dkdv_probs<CAUSAL, true, INT8DP>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
                                                  DUMP ? dp : nullptr);
             else
-                dkdv_probs<CAUSAL, false, INT8DP>(sm, buf, kop, sc, brow, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
+                dkdv_probs<CAUSAL, false, INT8DP>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
                                                   DUMP ? dp : nullptr);
             if (DUMP && dp) {
 #pragma unroll
@@ -356,9 +359,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             const float pm = wave_max64(__uint_as_float(umax(pm0, pm1)));
             if (lane == 0) sm.red[0][wave] = pm;
         }
-        // the next query block goes to the other buffer by DMA
+        // the next query block goes to the other buffer by DMA; it is waited
+        // for at the end of this step, so it lands during the dV and dK phases
         if (more) fetch(i + 1, buf ^ 1);
-        wait_vmem();
         lds_barrier();
         float dsm = 0.0f;
         if (active) {
@@ -462,6 +465,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
         }
+        // this wave's DMA of the next query block has landed; after the
+        // barrier every wave's has, and every wave is done with this buffer
+        wait_vmem();
         lds_barrier();
     };
     int i = i0;
@@ -525,8 +531,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
 // leave the accumulator as the B operand of dQ^T = K^T dS^T (contraction
 // over keys) with no transposition, and nothing of size N^2 is kept between
 // the two backward kernels.  Every product is formed from the key-block
-// kernel's operands in the same k order (the rank-2 score correction sums
-// -lse2_i and bias_j in the same order, the FP16 dO V^T MFMAs take the same
+// kernel's operands in the same k order (the score correction is the same
+// rounded sum of bias_j and -lse2_i, the FP16 dO V^T MFMAs take the same
 // channel chunks in the same sequence from the same -Delta input, and the
 // FMAs are written out), so its P, dS, tile maxima, scales and codes are
 // bitwise the key-block kernel's; the tile replay test checks this.
@@ -604,7 +610,8 @@ struct DqQuery {
     v4i qop[2];       // Q row-operand codes (B operand of K Q^T)
     v8h dob[4];       // dO in FP16, channels 16 ks + 8 h .. + 7 (B operand of V dO^T)
     v4i dor[2];       // all-INT8 dO V^T: dO row-operand codes (B operand of V dO^T)
-    float brow;       // B operand of the rank-2 score correction: -lse2 (h = 0) or 1 (h = 1)
+    float nlse;       // -lse2 of this lane's query (log2 domain)
+    float brow;       // MXFP8: B operand of the rank-2 score correction, -lse2 (h = 0) or 1 (h = 1)
     float bnd;        // B operand of the rank-1 product that puts -Delta in every row: -Delta (h = 0) or 0
     float sdo;        // dO block scale (all-INT8 dO V^T)
     uint32_t qw;      // Q block scale (MXFP8: the exponent bytes of this half, channel halves 0, 1)
@@ -632,11 +639,26 @@ __device__ __forceinline__ void dq_scores(const DqSmem& sm, int buf, const DqQue
             s = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qd.qop[0], v16i{});
             s = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qd.qop[1], s);
         }
-        // bias_j - lse2_i as [1 | bias] [-lse2 | 1]^T on the FP32 MFMA
-        // (32x32x2: lane l carries A[l%32][l/32] and B[l/32][l%32]), and
-        // -Delta_i in every row as [1 | 0] [-Delta | 0]^T
-        const v16f corr = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow,
-                                                               v16f{}, 0, 0, 0);
+        // bias_j - lse2_i: INT8, one addition per score (the same float sum as
+        // the key-block kernel's subtraction); MXFP8, [1 | bias] [-lse2 | 1]^T
+        // on the FP32 MFMA as in its key-block kernel (32x32x2: lane l carries
+        // A[l%32][l/32] and B[l/32][l%32]; the registers an addition per score
+        // needs would spill in this form).  -Delta_i in every row as
+        // [1 | 0] [-Delta | 0]^T on the same MFMA.
+        v16f corr;
+        if (MX) {
+            corr = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow, v16f{},
+                                                        0, 0, 0);
+        } else {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 b4 = *(const float4*)&sm.bias[buf][32 * kb + 8 * r4 + 4 * h];
+                corr[4 * r4 + 0] = b4.x + qd.nlse;
+                corr[4 * r4 + 1] = b4.y + qd.nlse;
+                corr[4 * r4 + 2] = b4.z + qd.nlse;
+                corr[4 * r4 + 3] = b4.w + qd.nlse;
+            }
+        }
         const v16f nd = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : 0.0f, qd.bnd, v16f{}, 0, 0, 0);
         // dP^T - Delta: the key-block kernel's products with the operands
         // swapped, the same channels in the same k steps from the same -Delta
@@ -715,6 +737,7 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
         const uint32_t w = ((const uint32_t*)a.sq)[bt + qblk];
         qd.qw = MX ? (uint32_t)ebyte(w, 2 * qhalf + 0) | ((uint32_t)ebyte(w, 2 * qhalf + 1) << 8) : w;
     }
+    qd.nlse = -lse2;
     qd.brow = h == 0 ? -lse2 : 1.0f;
     qd.bnd = h == 0 ? ndl : 0.0f;
 
