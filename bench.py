@@ -41,6 +41,9 @@ KERNEL_SOURCES = {
 # dK/dV kernel QK^T, P^T dO, dO V^T, dS^T Q; dQ kernel dS K (it also
 # recomputes QK^T and dO V^T, which the metric does not count again)
 KERNEL_UNITS = {"FWD_ATTN": 2, "BWD_DKDV": 4, "BWD_DQ": 1}
+# vector-ALU issue ceiling: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD
+# every 4 cycles at the 2.4 GHz rating
+VALU_PEAK_INSTR_PER_S = 1024 * 2.4e9 / 4
 
 
 def source_sha(stage: str) -> str:
@@ -214,6 +217,19 @@ def main():
         roof["frac_profile"] = round(ach_p / peak, 4)
         roof["sclk_mhz_measured"] = round(prof["sclk_mhz"], 0)
         roof["frac_at_measured_sclk"] = round(ach / (peak * prof["sclk_mhz"] / 2400.0), 4)
+        if prof.get("valu_instr_per_launch"):
+            # the bound these kernels actually meet: vector-ALU issue.  A wave64
+            # VALU instruction occupies a 16-lane SIMD for 4 cycles, so the chip
+            # issues at most 1024 SIMDs x 2.4 GHz / 4 of them per second; the
+            # kernel's count per launch is the committed SQ_INSTS_VALU (MFMA
+            # instructions included), its time this run's launch average
+            n_valu = prof["valu_instr_per_launch"]
+            valu_ach = n_valu / (stage_ms[dom] * 1e-3)
+            roof["valu"] = {"instr_per_launch": n_valu, "achieved": round(valu_ach / 1e9, 1),
+                            "peak": round(VALU_PEAK_INSTR_PER_S / 1e9, 1), "unit": "G wave64 instr/s",
+                            "frac": round(valu_ach / VALU_PEAK_INSTR_PER_S, 4),
+                            "frac_at_measured_sclk": round(valu_ach / (VALU_PEAK_INSTR_PER_S * prof["sclk_mhz"] / 2400.0), 4),
+                            "busy_profile": prof.get("valu_busy_profile")}
     out = {
         "metric": METRIC_FP4 if args.fp4 else METRIC,
         "value": round(tops, 2),
