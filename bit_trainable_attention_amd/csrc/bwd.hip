@@ -611,7 +611,7 @@ struct DqQuery {
     v8h dob[4];       // dO in FP16, channels 16 ks + 8 h .. + 7 (B operand of V dO^T)
     v4i dor[2];       // all-INT8 dO V^T: dO row-operand codes (B operand of V dO^T)
     float nlse;       // -lse2 of this lane's query (log2 domain)
-    float brow;       // MXFP8: B operand of the rank-2 score correction, -lse2 (h = 0) or 1 (h = 1)
+    float brow;       // non-causal MXFP8: B operand of the rank-2 score correction, -lse2 (h = 0) or 1 (h = 1)
     float bnd;        // B operand of the rank-1 product that puts -Delta in every row: -Delta (h = 0) or 0
     float sdo;        // dO block scale (all-INT8 dO V^T)
     uint32_t qw;      // Q block scale (MXFP8: the exponent bytes of this half, channel halves 0, 1)
@@ -639,14 +639,14 @@ __device__ __forceinline__ void dq_scores(const DqSmem& sm, int buf, const DqQue
             s = mfma_i8(sm.k[buf][(kb * 2 + 0) * 64 + lane], qd.qop[0], v16i{});
             s = mfma_i8(sm.k[buf][(kb * 2 + 1) * 64 + lane], qd.qop[1], s);
         }
-        // bias_j - lse2_i: INT8, one addition per score (the same float sum as
-        // the key-block kernel's subtraction); MXFP8, [1 | bias] [-lse2 | 1]^T
-        // on the FP32 MFMA as in its key-block kernel (32x32x2: lane l carries
-        // A[l%32][l/32] and B[l/32][l%32]; the registers an addition per score
-        // needs would spill in this form).  -Delta_i in every row as
-        // [1 | 0] [-Delta | 0]^T on the same MFMA.
+        // bias_j - lse2_i: one addition per score (the same rounded sum as the
+        // key-block kernels form); in the non-causal MXFP8 form, whose
+        // registers that would spill, [1 | bias] [-lse2 | 1]^T on the FP32
+        // MFMA instead (32x32x2: lane l carries A[l%32][l/32] and
+        // B[l/32][l%32]).  -Delta_i in every row as [1 | 0] [-Delta | 0]^T on
+        // the same MFMA.
         v16f corr;
-        if (MX) {
+        if (MX && !CAUSAL) {
             corr = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? 1.0f : sm.bias[buf][32 * kb + l32], qd.brow, v16f{},
                                                         0, 0, 0);
         } else {
