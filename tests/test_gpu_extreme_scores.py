@@ -3,7 +3,8 @@
 hundreds of natural-log units, softmax rows are nearly one-hot, most P values
 underflow to zero and LSE reaches ~850.  Every output is compared
 element-wise with the oracle of the same mode (the quantization-faithful
-INT8 oracle, and the MXFP8 oracle): the forward (O, LSE), the backward alone
+INT8 oracle, the MXFP8 oracle, and for the FP4 inference forward the FP4
+oracle): the forward (O, LSE), the backward alone
 (both sides given the oracle's O and LSE), and for INT8 end to end (each side
 feeds its own forward into its own backward).  Exact attention is not a bar
 here: a 64x64 block holding rows of RMS 20 and 0.05 quantizes the small rows
@@ -24,7 +25,7 @@ import torch
 
 import bit_trainable_attention_amd as sb
 import workloads as W
-from oracle import faithful as F, mxfp8 as X
+from oracle import faithful as F, fp4 as Y, mxfp8 as X
 from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
@@ -89,3 +90,22 @@ def test_extreme_score_range_parity(w, mode):
                          w.smooth_k)
         for name, t, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             G.parity(name, G.host_f32(t), b, mode, " (end to end)")
+
+
+@pytest.mark.parametrize("w", CASES, ids=_ids(CASES))
+def test_extreme_score_range_fp4_forward(w):
+    """The FP4 inference forward on the same inputs, against the oracle's FP4
+    mode (a P~ value next to an E2M1 midpoint may round to its neighbour on
+    one side: |dLSE| <= ln(3/2), widened by the float32 term as above)."""
+    print(f"[extreme fp4] {w.name} c{w.causal} q{w.smooth_q} k{w.smooth_k}", flush=True)
+    x = W.make_inputs(w)
+    f32 = {n: W.bf16_bits_to_f32(a) for n, a in x.items()}
+    o, lse = sb.fwd(G.dev(x["q"]), G.dev(x["k"]), G.dev(x["v"]), w.causal, w.smooth_q, w.smooth_k, fp4=True)
+    torch.cuda.synchronize()
+    o_g, lse_g = G.host_f32(o), lse.cpu().numpy()
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    o_f, lse_f = Y.fwd(f32["q"], f32["k"], f32["v"], w.causal, w.smooth_q, w.smooth_k)
+    G.parity("O", o_g, o_f, "fp4")
+    err = np.abs(lse_g - lse_f)
+    print(f"  LSE max err {np.max(err):.2e} (largest |LSE| {np.max(np.abs(lse_f)):.1f})", flush=True)
+    assert np.all(err <= 0.406 + 1e-5 * np.abs(lse_f))
