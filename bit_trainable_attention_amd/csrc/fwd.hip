@@ -321,8 +321,7 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            // log2-domain scores; the product also keeps the MFMA result away
-            // from the inline-assembly maximum below
+            // log2-domain scores
             z[kb][r] = SMOOTHQ ? __builtin_fmaf(s[kb][r], SCORE_SCALE_LOG2, bias[r]) : s[kb][r] * SCORE_SCALE_LOG2;
             if (MASK) {
                 const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
@@ -512,8 +511,7 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            // log2-domain scores (an ordinary VALU operation on the MFMA
-            // result before the inline-assembly maximum)
+            // log2-domain scores
             z[kb][r] = SMOOTHQ ? __builtin_fmaf(s[kb][r], SCORE_SCALE_LOG2, bias[r]) : s[kb][r] * SCORE_SCALE_LOG2;
             if (MASK) {
                 const int key = t * BLK + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4);
