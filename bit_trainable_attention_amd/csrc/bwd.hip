@@ -21,10 +21,11 @@
 //               dQ^T = K^T dS^T (contraction over keys); its dS values and
 //               codes are bitwise the key-block kernel's.
 // A 64x64 quantization tile of P or dS is held by a pair of waves, which
-// exchange their partial maxima through LDS.  The streamed operand tiles go
-// global -> LDS by DMA (two buffers in the key-block kernel, three in the dQ
-// kernel); FP16 rows are stored with their 16-byte chunks XOR-swizzled by row
-// so column reads do not collide on LDS banks.
+// exchange their partial maxima through LDS, so each kernel synchronizes its
+// workgroup once per step.  The streamed operand tiles go global -> LDS by DMA
+// into three buffers, each fetched a whole step before it is read; FP16 rows
+// are stored with their 16-byte chunks XOR-swizzled by row so column reads do
+// not collide on LDS banks.
 #include "attn.h"
 
 namespace sagebwd {
@@ -140,14 +141,16 @@ __device__ __forceinline__ void map_group_bwd(int ngroups, int BH, bool first_sm
 
 // ------------------------------------------------------------------ dK, dV
 
+constexpr int DKDV_BUFS = 3;
+
 struct DkdvSmem {
-    v4i q_r[2][256];     // Q row-operand codes (A operand of Q K^T)
-    v4i q_t[2][256];     // Q transposed codes (B operand of dS^T Q)
-    v4i do_t[2][256];    // dO transposed codes (B operand of P^T dO)
-    v8h do16[2][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
-    float lse2[2][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta of the query block
-    float qs[2][4];      // [0]: Q block scale, [1]: dO block scale
-    float red[2][4];     // partial tile maxima of P [0] and dS [1], per wave
+    v4i q_r[DKDV_BUFS][256];     // Q row-operand codes (A operand of Q K^T)
+    v4i q_t[DKDV_BUFS][256];     // Q transposed codes (B operand of dS^T Q)
+    v4i do_t[DKDV_BUFS][256];    // dO transposed codes (B operand of P^T dO)
+    v8h do16[DKDV_BUFS][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
+    float lse2[DKDV_BUFS][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta of the query block
+    float qs[DKDV_BUFS][4];      // [0]: Q block scale, [1]: dO block scale
+    float red[2][8];             // by step parity: partial tile maxima of P [0, 4) and |dS| [4, 8), per wave
 };
 
 // P for one 64-query x 32-key half tile in the S layout (lane = key,
@@ -319,23 +322,31 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     float gsum = 0.0f;                                          // sum_i s_dS colsum(dS codes), this half
 
     fetch(i0, 0);
+    if (i0 + 1 < T) fetch(i0 + 1, 1);
     wait_vmem();
     lds_barrier();
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
-    // the loop runs two query blocks per iteration so that each one's LDS
-    // buffer is a compile-time constant (every LDS address is then a base
-    // register plus an immediate offset)
+    // One barrier per step.  Before it: the scores, P, dP - Delta and dS of
+    // the step and both partial tile maxima (P and |dS|), written to LDS by
+    // step parity.  After it: both block scales, the P and dS codes, and the
+    // dV and dK products.  Query block i sits in LDS buffer (i - i0) % 3; the
+    // DMA of block i + 2 is issued right after step i's barrier (its buffer
+    // was last read in step i - 1, which every wave has finished by then) and
+    // waited for before step i + 1's barrier, a whole step later.  The loop
+    // runs three steps per iteration so that each LDS buffer is a
+    // compile-time constant (every LDS address a base register plus an
+    // immediate).
     auto step = [&](int i, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const bool more = i + 1 < T;
+        const int par = i & 1;
         const bool active = live && (!CAUSAL || i >= kvb);
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
-        float p[2][16];                      // [qb]: lane = key, regs = queries
+        float p[2][16], ds[2][16];           // [qb]: lane = key, regs = queries
         const float sQ = sm.qs[buf][0];
         const float sc = tile_scale(sQ, sK);
         uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
-        v16f dpe[2];
         if (active) {
+            v16f dpe[2];
             if (masked)
                 dkdv_probs<CAUSAL, true, INT8DP>(sm, buf, kop, sc, kbias, i, key, a.N, lane, h, p, dpe, vh, vop, sV,
                                                  DUMP ? dp : nullptr);
@@ -357,92 +368,77 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 pm1 = umax(pm1, umax(__float_as_uint(p[1][r]), __float_as_uint(p[1][r + 1])));
             }
             const float pm = wave_max64(__uint_as_float(umax(pm0, pm1)));
-            if (lane == 0) sm.red[0][wave] = pm;
-        }
-        // the next query block goes to the other buffer by DMA; it is waited
-        // for at the end of this step, so it lands during the dV and dK phases
-        if (more) fetch(i + 1, buf ^ 1);
-        lds_barrier();
-        float dsm = 0.0f;
-        if (active) {
-            float sP, invP;
-            // both partial maxima are >= 0: the larger is the larger bit pattern
-            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[0][wave]), __float_as_uint(sm.red[0][wave ^ 1]))),
-                        sP, invP);
-            // dV += s_P s_dO (P codes^T dO codes)
-            v4i pc[2];
+            if (lane == 0) sm.red[par][wave] = pm;
+            // dS = P * (dP - Delta)
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ds[qb][r] = p[qb][r] * dpe[qb][r];
+            float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
+                m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
+            }
+            const float dsm = wave_max64(max3f(m0, m1, m1));
+            if (lane == 0) sm.red[par][4 + wave] = dsm;
+            if (DUMP && dp) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<float>(dp, dumpoff::F2)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = ds[qb][r];
+            }
+        }
+        // this wave's DMA of block i + 1 has landed; after the barrier every
+        // wave's has, every partial maximum of this step is visible, and every
+        // wave is done with step i - 1's buffer
+        wait_vmem();
+        lds_barrier();
+        if (i + 2 < T) fetch(i + 2, (buf + 2) % DKDV_BUFS);
+        if (active) {
+            // the B operands of this step's dV and dK products, read from LDS
+            // before the code arithmetic so that it covers their latency
+            v4i dob[4], qtb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dob[j] = sm.do_t[buf][j * 64 + lane];
+                qtb[j] = sm.q_t[buf][j * 64 + lane];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // both partial maxima are >= 0: the larger is the larger bit pattern
+            float sP, invP, sdS, invdS;
+            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[par][wave]), __float_as_uint(sm.red[par][wave ^ 1]))),
+                        sP, invP);
+            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[par][4 + wave]),
+                                             __float_as_uint(sm.red[par][4 + (wave ^ 1)]))),
+                        sdS, invdS);
+            v4i pc[2], dc[2];
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
                 pc[qs] = v4i{pack_codes(p[qs][0], p[qs][1], p[qs][2], p[qs][3], invP),
                              pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invP),
                              pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invP),
                              pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invP)};
-            if (DUMP && dp) {
-                if (lane == 0 && kh == 0) dump_at<float>(dp, dumpoff::SC)[0] = sP;
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dp[dumpoff::C1 + (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] =
-                            (uint8_t)code_bits(p[qb][r], invP);
+                dc[qs] = v4i{pack_codes(ds[qs][0], ds[qs][1], ds[qs][2], ds[qs][3], invdS),
+                             pack_codes(ds[qs][4], ds[qs][5], ds[qs][6], ds[qs][7], invdS),
+                             pack_codes(ds[qs][8], ds[qs][9], ds[qs][10], ds[qs][11], invdS),
+                             pack_codes(ds[qs][12], ds[qs][13], ds[qs][14], ds[qs][15], invdS)};
             }
-            const float wv = sP * sm.qs[buf][1];
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(pc[0], sm.do_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
-                acc = mfma_i8(pc[1], sm.do_t[buf][(db * 2 + 1) * 64 + lane], acc);
-                if (DUMP && dp) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<int>(dp, dumpoff::ACC1)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
+            if (DUMP && dp) {
+                if (lane == 0 && kh == 0) {
+                    dump_at<float>(dp, dumpoff::SC)[0] = sP;
+                    dump_at<float>(dp, dumpoff::SC)[1] = sdS;
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
-            }
-            // dS = P * (dP - Delta) in place of P
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpe[qb][r];
-            {
-                float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    m0 = max_abs2f(m0, p[0][r], p[0][r + 1]);
-                    m1 = max_abs2f(m1, p[1][r], p[1][r + 1]);
-                }
-                dsm = wave_max64(max3f(m0, m1, m1));
-            }
-            if (lane == 0) sm.red[1][wave] = dsm;
-            if (DUMP && dp) {
-#pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<float>(dp, dumpoff::F2)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64);
+                        dp[dumpoff::C1 + o] = (uint8_t)code_bits(p[qb][r], invP);
+                        dp[dumpoff::C2 + o] = (uint8_t)code_bits(ds[qb][r], invdS);
+                    }
             }
-        }
-        lds_barrier();
-        if (active) {
-            float sdS, invdS;
-            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[1][wave]), __float_as_uint(sm.red[1][wave ^ 1]))),
-                        sdS, invdS);
-            if (DUMP && dp) {
-                if (lane == 0 && kh == 0) dump_at<float>(dp, dumpoff::SC)[1] = sdS;
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dp[dumpoff::C2 + (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] =
-                            (uint8_t)code_bits(p[qb][r], invdS);
-            }
-            v4i dc[2];
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
-                dc[qs] = v4i{pack_codes(p[qs][0], p[qs][1], p[qs][2], p[qs][3], invdS),
-                             pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invdS),
-                             pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invdS),
-                             pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invdS)};
             if (SMOOTHQ) {
                 int cs = 0;
 #pragma unroll
@@ -451,11 +447,25 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     for (int d4 = 0; d4 < 4; ++d4) cs = __builtin_amdgcn_sdot4(dc[qs][d4], 0x01010101, cs, false);
                 gsum = __builtin_fmaf((float)cs, sdS, gsum);
             }
+            // dV += s_P s_dO (P codes^T dO codes), dK += s_dS s_Q (dS codes^T Q codes)
+            const float wv = sP * sm.qs[buf][1];
             const float wk = sdS * sQ;
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(dc[0], sm.q_t[buf][(db * 2 + 0) * 64 + lane], v16i{});
-                acc = mfma_i8(dc[1], sm.q_t[buf][(db * 2 + 1) * 64 + lane], acc);
+                v16i acc = mfma_i8(pc[0], dob[db * 2 + 0], v16i{});
+                acc = mfma_i8(pc[1], dob[db * 2 + 1], acc);
+                if (DUMP && dp) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dump_at<int>(dp, dumpoff::ACC1)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
+            }
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                v16i acc = mfma_i8(dc[0], qtb[db * 2 + 0], v16i{});
+                acc = mfma_i8(dc[1], qtb[db * 2 + 1], acc);
                 if (DUMP && dp) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
@@ -465,17 +475,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
             }
         }
-        // this wave's DMA of the next query block has landed; after the
-        // barrier every wave's has, and every wave is done with this buffer
-        wait_vmem();
-        lds_barrier();
     };
     int i = i0;
-    for (; i + 1 < T; i += 2) {
+    for (; i + 2 < T; i += 3) {
         step(i, IntC<0>{});
         step(i + 1, IntC<1>{});
+        step(i + 2, IntC<2>{});
     }
     if (i < T) step(i, IntC<0>{});
+    if (i + 1 < T) step(i + 1, IntC<1>{});
 
     // epilogue: dK (x 1/8, plus colsum(dS) mu_q for Q-smoothing) and dV in bf16;
     // lane = channel, registers = keys of this wave's half block
