@@ -413,7 +413,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         kblock >= T || (p->causal && kblock > qblock))
         return SAGEBWD_ERR_INVALID_ARG;
     if (!dump || dump_bytes < (size_t)dumpoff::BYTES) return SAGEBWD_ERR_INVALID_ARG;
-    if (p->mxfp8 || p->fp4) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 kernels only
+    if (p->fp4) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 and MXFP8 kernels
     if (kernel == 0) {
         if ((rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream))) return rc;
         const Layout L = make_layout(*p, PASS_FWD);
@@ -422,7 +422,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         a.dump_bh = bh;
         a.dump_i = qblock;
         a.dump_t = kblock;
-        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, FMT_INT8, (hipStream_t)stream, true);
+        launch_fwd(a, p->B * p->H, p->causal, p->smooth_q, operand_format(*p), (hipStream_t)stream, true);
         return hip_status();
     }
     if ((rc = sagebwd_bwd_stage(p, SAGEBWD_STAGE_BWD_PREPARE, Q, K, V, O, LSE, dO, dQ, dK, dV, nullptr, 0, ws,

@@ -686,7 +686,7 @@ __device__ __forceinline__ void dq_scores(const DqSmem& sm, int buf, const DqQue
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            if (!MX && dump) sdump[kb][r] = s[r];
+            if (dump) sdump[kb][r] = MX ? __float_as_int(sx[r]) : s[r];
             const float sv = MX ? sx[r] : (float)s[r];
             float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, sc, corr[r]));
             if (MASK) {
@@ -826,6 +826,14 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
                 for (int r = 0; r < 16; r += 2) m = max_abs2f(m, ds[kb][r], ds[kb][r + 1]);
                 eS[kb] = mx_exponent(wave_max64(m));
                 dc[kb] = fp8_block_codes(ds[kb], pow2f(eS[kb]));
+                if (DUMP && dp) {
+                    // codes u8[q][k] at C1, exponents at [2 key half + query half] after the four P ones
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[dumpoff::C1 + qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] =
+                            (uint8_t)((uint32_t)dc[kb][r / 4] >> (8 * (r % 4)));
+                    if (lane == 0) dump_at<int>(dp, dumpoff::SC + 16)[2 * kb + qhalf] = eS[kb];
+                }
             }
             // dQ^T += K^T dS^T: B = the codes (k block h = key half h, scale
             // of this lane's query for key half h)
@@ -920,7 +928,7 @@ struct DkdvMxSmem {
 template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i kop, uint32_t q_w, int sk_e,
                                               float brow, int i, int key, int N, int lane, int h,
-                                              float (&p)[2][16]) {
+                                              float (&p)[2][16], uint8_t* dp = nullptr) {
     // all operands first (the LSE row is read by every lane, so no divergent
     // branch splits the reads from the MFMAs), then both query halves' MFMAs
     v8i qa[2];
@@ -934,6 +942,13 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
     v16f sx[2], corr[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) sx[qb] = mfma_fp8(qa[qb], kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
+    if (dp) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<float>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = sx[qb][r];
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
         corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
@@ -952,7 +967,20 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
     }
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+// MX tile dump: the code bytes of register r of query half qb (dword r / 4,
+// byte r % 4) and the exponents of the 32 x 32 blocks at [2 key half + query half].
+__device__ __forceinline__ void dump_mx_block(uint8_t* dp, int off_f, int off_c, int off_e, const float (&x)[16],
+                                              v4i codes, int e, int qb, int kh, int h, int lane, int key) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int o = (32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64);
+        dump_at<float>(dp, off_f)[o] = x[r];
+        dp[off_c + o] = (uint8_t)((uint32_t)codes[r / 4] >> (8 * (r % 4)));
+    }
+    if (lane == 0) dump_at<int>(dp, off_e)[2 * kh + qb] = e;
+}
+
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
     __shared__ DkdvMxSmem sm;
     const int tid = threadIdx.x, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -1021,8 +1049,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
         const uint32_t q_w = sm.qs[buf][0], do_w = sm.qs[buf][1];
         float p[2][16];   // [qb]: lane = key, registers = queries
-        if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p);
-        else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p);
+        uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
+        if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+        else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
         // P codes per 32x32 block (query half qb x this wave's keys)
         int eP[2];
         v4i pc[2];
@@ -1033,6 +1062,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
             for (int r = 0; r < 16; r += 2) pm = umax(pm, umax(__float_as_uint(p[qb][r]), __float_as_uint(p[qb][r + 1])));
             eP[qb] = mx_exponent(wave_max64(__uint_as_float(pm)));
             pc[qb] = fp8_block_codes(p[qb], pow2f(eP[qb]));
+            if (DUMP && dp) dump_mx_block(dp, dumpoff::F1, dumpoff::C1, dumpoff::SC, p[qb], pc[qb], eP[qb], qb, kh, h, lane, key);
         }
         // dV += P^T dO: A = P codes (row = key, 32-query block h), B = dO^T
         {
@@ -1072,6 +1102,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
             for (int r = 0; r < 16; r += 2) m = max_abs2f(m, p[qb][r], p[qb][r + 1]);
             eS[qb] = mx_exponent(wave_max64(m));
             dc[qb] = fp8_block_codes(p[qb], pow2f(eS[qb]));
+            if (DUMP && dp)
+                dump_mx_block(dp, dumpoff::F2, dumpoff::C2, dumpoff::SC + 16, p[qb], dc[qb], eS[qb], qb, kh, h, lane, key);
         }
         // dK += dS^T Q (and the dS column sums for the Q-smoothing term)
         {
@@ -1148,12 +1180,15 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
                     bool dump) {
     if (mx) {
         dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
-        if (causal) {
-            if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv_mx<true, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_bwd_dkdv_mx<true, false>), grid, block, 0, st, a);
-        } else {
-            if (smooth_q) hipLaunchKernelGGL((k_bwd_dkdv_mx<false, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_bwd_dkdv_mx<false, false>), grid, block, 0, st, a);
+        switch ((causal ? 4 : 0) | (smooth_q ? 2 : 0) | (dump ? 1 : 0)) {
+            case 0: hipLaunchKernelGGL((k_bwd_dkdv_mx<false, false, false>), grid, block, 0, st, a); break;
+            case 1: hipLaunchKernelGGL((k_bwd_dkdv_mx<false, false, true>), grid, block, 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_bwd_dkdv_mx<false, true, false>), grid, block, 0, st, a); break;
+            case 3: hipLaunchKernelGGL((k_bwd_dkdv_mx<false, true, true>), grid, block, 0, st, a); break;
+            case 4: hipLaunchKernelGGL((k_bwd_dkdv_mx<true, false, false>), grid, block, 0, st, a); break;
+            case 5: hipLaunchKernelGGL((k_bwd_dkdv_mx<true, false, true>), grid, block, 0, st, a); break;
+            case 6: hipLaunchKernelGGL((k_bwd_dkdv_mx<true, true, false>), grid, block, 0, st, a); break;
+            default: hipLaunchKernelGGL((k_bwd_dkdv_mx<true, true, true>), grid, block, 0, st, a); break;
         }
         return 0;
     }
@@ -1165,8 +1200,12 @@ int launch_bwd_dkdv(const BwdArgs& a, int BH, bool causal, bool smooth_q, bool i
 int launch_bwd_dq(const BwdArgs& a, int BH, bool causal, bool int8_dp, bool mx, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * BWD_WAVES);
     if (mx) {
-        if (causal) hipLaunchKernelGGL((k_bwd_dq<true, true, false, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_bwd_dq<false, true, false, false>), grid, block, 0, st, a);
+        switch ((causal ? 2 : 0) | (dump ? 1 : 0)) {
+            case 0: hipLaunchKernelGGL((k_bwd_dq<false, true, false, false>), grid, block, 0, st, a); break;
+            case 1: hipLaunchKernelGGL((k_bwd_dq<false, true, false, true>), grid, block, 0, st, a); break;
+            case 2: hipLaunchKernelGGL((k_bwd_dq<true, true, false, false>), grid, block, 0, st, a); break;
+            default: hipLaunchKernelGGL((k_bwd_dq<true, true, false, true>), grid, block, 0, st, a); break;
+        }
         return 0;
     }
     switch ((causal ? 4 : 0) | (int8_dp ? 2 : 0) | (dump ? 1 : 0)) {

@@ -296,15 +296,23 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
 // P~^T, every row of which is the same sum) and are rescaled whenever M_t
 // rises.
 
-template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+template <bool CAUSAL, bool SMOOTHQ, bool MASK, bool DUMP>
 __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop, int sq_e, uint32_t sk_w,
                                             uint32_t sv_w, int t, int q, int N, int lane, int h, float& M,
-                                            v16f (&O)[2], v16f& Lacc, v8i ones, int e_one, int e_pt) {
+                                            v16f (&O)[2], v16f& Lacc, v8i ones, int e_one, int e_pt, uint8_t* dp,
+                                            int qloc) {
     v16f s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
         s[kb] = mfma_fp8(cat8(sm.k[buf][(kb * 2 + 0) * 64 + lane], sm.k[buf][(kb * 2 + 1) * 64 + lane]), qop,
                          v16f{}, ebyte(sk_w, 2 * kb + h), sq_e);
+    if (DUMP && dp) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<float>(dp, dumpoff::A)[qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[kb][r];
+    }
     float z[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -329,6 +337,13 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
             }
         }
     }
+    if (DUMP && dp) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<float>(dp, dumpoff::F2)[qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = z[kb][r];
+    }
     float mx = row_max32(z);
     {
         // after the swap the two registers hold, in every lane, this lane's
@@ -351,6 +366,7 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
         Lacc[0] *= alpha;   // only register 0 of the row-sum accumulator is read
     }
     const float off = -M;
+    if (DUMP && dp && h == 0) dump_at<float>(dp, dumpoff::SC)[qloc] = M;
     v8i pc;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -364,6 +380,14 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
                 if (MASK && !(zz > -__builtin_inff())) v[j] = 0.0f;
             }
             pc[4 * kb + d4] = (int)fp8_quad(v[0], v[1], v[2], v[3], 0x1p-8f);
+            if (DUMP && dp) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kk = 32 * kb + 8 * d4 + 4 * h + j;
+                    dump_at<float>(dp, dumpoff::F1)[qloc * 64 + kk] = v[j];
+                    dp[dumpoff::C1 + qloc * 64 + kk] = (uint8_t)((uint32_t)pc[4 * kb + d4] >> (8 * j));
+                }
+            }
         }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -372,7 +396,7 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
     Lacc = mfma_fp8(ones, pc, Lacc, e_one, e_pt);
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -405,6 +429,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
                          0x38383838};
     const int q = qblk * BLK + 32 * qhalf + l32;
+    uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
     v4i pk = kg[tid], pv = vg[tid];
     float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -428,12 +453,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
         }
         if (live && t <= t_last) {
             const uint32_t sk_w = skw[t], sv_w = svw[t];
+            uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
             if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
-                fwd_tile_mx<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O, Lacc,
-                                                   ones, e_one, e_pt);
+                fwd_tile_mx<CAUSAL, SMOOTHQ, true, DUMP>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O,
+                                                         Lacc, ones, e_one, e_pt, dp, 32 * qhalf + l32);
             else
-                fwd_tile_mx<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O, Lacc,
-                                                    ones, e_one, e_pt);
+                fwd_tile_mx<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O,
+                                                          Lacc, ones, e_one, e_pt, dp, 32 * qhalf + l32);
         }
         if (more) {
             sm.k[buf ^ 1][tid] = pk;
@@ -670,13 +696,19 @@ int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hi
         return 0;
     }
     if (fmt == FMT_MXFP8) {
+#define SAGEBWD_FWD_MX(C, S)                                                                     \
+    do {                                                                                         \
+        if (dump) hipLaunchKernelGGL((k_fwd_mx<C, S, true>), grid, block, 0, st, a);             \
+        else hipLaunchKernelGGL((k_fwd_mx<C, S, false>), grid, block, 0, st, a);                 \
+    } while (0)
         if (causal) {
-            if (smooth_q) hipLaunchKernelGGL((k_fwd_mx<true, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd_mx<true, false>), grid, block, 0, st, a);
+            if (smooth_q) SAGEBWD_FWD_MX(true, true);
+            else SAGEBWD_FWD_MX(true, false);
         } else {
-            if (smooth_q) hipLaunchKernelGGL((k_fwd_mx<false, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd_mx<false, false>), grid, block, 0, st, a);
+            if (smooth_q) SAGEBWD_FWD_MX(false, true);
+            else SAGEBWD_FWD_MX(false, false);
         }
+#undef SAGEBWD_FWD_MX
         return 0;
     }
 #define SAGEBWD_FWD(C, S)                                                                        \

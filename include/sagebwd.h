@@ -83,9 +83,9 @@ typedef struct sagebwd_params {
                            [-126, 127]; the forward's P~ = exp(S - running row
                            max) coded as E4M3(256 P~).  Smoothing, QK-norm,
                            the FP16 dO V^T and the outputs are as in the INT8
-                           mode.  Not with int8_dp (SAGEBWD_ERR_UNSUPPORTED)
-                           nor with sagebwd_debug_tile.  Forward and backward
-                           must be called with the same value. */
+                           mode.  Not with int8_dp (SAGEBWD_ERR_UNSUPPORTED).
+                           Forward and backward must be called with the same
+                           value. */
     int32_t fp4;        /* 0 or 1: forward only (inference).  The FP4 attention of
                            the SageAttention3 summary ("Approach": FP4
                            microscaling on both matmuls) in MI355X's MXFP4
@@ -269,8 +269,18 @@ const char* sagebwd_status_string(int status);
  *     u8[q][k] at 32768, dS K i32[q][c] at 36864, s_dS f32 at 90112
  * (q, k: query and key within the blocks; c: channel), so that the INT8
  * codes, block scales and integer tile products can be re-derived exactly
- * from the kernel's own pre-quantization values.  Tiles above the causal
- * diagonal are never computed and are rejected (SAGEBWD_ERR_INVALID_ARG). */
+ * from the kernel's own pre-quantization values.  With mxfp8 = 1 the MXFP8
+ * kernels dump their tile instead (no integer products exist there: the FP8
+ * MFMA accumulates in float32):
+ *   kernel 0: the FP8 product S f32[q][k] at 0, P~ f32[q][k] at 16384, P~
+ *     E4M3 codes u8[q][k] at 32768, the log2-domain scores z f32[q][k] at
+ *     53248, the running row maxima after this tile f32[q] at 90112
+ *   kernel 1: S at 0, P at 16384, P codes at 32768, dS f32[q][k] at 53248,
+ *     dS codes u8[q][k] at 69632, the E8M0 exponents (unbiased, int32) of P
+ *     at 90112 and of dS at 90128, each indexed 2 * (key half) + query half
+ *   kernel 2: S at 0, dS at 53248, dS codes at 32768, dS exponents at 90128
+ * Tiles above the causal diagonal are never computed and are rejected
+ * (SAGEBWD_ERR_INVALID_ARG); fp4 returns SAGEBWD_ERR_UNSUPPORTED. */
 #define SAGEBWD_DUMP_BYTES 90368
 int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, int kblock,
                        const void* Q, const void* K, const void* V, void* O, float* LSE, const void* dO,

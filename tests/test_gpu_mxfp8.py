@@ -219,9 +219,10 @@ def test_mx_rejections():
     z = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sb.SageBwdError):
         sb.bwd(z, z, z, z, torch.zeros(1, 1, 64, device="cuda"), z, mxfp8=True, int8_dp=True)
+    # the tile dump exists in MXFP8 mode (tests/test_gpu_replay_mx.py), but not with the INT8 ablation
     with pytest.raises(sb.SageBwdError, match="unsupported"):
-        sb.debug_tile("fwd", 0, 0, 0, z, z, z, torch.empty_like(z), torch.zeros(1, 1, 64, device="cuda"),
-                      mxfp8=True)
+        sb.debug_tile("dkdv", 0, 0, 0, z, z, z, z, torch.zeros(1, 1, 64, device="cuda"), z, mxfp8=True,
+                      int8_dp=True)
 
 
 FULL = [("llama16k", (0, 29)), ("video", (1, 3))]
