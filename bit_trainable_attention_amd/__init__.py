@@ -225,17 +225,19 @@ DEBUG_KERNELS = {"fwd": 0, "dkdv": 1, "dq": 2}
 
 
 def debug_tile(kernel, bh, qblock, kblock, q, k, v, o, lse, do=None, causal=False, smooth_q=False,
-               smooth_k=True, int8_dp=False, qk_norm=False, mxfp8=False, return_grads=False):
+               smooth_k=True, int8_dp=False, qk_norm=False, mxfp8=False, return_grads=False, fp4=False):
     """Run one attention kernel's debug instantiation and return the raw
     SAGEBWD_DUMP_BYTES dump of tile (bh, qblock, kblock) as a CPU uint8
     tensor (see include/sagebwd.h for the layout).  kernel: "fwd" writes into
     o and lse; "dkdv" and "dq" read o, lse and do.  With return_grads, also
-    the (dQ, dK, dV) buffers the backward kernels wrote (None for "fwd")."""
+    the (dQ, dK, dV) buffers the backward kernels wrote (None for "fwd").
+    fp4: the FP4 inference forward ("fwd" only)."""
     _check_qkv(q, k, v)
     B, H, N, D = q.shape
-    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8)
+    p = make_params(B, H, N, causal, smooth_q, smooth_k, D, int8_dp, qk_norm, mxfp8, fp4)
     lib = load_library()
-    ws = torch.empty(lib.sagebwd_bwd_workspace_size(ctypes.byref(p)), dtype=torch.uint8, device=q.device)
+    nbytes = (lib.sagebwd_fwd_workspace_size if fp4 else lib.sagebwd_bwd_workspace_size)(ctypes.byref(p))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     dump = torch.zeros(DUMP_BYTES, dtype=torch.uint8, device=q.device)
     kid = DEBUG_KERNELS[kernel]
     grads = [torch.empty_like(q) for _ in range(3)] if kid else [None, None, None]

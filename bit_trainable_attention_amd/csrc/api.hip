@@ -413,7 +413,7 @@ int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, 
         kblock >= T || (p->causal && kblock > qblock))
         return SAGEBWD_ERR_INVALID_ARG;
     if (!dump || dump_bytes < (size_t)dumpoff::BYTES) return SAGEBWD_ERR_INVALID_ARG;
-    if (p->fp4) return SAGEBWD_ERR_UNSUPPORTED;   // the tile dump exists for the INT8 and MXFP8 kernels
+    if (p->fp4 && kernel != 0) return SAGEBWD_ERR_UNSUPPORTED;   // FP4: forward only
     if (kernel == 0) {
         if ((rc = sagebwd_fwd_stage(p, SAGEBWD_STAGE_FWD_PREPARE, Q, K, V, O, LSE, ws, ws_bytes, stream))) return rc;
         const Layout L = make_layout(*p, PASS_FWD);

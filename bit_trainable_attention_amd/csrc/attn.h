@@ -55,7 +55,7 @@ struct BwdArgs {
     int dump_bh, dump_i, dump_t;       // which (head, query block, key block) to dump
 };
 
-// fmt: FMT_INT8, FMT_MXFP8 or FMT_FP4 (the tile dump exists for INT8 and MXFP8)
+// fmt: FMT_INT8, FMT_MXFP8 or FMT_FP4 (each with a tile-dump instantiation)
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hipStream_t st, bool dump = false);
 // int8_dp: the all-INT8 ablation, dO V^T from INT8 codes instead of FP16;
 // mx: MXFP8 codes and block exponents (neither int8_dp nor a tile dump)

@@ -511,16 +511,23 @@ struct FwdFp4Smem {
     float bias[2][64];
 };
 
-template <bool CAUSAL, bool SMOOTHQ, bool MASK>
+template <bool CAUSAL, bool SMOOTHQ, bool MASK, bool DUMP>
 __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i qop, int sq_e, int t, int q, int N,
                                              int lane, int h, int l32, float& M, v16f (&O)[2], v16f& Lacc,
-                                             int e_one) {
+                                             int e_one, uint8_t* dp, int qloc) {
     const uint8_t* kx = (const uint8_t*)sm.k[buf] + FP4_EXP_OFF;
     const uint8_t* vx = (const uint8_t*)sm.v[buf] + FP4_EXP_OFF;
     v16f s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
         s[kb] = mfma_fp4(sm.k[buf][kb * 64 + lane], qop, v16f{}, kx[2 * (32 * kb + l32) + h], sq_e);
+    if (DUMP && dp) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<float>(dp, dumpoff::A)[qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = s[kb][r];
+    }
     float z[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -544,6 +551,13 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
                 if (key >= N || (CAUSAL && key > q)) z[kb][r] = -__builtin_inff();
             }
         }
+    }
+    if (DUMP && dp) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dump_at<float>(dp, dumpoff::F2)[qloc * 64 + 32 * kb + 8 * (r / 4) + 4 * h + (r % 4)] = z[kb][r];
     }
     float mx = row_max32(z);
     {
@@ -581,6 +595,18 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
     const float psc = pow2f(pe);
     const v4i pc = v4i{(int)fp4_oct(p, psc), (int)fp4_oct(p + 8, psc), (int)fp4_oct(p + 16, psc),
                        (int)fp4_oct(p + 24, psc)};
+    if (DUMP && dp) {
+        // P~ and its code nibble per [query][key]; the block exponent per
+        // [query][key class]; the running maximum per query
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int kk = 32 * (i / 16) + 8 * ((i % 16) / 4) + 4 * h + (i % 4);
+            dump_at<float>(dp, dumpoff::F1)[qloc * 64 + kk] = p[i];
+            dp[dumpoff::C1 + qloc * 64 + kk] = (uint8_t)(((uint32_t)pc[i / 8] >> (4 * (i % 8))) & 0xFu);
+        }
+        dump_at<int>(dp, dumpoff::ACC1)[qloc * 2 + h] = pe;
+        if (h == 0) dump_at<float>(dp, dumpoff::SC)[qloc] = M;
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
         O[db] = mfma_fp4(sm.v[buf][db * 64 + lane], pc, O[db], vx[2 * (32 * db + l32) + h], pe + 127);
@@ -588,7 +614,7 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
     Lacc = mfma_fp4(ones, pc, Lacc, e_one, pe + 127);
 }
 
-template <bool CAUSAL, bool SMOOTHQ>
+template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
 __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     __shared__ FwdFp4Smem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -616,6 +642,7 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     const int e_one = opaque(E8M0_ONE);
     const int q = qblk * BLK + 32 * qhalf + l32;
     const bool loader = tid < 136;
+    uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
     v4i pk = loader ? kg[tid] : v4i{}, pv = loader ? vg[tid] : v4i{};
     float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -640,10 +667,13 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
         }
         if (more && SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
         if (live && t <= t_last) {
+            uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
             if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
-                fwd_tile_fp4<CAUSAL, SMOOTHQ, true>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
+                fwd_tile_fp4<CAUSAL, SMOOTHQ, true, DUMP>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc,
+                                                          e_one, dp, 32 * qhalf + l32);
             else
-                fwd_tile_fp4<CAUSAL, SMOOTHQ, false>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc, e_one);
+                fwd_tile_fp4<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc,
+                                                           e_one, dp, 32 * qhalf + l32);
         }
         if (more) {
             if (loader) {
@@ -686,13 +716,19 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
 int launch_fwd(const FwdArgs& a, int BH, bool causal, bool smooth_q, int fmt, hipStream_t st, bool dump) {
     dim3 grid(a.ngroups * BH), block(64 * FWD_WAVES);
     if (fmt == FMT_FP4) {
+#define SAGEBWD_FWD_FP4(C, S)                                                                    \
+    do {                                                                                         \
+        if (dump) hipLaunchKernelGGL((k_fwd_fp4<C, S, true>), grid, block, 0, st, a);            \
+        else hipLaunchKernelGGL((k_fwd_fp4<C, S, false>), grid, block, 0, st, a);                \
+    } while (0)
         if (causal) {
-            if (smooth_q) hipLaunchKernelGGL((k_fwd_fp4<true, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd_fp4<true, false>), grid, block, 0, st, a);
+            if (smooth_q) SAGEBWD_FWD_FP4(true, true);
+            else SAGEBWD_FWD_FP4(true, false);
         } else {
-            if (smooth_q) hipLaunchKernelGGL((k_fwd_fp4<false, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_fwd_fp4<false, false>), grid, block, 0, st, a);
+            if (smooth_q) SAGEBWD_FWD_FP4(false, true);
+            else SAGEBWD_FWD_FP4(false, false);
         }
+#undef SAGEBWD_FWD_FP4
         return 0;
     }
     if (fmt == FMT_MXFP8) {

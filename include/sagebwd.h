@@ -98,9 +98,9 @@ typedef struct sagebwd_params {
                            (key % 8) / 4 of a 64-key tile; P~ = exp(S - running
                            row max); the Q-smoothing bias from the float
                            centred K.  Not with mxfp8 or int8_dp; the
-                           backward entry points, sagebwd_debug_tile and
-                           sagebwd_prepare with dO return
-                           SAGEBWD_ERR_UNSUPPORTED. */
+                           backward entry points, the backward kernels of
+                           sagebwd_debug_tile and sagebwd_prepare with dO
+                           return SAGEBWD_ERR_UNSUPPORTED. */
 } sagebwd_params;
 
 #define SAGEBWD_OK               0
@@ -279,8 +279,11 @@ const char* sagebwd_status_string(int status);
  *     dS codes u8[q][k] at 69632, the E8M0 exponents (unbiased, int32) of P
  *     at 90112 and of dS at 90128, each indexed 2 * (key half) + query half
  *   kernel 2: S at 0, dS at 53248, dS codes at 32768, dS exponents at 90128
- * Tiles above the causal diagonal are never computed and are rejected
- * (SAGEBWD_ERR_INVALID_ARG); fp4 returns SAGEBWD_ERR_UNSUPPORTED. */
+ * and with fp4 = 1 (kernel 0 only; SAGEBWD_ERR_UNSUPPORTED otherwise) the FP4
+ * forward: S, P~, z and the running maxima as the MXFP8 forward, the E2M1
+ * code nibbles u8[q][k] at 32768 and the P~ block exponents int32[q][key
+ * class (k % 8) / 4] at 36864.  Tiles above the causal diagonal are never
+ * computed and are rejected (SAGEBWD_ERR_INVALID_ARG). */
 #define SAGEBWD_DUMP_BYTES 90368
 int sagebwd_debug_tile(const sagebwd_params* p, int kernel, int bh, int qblock, int kblock,
                        const void* Q, const void* K, const void* V, void* O, float* LSE, const void* dO,

@@ -80,9 +80,10 @@ def test_param_validation(lib):
                                      None) == UNSUPPORTED
     assert lib.sagebwd_prepare(ctypes.byref(P(fp4=1)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                None) == UNSUPPORTED
-    # the tile dump exists for the INT8 and MXFP8 kernels, not the FP4 forward
-    assert lib.sagebwd_debug_tile(ctypes.byref(P(fp4=1)), 0, 0, 0, 0, *([FAKE] * 10), FAKE, 1 << 20, FAKE, 1 << 40,
-                                  None) == UNSUPPORTED
+    # FP4 has no backward kernels to dump
+    for kernel in (1, 2):
+        assert lib.sagebwd_debug_tile(ctypes.byref(P(fp4=1)), kernel, 0, 0, 0, *([FAKE] * 10), FAKE, 1 << 20, FAKE,
+                                      1 << 40, None) == UNSUPPORTED
     assert call_fwd(lib, P(D=128)) == UNSUPPORTED
     assert call_fwd(lib, P(N=(1 << 18) + 1)) == UNSUPPORTED
     assert call_fwd(lib, P(B=256, H=256)) == UNSUPPORTED

@@ -1,6 +1,6 @@
-"""Replay checks of single tiles of the MXFP8 kernels: bit-exact E4M3 codes and
+"""Replay checks of single tiles of the MXFP8 kernels (bit-exact E4M3 codes and
 E8M0 block exponents, and the dQ kernel's recomputed tile against the dK/dV
-kernel's.
+kernel's) and of the FP4 inference forward (E2M1 codes and exponents).
 
 The MXFP8 forward and backward apply the block scales inside the FP8 matrix
 instruction and accumulate O, dK, dV and dQ in its float32 accumulators, so
@@ -29,12 +29,12 @@ import torch
 
 import bit_trainable_attention_amd as sb
 import workloads as W
-from oracle import mxfp8 as X
+from oracle import fp4 as Y, mxfp8 as X
 from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-A, F1, C1, F2, C2, SC = 0, 16384, 32768, 53248, 69632, 90112
+A, F1, C1, ACC1, F2, C2, SC = 0, 16384, 32768, 36864, 53248, 69632, 90112
 LOG2E = 1.4426950408889634
 
 CASES = [
@@ -171,3 +171,69 @@ def test_mx_tile_replay_bitexact(name, w, bh, tiles):
               f"{r_fwd:.1e} (fwd) {r_bwd:.1e} (bwd)", flush=True)
     assert fresh_diff <= 0.02 * fresh_total, (fresh_diff, fresh_total)
     assert fwd_diff <= 0.02 * max(fwd_total, 1), (fwd_diff, fwd_total)
+
+
+FP4_CASES = [
+    ("tiny", W.WORKLOADS["tiny"], 1, [(0, 0), (1, 1), (0, 1)]),
+    ("ragged_causal", W.custom(1, 2, 200, True, True, True, "kbias", 71), 1, [(3, 3), (3, 0), (2, 1)]),
+    ("llama16k", W.WORKLOADS["llama16k"], 5, [(255, 255), (100, 0)]),
+]
+
+
+@pytest.mark.parametrize("name,w,bh,tiles", FP4_CASES, ids=[c[0] for c in FP4_CASES])
+def test_fp4_tile_replay_bitexact(name, w, bh, tiles):
+    """The FP4 inference forward's tile: the P~ block exponents (one per query
+    and key class (key mod 8) div 4) and E2M1 code nibbles are the oracle's
+    Y2 of the dumped P~; P~ = exp2(z - M); the FP4 scores against the exact
+    products of the oracle's dequantized operands; production O and LSE
+    equal the debug instantiation's."""
+    print(f"[replay fp4] {name} B{w.B} H{w.H} N{w.N} causal={w.causal} head {bh} tiles {tiles}", flush=True)
+    b, h = divmod(bh, w.H)
+    x = W.make_inputs(w)
+    tq, tk, tv = (G.dev(x[n]) for n in ("q", "k", "v"))
+    f = {n: W.bf16_bits_to_f32(x[n][b, h]) for n in ("q", "k", "v")}
+    del x
+    N = w.N
+    pp = Y.prepare(f["q"], f["k"], f["v"], w.smooth_q, w.smooth_k)
+    po, plse = sb.fwd(tq, tk, tv, w.causal, w.smooth_q, w.smooth_k, fp4=True)
+    torch.cuda.synchronize()
+    cls = (np.arange(64) % 8) // 4                    # key class of each key of a tile
+    for (i, t) in tiles:
+        rows = np.arange(64 * i, 64 * i + 64)
+        cols = np.arange(64 * t, 64 * t + 64)
+        keep = (rows[:, None] < N) & (cols[None, :] < N)
+        if w.causal:
+            keep &= cols[None, :] <= rows[:, None]
+        fr = rows < N
+        live = keep.any(axis=1)
+        fo, fl = torch.empty_like(tq), torch.empty(w.B, w.H, N, device="cuda")
+        d = sb.debug_tile("fwd", bh, i, t, tq, tk, tv, fo, fl, None, w.causal, w.smooth_q, w.smooth_k,
+                          fp4=True).numpy().tobytes()
+        assert torch.equal(fo[b, h].view(torch.int16), po[b, h].view(torch.int16)), ("fp4 prod O", i, t)
+        assert torch.equal(fl[b, h], plse[b, h]), ("fp4 prod LSE", i, t)
+        r_s = _check_scores(_blk(d, A, np.float32), pp, rows, cols, keep, ("fp4 S", i, t))
+        z = _blk(d, F2, np.float32)
+        assert np.all(np.isneginf(z[fr][~keep[fr]])) and np.all(np.isfinite(z[keep])), ("fp4 z mask", i, t)
+        zref = (_blk(d, A, np.float32).astype(np.float64) + pp.b[cols][None, :]) * (LOG2E / 8.0)
+        assert np.all(np.abs(z[keep] - zref[keep]) <= 1e-6 * (1.0 + np.abs(zref[keep]))), ("fp4 z", i, t)
+        M = np.frombuffer(d, np.float32, 64, SC)
+        zmax = np.max(np.where(keep, z, -np.inf), axis=1)
+        assert np.all(M[live] >= zmax[live]), ("fp4 running max", i, t)
+        if t == 0:
+            assert np.array_equal(M[live], zmax[live]), ("fp4 first-tile max", i, t)
+        pt = _blk(d, F1, np.float32)
+        arg = (z.astype(np.float32) + (-M[:, None]).astype(np.float32)).astype(np.float32)
+        with np.errstate(invalid="ignore"):
+            pref = np.where(keep, np.exp2(arg.astype(np.float64)), 0.0)
+        assert np.all((np.abs(pt - pref) <= 2.0 ** -21 * pref + 2.0 ** -120)[fr]), ("fp4 P~", i, t)
+        assert np.all((pt >= 0) & (pt <= 1)), ("fp4 P~ range", i, t)
+        # Y2 per (query, key class): exponent, then E2M1 codes of P~ 2^-e
+        ex = np.frombuffer(d, np.int32, 128, ACC1).reshape(64, 2)
+        ptd = pt.astype(np.float64)
+        e_ref = np.stack([Y.fp4_exponent(np.max(ptd[:, cls == c], axis=1)) for c in (0, 1)], axis=1)
+        assert np.array_equal(ex, e_ref), ("fp4 exponents", i, t)
+        codes = _blk(d, C1, np.uint8)
+        scaled = ptd * np.ldexp(1.0, -ex[:, cls])
+        assert np.array_equal(codes, Y.e2m1_encode(scaled)), ("fp4 codes", i, t)
+        print(f"  tile ({i},{t}): exponents and E2M1 codes bit-exact, production outputs equal; "
+              f"score error / sum|terms| {r_s:.1e}", flush=True)
