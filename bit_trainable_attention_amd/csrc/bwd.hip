@@ -413,18 +413,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             block_scale(__uint_as_float(umax(__float_as_uint(sm.red[par][4 + wave]),
                                              __float_as_uint(sm.red[par][4 + (wave ^ 1)]))),
                         sdS, invdS);
+            // P codes, then the dV products; the dS codes are formed while
+            // they run, then the dK products, under which dV is updated
             v4i pc[2], dc[2];
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) {
+            for (int qs = 0; qs < 2; ++qs)
                 pc[qs] = v4i{pack_codes(p[qs][0], p[qs][1], p[qs][2], p[qs][3], invP),
                              pack_codes(p[qs][4], p[qs][5], p[qs][6], p[qs][7], invP),
                              pack_codes(p[qs][8], p[qs][9], p[qs][10], p[qs][11], invP),
                              pack_codes(p[qs][12], p[qs][13], p[qs][14], p[qs][15], invP)};
-                dc[qs] = v4i{pack_codes(ds[qs][0], ds[qs][1], ds[qs][2], ds[qs][3], invdS),
-                             pack_codes(ds[qs][4], ds[qs][5], ds[qs][6], ds[qs][7], invdS),
-                             pack_codes(ds[qs][8], ds[qs][9], ds[qs][10], ds[qs][11], invdS),
-                             pack_codes(ds[qs][12], ds[qs][13], ds[qs][14], ds[qs][15], invdS)};
-            }
             if (DUMP && dp) {
                 if (lane == 0 && kh == 0) {
                     dump_at<float>(dp, dumpoff::SC)[0] = sP;
@@ -439,6 +436,22 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                         dp[dumpoff::C2 + o] = (uint8_t)code_bits(ds[qb][r], invdS);
                     }
             }
+            // dV += s_P s_dO (P codes^T dO codes), dK += s_dS s_Q (dS codes^T Q codes)
+            const float wv = sP * sm.qs[buf][1];
+            const float wk = sdS * sQ;
+            v16i av[2], ak[2];
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+                av[db] = mfma_i8(pc[0], dob[db * 2 + 0], v16i{});
+                av[db] = mfma_i8(pc[1], dob[db * 2 + 1], av[db]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs)
+                dc[qs] = v4i{pack_codes(ds[qs][0], ds[qs][1], ds[qs][2], ds[qs][3], invdS),
+                             pack_codes(ds[qs][4], ds[qs][5], ds[qs][6], ds[qs][7], invdS),
+                             pack_codes(ds[qs][8], ds[qs][9], ds[qs][10], ds[qs][11], invdS),
+                             pack_codes(ds[qs][12], ds[qs][13], ds[qs][14], ds[qs][15], invdS)};
             if (SMOOTHQ) {
                 int cs = 0;
 #pragma unroll
@@ -447,33 +460,31 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     for (int d4 = 0; d4 < 4; ++d4) cs = __builtin_amdgcn_sdot4(dc[qs][d4], 0x01010101, cs, false);
                 gsum = __builtin_fmaf((float)cs, sdS, gsum);
             }
-            // dV += s_P s_dO (P codes^T dO codes), dK += s_dS s_Q (dS codes^T Q codes)
-            const float wv = sP * sm.qs[buf][1];
-            const float wk = sdS * sQ;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(pc[0], dob[db * 2 + 0], v16i{});
-                acc = mfma_i8(pc[1], dob[db * 2 + 1], acc);
-                if (DUMP && dp) {
+                ak[db] = mfma_i8(dc[0], qtb[db * 2 + 0], v16i{});
+                ak[db] = mfma_i8(dc[1], qtb[db * 2 + 1], ak[db]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (DUMP && dp) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<int>(dp, dumpoff::ACC1)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
-                }
+                for (int db = 0; db < 2; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)acc[r], wv, dv[db][r]);
+                    for (int r = 0; r < 16; ++r) {
+                        const int o = (32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32;
+                        dump_at<int>(dp, dumpoff::ACC1)[o] = av[db][r];
+                        dump_at<int>(dp, dumpoff::ACC2)[o] = ak[db][r];
+                    }
             }
 #pragma unroll
-            for (int db = 0; db < 2; ++db) {
-                v16i acc = mfma_i8(dc[0], qtb[db * 2 + 0], v16i{});
-                acc = mfma_i8(dc[1], qtb[db * 2 + 1], acc);
-                if (DUMP && dp) {
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dump_at<int>(dp, dumpoff::ACC2)[(32 * kh + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + 32 * db + l32] = acc[r];
-                }
+                for (int r = 0; r < 16; ++r) dv[db][r] = __builtin_fmaf((float)av[db][r], wv, dv[db][r]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)acc[r], wk, dk[db][r]);
-            }
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dk[db][r] = __builtin_fmaf((float)ak[db][r], wk, dk[db][r]);
         }
     };
     int i = i0;
