@@ -934,25 +934,52 @@ struct DkdvMxSmem {
 };
 
 // S = Q K^T (dequantized in the MFMA) and P = exp2(S log2(e)/8 + bias_j -
-// lse2_i) for one 64-query x 32-key tile (lane = key, registers = queries);
-// MASK only on the causal diagonal and the ragged last key block.
+// lse2_i) for one 64-query x 32-key tile (lane = key, registers = queries),
+// the correction bias_j - lse2_i one subtraction per score as in the INT8
+// kernel; dP - Delta (FP16 MFMA, -Delta as the accumulator input) is formed
+// here too, its MFMAs placed one by one between groups of the exps.  MASK
+// only on the causal diagonal and the ragged last key block.
 template <bool CAUSAL, bool MASK>
 __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i kop, uint32_t q_w, int sk_e,
-                                              float brow, int i, int key, int N, int lane, int h,
-                                              float (&p)[2][16], uint8_t* dp = nullptr) {
-    // all operands first (the LSE row is read by every lane, so no divergent
-    // branch splits the reads from the MFMAs), then both query halves' MFMAs
+                                              float kbias, int i, int key, int N, int lane, int h,
+                                              float (&p)[2][16], v16f (&dpe)[2], const v8h (&vh)[4],
+                                              uint8_t* dp = nullptr) {
     v8i qa[2];
-    float lv[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < 2; ++qb)
         qa[qb] = cat8(sm.q_r[buf][(qb * 2 + 0) * 64 + lane], sm.q_r[buf][(qb * 2 + 1) * 64 + lane]);
-        lv[qb] = sm.lse2[buf][32 * qb + lane % 32];
-        asm volatile("" : "+v"(lv[qb]));
-    }
     v16f sx[2], corr[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) sx[qb] = mfma_fp8(qa[qb], kop, v16f{}, ebyte(q_w, 2 * qb + h), sk_e);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 l4 = *(const float4*)&sm.lse2[buf][32 * qb + 8 * r4 + 4 * h];
+            corr[qb][4 * r4 + 0] = kbias - l4.x;
+            corr[qb][4 * r4 + 1] = kbias - l4.y;
+            corr[qb][4 * r4 + 2] = kbias - l4.z;
+            corr[qb][4 * r4 + 3] = kbias - l4.w;
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    const int l32 = lane % 32;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int row = 32 * qb + l32;
+        v16f nd;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
+            nd[4 * r4 + 0] = d4.x;
+            nd[4 * r4 + 1] = d4.y;
+            nd[4 * r4 + 2] = d4.z;
+            nd[4 * r4 + 3] = d4.w;
+        }
+        v16f d = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
+        d = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], d);
+        d = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], d);
+        dpe[qb] = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], d);
+    }
     if (dp) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -960,9 +987,6 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
             for (int r = 0; r < 16; ++r)
                 dump_at<float>(dp, dumpoff::A)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = sx[qb][r];
     }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-        corr[qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(h == 0 ? -lv[qb] : 1.0f, brow, v16f{}, 0, 0, 0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -975,6 +999,13 @@ __device__ __forceinline__ void dkdv_probs_mx(const DkdvMxSmem& sm, int buf, v8i
             }
             p[qb][r] = pv;
         }
+    }
+    // the score MFMAs first, then each dP MFMA between groups of exps
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
     }
 }
 
@@ -1020,7 +1051,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         if (SMOOTHQ) kbias = a.bias[rowbase + key];
         sk_e = ebyte(((const uint32_t*)a.sk)[bt + kvb], 2 * kh + h);   // column = key, 32-channel block h
     }
-    const float brow = h == 0 ? 1.0f : kbias;
     const int e_one = opaque(E8M0_ONE);
     const v8i ones = v8i{0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838,
                          0x38383838};
@@ -1061,8 +1091,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         const uint32_t q_w = sm.qs[buf][0], do_w = sm.qs[buf][1];
         float p[2][16];   // [qb]: lane = key, registers = queries
         uint8_t* dp = (DUMP && bh == a.dump_bh && kvb == a.dump_t && i == a.dump_i) ? a.dump : nullptr;
-        if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
-        else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, brow, i, key, a.N, lane, h, p, DUMP ? dp : nullptr);
+        v16f dpe[2];
+        if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, kbias, i, key, a.N, lane, h, p, dpe, vh, DUMP ? dp : nullptr);
+        else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, kbias, i, key, a.N, lane, h, p, dpe, vh, DUMP ? dp : nullptr);
         // P codes per 32x32 block (query half qb x this wave's keys)
         int eP[2];
         v4i pc[2];
@@ -1084,26 +1115,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
                 dv[db] = mfma_fp8(pa, cat8(sm.do_t[buf][(db * 2 + 0) * 64 + lane], sm.do_t[buf][(db * 2 + 1) * 64 + lane]),
                                   dv[db], pe, ebyte(do_w, 2 * h + db));
         }
-        // dS = P * (dO V^T - Delta) (FP16 MFMA, -Delta as the accumulator input)
+        // dS = P * (dP - Delta)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int row = 32 * qb + l32;
-            v16f nd;
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 d4 = *(const float4*)&sm.lse2[buf][64 + 32 * qb + 8 * r4 + 4 * h];
-                nd[4 * r4 + 0] = d4.x;
-                nd[4 * r4 + 1] = d4.y;
-                nd[4 * r4 + 2] = d4.z;
-                nd[4 * r4 + 3] = d4.w;
-            }
-            v16f dpd = mfma_f16(sm.do16[buf][swz(row, 0 + h)], vh[0], nd);
-            dpd = mfma_f16(sm.do16[buf][swz(row, 2 + h)], vh[1], dpd);
-            dpd = mfma_f16(sm.do16[buf][swz(row, 4 + h)], vh[2], dpd);
-            dpd = mfma_f16(sm.do16[buf][swz(row, 6 + h)], vh[3], dpd);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpd[r];
-        }
+            for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpe[qb][r];
         int eS[2];
         v4i dc[2];
 #pragma unroll
