@@ -62,3 +62,33 @@ def test_graph_replay_bitwise(w, mode):
                                r.view(torch.int16) if r.dtype == torch.bfloat16 else r.view(torch.int32)), \
                 f"replay {rep}: {name} differs from the eager call"
         print(f"  replay {rep}: O, LSE, dQ, dK, dV bitwise equal to the eager calls", flush=True)
+
+
+def test_graph_replay_fp4_forward():
+    """The FP4 inference forward captured alone replays bit for bit too."""
+    w = W.custom(1, 2, 260, True, True, True, "kbias", 73)
+    print(f"[graph fp4] {w.name} B{w.B} H{w.H} N{w.N} causal={w.causal}", flush=True)
+    x = W.make_inputs(w)
+    q, k, v = (G.dev(x[n]) for n in ("q", "k", "v"))
+    flags = (w.causal, w.smooth_q, w.smooth_k)
+    B, H, N, _ = q.shape
+    nf = sb.workspace_size(B, H, N, *flags, fp4=True)
+    ws = torch.empty(nf, dtype=torch.uint8, device="cuda")
+    o_e, lse_e = sb.fwd(q, k, v, *flags, workspace=ws, fp4=True)
+    torch.cuda.synchronize()
+    ws2 = torch.empty_like(ws)
+    o, lse = torch.empty_like(o_e), torch.empty_like(lse_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sb.fwd(q, k, v, *flags, workspace=ws2, out=(o, lse), fp4=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws2.fill_(0x3C)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"replay {rep}: O"
+        assert torch.equal(lse.view(torch.int32), lse_e.view(torch.int32)), f"replay {rep}: LSE"
+        print(f"  replay {rep}: O, LSE bitwise equal to the eager call", flush=True)
