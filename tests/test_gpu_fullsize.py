@@ -238,3 +238,39 @@ def test_max_n(mode):
         err = M.rel_l2(dq_g, dq_f)
         print(f"  dQ rel-L2 vs oracle {err:.2e}", flush=True)
         assert np.all(np.isfinite(dq_g)) and err <= 1e-2
+
+
+def test_max_heads():
+    """The largest B*H the ABI accepts (65 535 heads of N = 65, causal, both
+    smoothings): forward and backward run over the whole grid, and four heads
+    spread over it (first, second, middle, last) are compared with the
+    oracle: O and LSE, and dQ, dK, dV with both sides given the GPU's O and
+    LSE.  The other heads hold a copy of head 0's inputs (heads are
+    independent; only the grid size matters there)."""
+    B, H, N = 1, 65535, 65
+    w = W.custom(B, H, N, True, True, True, "kbias", 320)
+    sample = [0, 1, 32767, 65534]
+    print(f"[max heads] B{B} H{H} N{N} causal sampled heads {sample}", flush=True)
+    heads = {h: W.make_head(w, 0, h) for h in sample}
+    x = {n: np.empty((B, H, N, 64), np.uint16) for n in ("q", "k", "v", "do")}
+    for n in x:
+        x[n][0, :] = heads[0][n]
+        for h in sample:
+            x[n][0, h] = heads[h][n]
+    tq, tk, tv, tdo = (G.dev(x[n]) for n in ("q", "k", "v", "do"))
+    del x
+    o, lse = sb.fwd(tq, tk, tv, True, True, True)
+    dq, dk, dv = sb.bwd(tq, tk, tv, o, lse, tdo, True, True, True)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    for h in sample:
+        f = {n: W.bf16_bits_to_f32(heads[h][n])[None, None] for n in heads[h]}
+        o_f, lse_f = F.fwd(f["q"], f["k"], f["v"], True, True, True)
+        o_g = G.host_f32(o[0, h:h + 1])[None]
+        lse_g = lse[0, h].cpu().numpy()
+        G.parity("O", o_g, o_f, "int8", f" (head {h})")
+        assert np.max(np.abs(lse_g - lse_f[0, 0])) <= 2e-3
+        ref = F.bwd(f["q"], f["k"], f["v"], o_g, lse_g[None, None].astype(np.float32), f["do"], True, True, True)
+        for name, t, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            G.parity(name, G.host_f32(t[0, h:h + 1])[None], r, "int8", f" (head {h})")
