@@ -59,8 +59,9 @@ __device__ __forceinline__ float half_sum32(float v) {
 // Maximum over the 64 lanes of a wave of non-negative floats, returned as a
 // uniform value.  Non-negative floats order like their bit patterns, so the
 // reduction runs on unsigned integers: DPP within each 16-lane row, then two
-// DPP row broadcasts that leave the maximum in lane 63, read once.
-__device__ __forceinline__ float wave_max64(float f) {
+// DPP row broadcasts that leave the maximum in lane 63 (wave_max64_v returns
+// that register, for a store from lane 63; wave_max64 reads it once).
+__device__ __forceinline__ uint32_t wave_max64_v(float f) {
     uint32_t v = __float_as_uint(f);
     v = umax(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
     v = umax(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
@@ -72,7 +73,10 @@ __device__ __forceinline__ float wave_max64(float f) {
     // their own value)
     v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
     v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
-    return __uint_as_float(__builtin_amdgcn_readlane(v, 63));
+    return v;
+}
+__device__ __forceinline__ float wave_max64(float f) {
+    return __uint_as_float(__builtin_amdgcn_readlane(wave_max64_v(f), 63));
 }
 
 // Four signed codes rne(x * inv) packed into one dword.
@@ -102,6 +106,18 @@ __device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_wave_base)
 __device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_wave_base) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                      (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
+}
+// The same through a raw buffer resource: the address is the resource's base
+// plus a per-lane byte offset (a VGPR) plus a wave-uniform byte offset (an
+// SGPR), so a stream walked block by block costs no vector-ALU address
+// arithmetic per copy; reads beyond the resource's size return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bdma16_to_lds(rsrc_t r, uint32_t lane_off, uint32_t wave_off, void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, lane_off,
+                                             wave_off, 0, 0);
 }
 // Wait for this wave's outstanding vector-memory loads (LDS DMA included).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -150,7 +166,7 @@ struct DkdvSmem {
     v8h do16[DKDV_BUFS][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
     float lse2[DKDV_BUFS][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta of the query block
     float qs[DKDV_BUFS][4];      // [0]: Q block scale, [1]: dO block scale
-    float red[2][8];             // by step parity: partial tile maxima of P [0, 4) and |dS| [4, 8), per wave
+    alignas(16) float red[DKDV_BUFS][2][4];   // partial tile maxima [key block][P, P, |dS|, |dS| of its two waves]
 };
 
 // P for one 64-query x 32-key half tile in the S layout (lane = key,
@@ -299,19 +315,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     const v4i* qrg = (const v4i*)(a.q_r + bt * 4096);
     const v4i* qtg = (const v4i*)(a.q_t + bt * 4096);
     const v4i* dtg = (const v4i*)(a.do_t + bt * 4096);
-    auto fetch = [&](int i, int b) {
-        dma16_to_lds(qrg + (size_t)i * 256 + tid, &sm.q_r[b][64 * wave]);
-        dma16_to_lds(qtg + (size_t)i * 256 + tid, &sm.q_t[b][64 * wave]);
-        dma16_to_lds(dtg + (size_t)i * 256 + tid, &sm.do_t[b][64 * wave]);
-        if (INT8DP) {
-            dma16_to_lds((const v4i*)(a.do_r + bt * 4096) + (size_t)i * 256 + tid, (v4i*)sm.do16[b] + 64 * wave);
-        } else {
-            const v4i* hs = (const v4i*)(a.do16 + (rowbase + (size_t)i * BLK) * HD);
+    // the head's code blocks and FP16 dO rows as buffer resources: per-lane
+    // offsets fixed, the block's offset wave-uniform
+    const uint32_t cb = (uint32_t)T * 4096u;
+    const rsrc_t r_qr = raw_rsrc(qrg, cb), r_qt = raw_rsrc(qtg, cb), r_dt = raw_rsrc(dtg, cb);
+    const rsrc_t r_do = INT8DP ? raw_rsrc(a.do_r + bt * 4096, cb) : raw_rsrc(a.do16 + rowbase * HD, 2u * cb);
+    const uint32_t off16 = 16u * (uint32_t)tid;
+    uint32_t offh[2];   // byte offset of this lane's chunk of a swizzled FP16 dO block, j = 0, 1
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int s = 256 * j + tid, row = s / 8;
-                dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
-            }
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t s = 256u * j + (uint32_t)tid, row = s / 8;
+        offh[j] = 16u * (row * 8 + ((s % 8) ^ ((row >> 1) & 7)));
+    }
+    auto fetch = [&](int i, int b) {
+        bdma16_to_lds(r_qr, off16, (uint32_t)i * 4096u, &sm.q_r[b][64 * wave]);
+        bdma16_to_lds(r_qt, off16, (uint32_t)i * 4096u, &sm.q_t[b][64 * wave]);
+        bdma16_to_lds(r_dt, off16, (uint32_t)i * 4096u, &sm.do_t[b][64 * wave]);
+        if (INT8DP) {
+            bdma16_to_lds(r_do, off16, (uint32_t)i * 4096u, (v4i*)sm.do16[b] + 64 * wave);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bdma16_to_lds(r_do, offh[j], (uint32_t)i * 8192u, (v4i*)sm.do16[b] + 256 * j + 64 * wave);
         }
         if (wave == 0 && lane < 32)
             dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
@@ -327,9 +352,12 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     lds_barrier();
     const bool ragged_keys = (kvb == T - 1) && (a.N & (BLK - 1)) != 0;
     // One barrier per step.  Before it: the scores, P, dP - Delta and dS of
-    // the step and both partial tile maxima (P and |dS|), written to LDS by
-    // step parity.  After it: both block scales, the P and dS codes, and the
-    // dV and dK products.  Query block i sits in LDS buffer (i - i0) % 3; the
+    // the step and both partial tile maxima (P and |dS|), written to LDS in
+    // the slots of the step's buffer (lane 63 holds the wave's maximum; the
+    // slots are rewritten three steps later, when every wave has read them).
+    // After it: both block scales (the pair's four maxima in one 16-byte
+    // read), the P and dS codes, and the dV and dK products.  Query block i
+    // sits in LDS buffer (i - i0) % 3; the
     // DMA of block i + 2 is issued right after step i's barrier (its buffer
     // was last read in step i - 1, which every wave has finished by then) and
     // waited for before step i + 1's barrier, a whole step later.  The loop
@@ -338,7 +366,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
     // immediate).
     auto step = [&](int i, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const int par = i & 1;
         const bool active = live && (!CAUSAL || i >= kvb);
         const bool masked = (CAUSAL && i == kvb) || ragged_keys;
         float p[2][16], ds[2][16];           // [qb]: lane = key, regs = queries
@@ -367,8 +394,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 pm0 = umax(pm0, umax(__float_as_uint(p[0][r]), __float_as_uint(p[0][r + 1])));
                 pm1 = umax(pm1, umax(__float_as_uint(p[1][r]), __float_as_uint(p[1][r + 1])));
             }
-            const float pm = wave_max64(__uint_as_float(umax(pm0, pm1)));
-            if (lane == 0) sm.red[par][wave] = pm;
+            const uint32_t pm = wave_max64_v(__uint_as_float(umax(pm0, pm1)));
+            if (lane == 63) sm.red[buf][wave / 2][kh] = __uint_as_float(pm);
             // dS = P * (dP - Delta)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -380,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
                 m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
             }
-            const float dsm = wave_max64(max3f(m0, m1, m1));
-            if (lane == 0) sm.red[par][4 + wave] = dsm;
+            const uint32_t dsm = wave_max64_v(max3f(m0, m1, m1));
+            if (lane == 63) sm.red[buf][wave / 2][2 + kh] = __uint_as_float(dsm);
             if (DUMP && dp) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -408,11 +435,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             // both partial maxima are >= 0: the larger is the larger bit pattern
             float sP, invP, sdS, invdS;
-            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[par][wave]), __float_as_uint(sm.red[par][wave ^ 1]))),
-                        sP, invP);
-            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[par][4 + wave]),
-                                             __float_as_uint(sm.red[par][4 + (wave ^ 1)]))),
-                        sdS, invdS);
+            const v4i rm = *(const v4i*)&sm.red[buf][wave / 2][0];
+            block_scale(__uint_as_float(umax((uint32_t)rm[0], (uint32_t)rm[1])), sP, invP);
+            block_scale(__uint_as_float(umax((uint32_t)rm[2], (uint32_t)rm[3])), sdS, invdS);
             // P codes, then the dV products; the dS codes are formed while
             // they run, then the dK products, under which dV is updated
             v4i pc[2], dc[2];
@@ -575,7 +600,7 @@ struct DqSmem {
                              // all-INT8 dO V^T: V row-operand codes in its first 4 KB
     float bias[DQ_BUFS][64]; // Q-smoothing key bias (log2 domain; 0 without Q-smoothing)
     float sk[DQ_BUFS][4];    // [0]: K block scale (MXFP8: its exponent word), [1]: V block scale (all-INT8)
-    float red[2][4];         // partial |dS| maxima per wave, by step parity (INT8)
+    alignas(8) float red[DQ_BUFS][2][2];   // partial |dS| maxima [query block][its two waves] (INT8)
 };
 
 // dQ (x 1/8) in bf16; with QK-norm dQ = r (dQ_n - Q_n mean_c(dQ_n Q_n)), the
@@ -762,19 +787,28 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
 
     const v4i* kg = (const v4i*)(a.k_r + bt * 4096);
     const v4i* ktg = (const v4i*)(a.k_t + bt * 4096);
-    auto fetch = [&](int t, int b) {
-        dma16_to_lds(kg + (size_t)t * 256 + tid, &sm.k[b][64 * wave]);
-        dma16_to_lds(ktg + (size_t)t * 256 + tid, &sm.kt[b][64 * wave]);
-        if (INT8DP) {
-            dma16_to_lds((const v4i*)(a.v_r + bt * 4096) + (size_t)t * 256 + tid, (v4i*)sm.v16[b] + 64 * wave);
-        } else {
-            // LDS slot s of the FP16 V tile holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
-            const v4i* hs = (const v4i*)(a.v16 + (rowbase + (size_t)t * BLK) * HD);
+    // the head's code blocks and FP16 V rows as buffer resources: per-lane
+    // offsets fixed, the block's offset wave-uniform
+    const uint32_t cb = (uint32_t)T * 4096u;
+    const rsrc_t r_k = raw_rsrc(kg, cb), r_kt = raw_rsrc(ktg, cb);
+    const rsrc_t r_v = INT8DP ? raw_rsrc(a.v_r + bt * 4096, cb) : raw_rsrc(a.v16 + rowbase * HD, 2u * cb);
+    const uint32_t off16 = 16u * (uint32_t)tid;
+    // LDS slot s of the FP16 V tile holds global chunk (s / 8, (s % 8) ^ (s / 16 % 8)), the swizzled layout
+    uint32_t offh[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int s = 256 * j + tid, row = s / 8;
-                dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.v16[b] + 256 * j + 64 * wave);
-            }
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t s = 256u * j + (uint32_t)tid, row = s / 8;
+        offh[j] = 16u * (row * 8 + ((s % 8) ^ ((row >> 1) & 7)));
+    }
+    auto fetch = [&](int t, int b) {
+        bdma16_to_lds(r_k, off16, (uint32_t)t * 4096u, &sm.k[b][64 * wave]);
+        bdma16_to_lds(r_kt, off16, (uint32_t)t * 4096u, &sm.kt[b][64 * wave]);
+        if (INT8DP) {
+            bdma16_to_lds(r_v, off16, (uint32_t)t * 4096u, (v4i*)sm.v16[b] + 64 * wave);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bdma16_to_lds(r_v, offh[j], (uint32_t)t * 8192u, (v4i*)sm.v16[b] + 256 * j + 64 * wave);
         }
         if (wave == 2 && lane < 16) dma16_to_lds(a.bias + rowbase + (size_t)t * BLK + 4 * lane, &sm.bias[b][0]);
         if (wave == 3 && lane < (INT8DP ? 2 : 1)) dma4_to_lds((lane == 0 ? a.sk : a.sv) + bt + t, &sm.sk[b][0]);
@@ -815,8 +849,8 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
                     m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
                     m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
                 }
-                const float dsm = wave_max64(__builtin_fmaxf(m0, m1));
-                if (lane == 0) sm.red[t & 1][wave] = dsm;
+                const uint32_t dsm = wave_max64_v(__builtin_fmaxf(m0, m1));
+                if (lane == 63) sm.red[buf][wave / 2][qhalf] = __uint_as_float(dsm);
             }
         }
         // this wave's DMA of step t + 1 (issued a step ago) has landed; after
@@ -858,9 +892,8 @@ __global__ __launch_bounds__(256, 3) void k_bwd_dq(BwdArgs a) {
         } else {
             float sdS, invdS;
             // both partial maxima are >= 0: the larger is the larger bit pattern
-            block_scale(__uint_as_float(umax(__float_as_uint(sm.red[t & 1][wave]),
-                                             __float_as_uint(sm.red[t & 1][wave ^ 1]))),
-                        sdS, invdS);
+            const v2i rm = *(const v2i*)&sm.red[buf][wave / 2][0];
+            block_scale(__uint_as_float(umax((uint32_t)rm[0], (uint32_t)rm[1])), sdS, invdS);
             v4i dc[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
