@@ -338,9 +338,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             for (int j = 0; j < 2; ++j)
                 bdma16_to_lds(r_do, offh[j], (uint32_t)i * 8192u, (v4i*)sm.do16[b] + 256 * j + 64 * wave);
         }
-        if (wave == 0 && lane < 32)
-            dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
-        if (wave == 1 && lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
+        // wave-uniform branches first, so the other waves skip them on the scalar unit
+        if (wave == 0) {
+            if (lane < 32)
+                dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16),
+                             &sm.lse2[b][0]);
+        } else if (wave == 1) {
+            if (lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
+        }
     };
 
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
@@ -387,14 +392,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                     for (int r = 0; r < 16; ++r)
                         dump_at<float>(dp, dumpoff::F1)[(32 * qb + 8 * (r / 4) + 4 * h + (r % 4)) * 64 + (key % 64)] = p[qb][r];
             }
-            // P >= 0: its maximum is the maximum of the bit patterns
-            uint32_t pm0 = 0, pm1 = 0;
+            // one v_max3_f32 per two values (P >= 0, so the wave reduction
+            // may compare bit patterns)
+            float pm0 = 0.0f, pm1 = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                pm0 = umax(pm0, umax(__float_as_uint(p[0][r]), __float_as_uint(p[0][r + 1])));
-                pm1 = umax(pm1, umax(__float_as_uint(p[1][r]), __float_as_uint(p[1][r + 1])));
+                pm0 = max3f(pm0, p[0][r], p[0][r + 1]);
+                pm1 = max3f(pm1, p[1][r], p[1][r + 1]);
             }
-            const uint32_t pm = wave_max64_v(__uint_as_float(umax(pm0, pm1)));
+            const uint32_t pm = wave_max64_v(__builtin_fmaxf(pm0, pm1));
             if (lane == 63) sm.red[buf][wave / 2][kh] = __uint_as_float(pm);
             // dS = P * (dP - Delta)
 #pragma unroll
@@ -1102,9 +1108,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
             const int s = 256 * j + tid, row = s / 8;
             dma16_to_lds(hs + row * 8 + ((s % 8) ^ ((row >> 1) & 7)), (v4i*)sm.do16[b] + 256 * j + 64 * wave);
         }
-        if (wave == 0 && lane < 32)
-            dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16), &sm.lse2[b][0]);
-        if (wave == 1 && lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
+        // wave-uniform branches first, so the other waves skip them on the scalar unit
+        if (wave == 0) {
+            if (lane < 32)
+                dma16_to_lds((lane < 16 ? a.lse2 : a.delta) + rowbase + (size_t)i * BLK + 4 * (lane % 16),
+                             &sm.lse2[b][0]);
+        } else if (wave == 1) {
+            if (lane < 2) dma4_to_lds((lane == 0 ? a.sq : a.sdo) + bt + i, &sm.qs[b][0]);
+        }
     };
 
     v16f dk[2] = {v16f{}, v16f{}}, dv[2] = {v16f{}, v16f{}};   // [db]: lane = channel, regs = keys
