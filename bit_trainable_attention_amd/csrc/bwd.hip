@@ -96,40 +96,6 @@ __device__ __forceinline__ v4i fp8_block_codes(const float (&x)[16], float scale
 // 64 banks (with c ^ (r % 8), rows r and r + 8 would collide).
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ ((row >> 1) & 7)); }
 
-// Global -> LDS copies that bypass the registers (global_load_lds): every
-// lane of the wave moves 16 (4) bytes from its own global address to
-// lds_wave_base + 16 (4) * lane.  Completion is counted by vmcnt.
-__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4_to_lds(const void* g, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds_wave_base, 4, 0, 0);
-}
-// The same through a raw buffer resource: the address is the resource's base
-// plus a per-lane byte offset (a VGPR) plus a wave-uniform byte offset (an
-// SGPR), so a stream walked block by block costs no vector-ALU address
-// arithmetic per copy; reads beyond the resource's size return zeros.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void bdma16_to_lds(rsrc_t r, uint32_t lane_off, uint32_t wave_off, void* lds_wave_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, lane_off,
-                                             wave_off, 0, 0);
-}
-// Wait for this wave's outstanding vector-memory loads (LDS DMA included).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// Workgroup barrier for LDS traffic only: this wave's LDS operations are
-// complete, then s_barrier (a compiler memory barrier too).  Unlike
-// __syncthreads() it does not wait for this wave's global stores; the DMA
-// into LDS is waited for explicitly before it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // Workgroup -> (head, group) as in the forward: causal grids deal the
 // longest group of every head first (longest_first), others keep the groups
 // of a head on one XCD when the head count allows.  first_small selects which

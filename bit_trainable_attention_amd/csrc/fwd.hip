@@ -8,14 +8,15 @@
 //
 // Work split (gfx950): a workgroup of 4 waves owns 128 query rows (two
 // quantization blocks of Q); each wave owns 32 of them.  The K and V code
-// tiles of each 64-key step are loaded once per workgroup into LDS, double
-// buffered and fetched one step ahead, and every wave reads its MFMA operands
-// from there (16 bytes per lane per 32x32 operand).  Computing S^T rather than
-// S puts one query per lane column, so every softmax row statistic lives in
-// one lane and its partner in the other half-wave, and the P~ codes leave the
-// accumulator already in the B-operand layout of V^T P~^T.  Every kernel
-// stays within 256 registers per wave (at least two waves per SIMD; the
-// causal INT8 kernel needs 126, so four fit).  Causal grids start the longest
+// tiles of each 64-key step go global -> LDS once per workgroup by DMA
+// (buffer loads into LDS, no registers held), double buffered and fetched one
+// step ahead, and every wave reads its MFMA operands from there (16 bytes per
+// lane per 32x32 operand).  Computing S^T rather than S puts one query per
+// lane column, so every softmax row statistic lives in one lane and its
+// partner in the other half-wave, and the P~ codes leave the accumulator
+// already in the B-operand layout of V^T P~^T.  The causal kernels are held
+// to 128 registers per wave (four waves per SIMD), the non-causal INT8 one to
+// 168 (three); the other non-causal ones take up to 256.  Causal grids start the longest
 // query groups of all heads first; non-causal ones deal the workgroups of one
 // head to one XCD when the head count allows (its K/V codes then stay in
 // that XCD's L2).
@@ -184,7 +185,7 @@ __device__ __forceinline__ void fwd_tile(const FwdSmem& sm, int buf, const v4i (
 }
 
 template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
+__global__ __launch_bounds__(256, CAUSAL ? 4 : 3) void k_fwd(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
@@ -212,14 +213,20 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     const int q = qblk * BLK + 32 * qhalf + l32;
     uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
-    // prologue: tile 0 into buffer 0
-    v4i pk = kg[tid], pv = vg[tid];
-    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
-    sm.k[0][tid] = pk;
-    sm.v[0][tid] = pv;
-    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
-    __syncthreads();
+    // key block t's K and V code blocks (and key bias) -> LDS buffer b by DMA
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const rsrc_t r_k = raw_rsrc(kg, (uint32_t)T * 4096u), r_v = raw_rsrc(vg, (uint32_t)T * 4096u);
+    const rsrc_t r_b = raw_rsrc(bg, (uint32_t)T * 256u);
+    const uint32_t off16 = 16u * (uint32_t)tid;
+    auto fetch = [&](int t, int b) {
+        bdma16_to_lds(r_k, off16, (uint32_t)t * 4096u, &sm.k[b][64 * wave_u]);
+        bdma16_to_lds(r_v, off16, (uint32_t)t * 4096u, &sm.v[b][64 * wave_u]);
+        if (SMOOTHQ && wave_u == 0 && lane < 16)
+            bdma16_to_lds(r_b, 16u * (uint32_t)lane, (uint32_t)t * 256u, &sm.bias[b][0]);
+    };
+    fetch(0, 0);
+    wait_vmem();
+    lds_barrier();
 
     float M = -__builtin_inff();   // reference max (log2), raised lazily
     float L = 0.0f;                // sum over tiles of exp2(m_t - M) * (code sum of this half-wave)
@@ -228,11 +235,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
     auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
-        if (more) {
-            pk = kg[(size_t)(t + 1) * 256 + tid];
-            pv = vg[(size_t)(t + 1) * 256 + tid];
-            if (SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
-        }
+        // buffer buf ^ 1 was last read in step t - 1, which every wave has
+        // finished; the copy is waited for before this step's barrier
+        if (more) fetch(t + 1, buf ^ 1);
         if (live && t <= t_last) {
             const float sc = tile_scale(sQ, a.sk[bt + t]);
             const float sv = a.sv[bt + t];
@@ -244,12 +249,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd(FwdArgs a) {
                 fwd_tile<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sc, sv, t, q, a.N, lane, h, M, L, O, dp,
                                                        32 * qhalf + l32);
         }
-        if (more) {
-            sm.k[buf ^ 1][tid] = pk;
-            sm.v[buf ^ 1][tid] = pv;
-            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
-        }
-        __syncthreads();
+        wait_vmem();
+        lds_barrier();
     };
     // Only the last two steps can hold a masked tile (the causal diagonal
     // and the ragged last key block come last), so they run in a loop of
@@ -397,7 +398,7 @@ __device__ __forceinline__ void fwd_tile_mx(const FwdSmem& sm, int buf, v8i qop,
 }
 
 template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
+__global__ __launch_bounds__(256, CAUSAL ? 4 : 2) void k_fwd_mx(FwdArgs a) {
     __shared__ FwdSmem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
@@ -431,13 +432,20 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     const int q = qblk * BLK + 32 * qhalf + l32;
     uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
-    v4i pk = kg[tid], pv = vg[tid];
-    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
-    sm.k[0][tid] = pk;
-    sm.v[0][tid] = pv;
-    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
-    __syncthreads();
+    // key block t's K and V code blocks (and key bias) -> LDS buffer b by DMA
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const rsrc_t r_k = raw_rsrc(kg, (uint32_t)T * 4096u), r_v = raw_rsrc(vg, (uint32_t)T * 4096u);
+    const rsrc_t r_b = raw_rsrc(bg, (uint32_t)T * 256u);
+    const uint32_t off16 = 16u * (uint32_t)tid;
+    auto fetch = [&](int t, int b) {
+        bdma16_to_lds(r_k, off16, (uint32_t)t * 4096u, &sm.k[b][64 * wave_u]);
+        bdma16_to_lds(r_v, off16, (uint32_t)t * 4096u, &sm.v[b][64 * wave_u]);
+        if (SMOOTHQ && wave_u == 0 && lane < 16)
+            bdma16_to_lds(r_b, 16u * (uint32_t)lane, (uint32_t)t * 256u, &sm.bias[b][0]);
+    };
+    fetch(0, 0);
+    wait_vmem();
+    lds_barrier();
 
     float M = -__builtin_inff();   // running row maximum (log2)
     v16f O[2] = {v16f{}, v16f{}};  // [db]: lane = query, registers = channels
@@ -446,11 +454,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
     auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
-        if (more) {
-            pk = kg[(size_t)(t + 1) * 256 + tid];
-            pv = vg[(size_t)(t + 1) * 256 + tid];
-            if (SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
-        }
+        // buffer buf ^ 1 was last read in step t - 1, which every wave has
+        // finished; the copy is waited for before this step's barrier
+        if (more) fetch(t + 1, buf ^ 1);
         if (live && t <= t_last) {
             const uint32_t sk_w = skw[t], sv_w = svw[t];
             uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
@@ -461,12 +467,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_mx(FwdArgs a) {
                 fwd_tile_mx<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sq_e, sk_w, sv_w, t, q, a.N, lane, h, M, O,
                                                           Lacc, ones, e_one, e_pt, dp, 32 * qhalf + l32);
         }
-        if (more) {
-            sm.k[buf ^ 1][tid] = pk;
-            sm.v[buf ^ 1][tid] = pv;
-            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
-        }
-        __syncthreads();
+        wait_vmem();
+        lds_barrier();
     };
     // Only the last two steps can hold a masked tile (the causal diagonal
     // and the ragged last key block come last), so they run in a loop of
@@ -615,7 +617,7 @@ __device__ __forceinline__ void fwd_tile_fp4(const FwdFp4Smem& sm, int buf, v4i 
 }
 
 template <bool CAUSAL, bool SMOOTHQ, bool DUMP>
-__global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
+__global__ __launch_bounds__(256, CAUSAL ? 4 : 2) void k_fwd_fp4(FwdArgs a) {
     __shared__ FwdFp4Smem sm;
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     int bh, g;
@@ -641,18 +643,25 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     }
     const int e_one = opaque(E8M0_ONE);
     const int q = qblk * BLK + 32 * qhalf + l32;
-    const bool loader = tid < 136;
     uint8_t* dp_sel = (DUMP && bh == a.dump_bh && qblk == a.dump_i) ? a.dump : nullptr;
 
-    v4i pk = loader ? kg[tid] : v4i{}, pv = loader ? vg[tid] : v4i{};
-    float4 pb = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (SMOOTHQ && tid < 16) pb = ((const float4*)bg)[tid];
-    if (loader) {
-        sm.k[0][tid] = pk;
-        sm.v[0][tid] = pv;
-    }
-    if (SMOOTHQ && tid < 16) ((float4*)sm.bias[0])[tid] = pb;
-    __syncthreads();
+    // key block t's K and V FP4 blocks (136 chunks of 16 bytes: waves 0 and
+    // 1 and lanes 0-7 of wave 2) and key bias -> LDS buffer b by DMA
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const rsrc_t r_k = raw_rsrc(kg, (uint32_t)T * 4096u), r_v = raw_rsrc(vg, (uint32_t)T * 4096u);
+    const rsrc_t r_b = raw_rsrc(bg, (uint32_t)T * 256u);
+    const uint32_t off16 = 16u * (uint32_t)tid;
+    auto fetch = [&](int t, int b) {
+        if (wave_u < 2 || (wave_u == 2 && lane < 8)) {
+            bdma16_to_lds(r_k, off16, (uint32_t)t * 4096u, &sm.k[b][64 * wave_u]);
+            bdma16_to_lds(r_v, off16, (uint32_t)t * 4096u, &sm.v[b][64 * wave_u]);
+        }
+        if (SMOOTHQ && wave_u == 3 && lane < 16)
+            bdma16_to_lds(r_b, 16u * (uint32_t)lane, (uint32_t)t * 256u, &sm.bias[b][0]);
+    };
+    fetch(0, 0);
+    wait_vmem();
+    lds_barrier();
 
     float M = -__builtin_inff();
     v16f O[2] = {v16f{}, v16f{}};
@@ -661,11 +670,9 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
     auto step = [&](int t, auto maybe_masked) {
         const int buf = t & 1;
         const bool more = t < t_last_wg;
-        if (more && loader) {
-            pk = kg[(size_t)(t + 1) * 256 + tid];
-            pv = vg[(size_t)(t + 1) * 256 + tid];
-        }
-        if (more && SMOOTHQ && tid < 16) pb = ((const float4*)(bg + (t + 1) * BLK))[tid];
+        // buffer buf ^ 1 was last read in step t - 1, which every wave has
+        // finished; the copy is waited for before this step's barrier
+        if (more) fetch(t + 1, buf ^ 1);
         if (live && t <= t_last) {
             uint8_t* dp = (DUMP && t == a.dump_t) ? dp_sel : nullptr;
             if (decltype(maybe_masked)::value && ((CAUSAL && t == qblk) || (ragged && t == T - 1)))
@@ -675,14 +682,8 @@ __global__ __launch_bounds__(256, 2) void k_fwd_fp4(FwdArgs a) {
                 fwd_tile_fp4<CAUSAL, SMOOTHQ, false, DUMP>(sm, buf, qop, sq_e, t, q, a.N, lane, h, l32, M, O, Lacc,
                                                            e_one, dp, 32 * qhalf + l32);
         }
-        if (more) {
-            if (loader) {
-                sm.k[buf ^ 1][tid] = pk;
-                sm.v[buf ^ 1][tid] = pv;
-            }
-            if (SMOOTHQ && tid < 16) ((float4*)sm.bias[buf ^ 1])[tid] = pb;
-        }
-        __syncthreads();
+        wait_vmem();
+        lds_barrier();
     };
     // Only the last two steps can hold a masked tile (the causal diagonal
     // and the ragged last key block come last), so they run in a loop of
