@@ -78,6 +78,25 @@ __device__ __forceinline__ uint32_t wave_max64_v(float f) {
 __device__ __forceinline__ float wave_max64(float f) {
     return __uint_as_float(__builtin_amdgcn_readlane(wave_max64_v(f), 63));
 }
+// Two such maxima with their reduction steps interleaved (the two
+// dependency chains fill each other's DPP wait states).
+__device__ __forceinline__ void wave_max64x2(float f0, float f1, float& m0, float& m1) {
+    uint32_t v = __float_as_uint(f0), w = __float_as_uint(f1);
+    v = umax(v, dppu<0xB1>(v));
+    w = umax(w, dppu<0xB1>(w));
+    v = umax(v, dppu<0x4E>(v));
+    w = umax(w, dppu<0x4E>(w));
+    v = umax(v, dppu<0x141>(v));
+    w = umax(w, dppu<0x141>(w));
+    v = umax(v, dppu<0x140>(v));
+    w = umax(w, dppu<0x140>(w));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+    w = umax(w, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x142, 0xA, 0xF, false));
+    v = umax(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+    w = umax(w, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, 0x143, 0xC, 0xF, false));
+    m0 = __uint_as_float(__builtin_amdgcn_readlane(v, 63));
+    m1 = __uint_as_float(__builtin_amdgcn_readlane(w, 63));
+}
 
 // Four signed codes rne(x * inv) packed into one dword.
 __device__ __forceinline__ int pack_codes(float x0, float x1, float x2, float x3, float inv) {
@@ -132,7 +151,7 @@ struct DkdvSmem {
     v8h do16[DKDV_BUFS][512];    // dO in FP16, [64 rows][8 chunks], swizzled (A operand of dO V^T)
     float lse2[DKDV_BUFS][128];  // [0, 64): log2-domain LSE, [64, 128): -Delta of the query block
     float qs[DKDV_BUFS][4];      // [0]: Q block scale, [1]: dO block scale
-    alignas(16) float red[DKDV_BUFS][2][4];   // partial tile maxima [key block][P, P, |dS|, |dS| of its two waves]
+    alignas(16) float red[DKDV_BUFS][2][4];   // partial tile maxima [key block][P, |dS| of wave 0, P, |dS| of wave 1]
 };
 
 // P for one 64-query x 32-key half tile in the S layout (lane = key,
@@ -366,8 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 pm0 = max3f(pm0, p[0][r], p[0][r + 1]);
                 pm1 = max3f(pm1, p[1][r], p[1][r + 1]);
             }
-            const uint32_t pm = wave_max64_v(__builtin_fmaxf(pm0, pm1));
-            if (lane == 63) sm.red[buf][wave / 2][kh] = __uint_as_float(pm);
+            const float pml = __builtin_fmaxf(pm0, pm1);
             // dS = P * (dP - Delta)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
@@ -379,8 +397,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
                 m0 = max_abs2f(m0, ds[0][r], ds[0][r + 1]);
                 m1 = max_abs2f(m1, ds[1][r], ds[1][r + 1]);
             }
+            // both wave reductions, then one 8-byte store from lane 63
+            const uint32_t pm = wave_max64_v(pml);
             const uint32_t dsm = wave_max64_v(max3f(m0, m1, m1));
-            if (lane == 63) sm.red[buf][wave / 2][2 + kh] = __uint_as_float(dsm);
+            if (lane == 63) *(v2i*)&sm.red[buf][wave / 2][2 * kh] = v2i{(int)pm, (int)dsm};
             if (DUMP && dp) {
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -408,8 +428,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv(BwdArgs a) {
             // both partial maxima are >= 0: the larger is the larger bit pattern
             float sP, invP, sdS, invdS;
             const v4i rm = *(const v4i*)&sm.red[buf][wave / 2][0];
-            block_scale(__uint_as_float(umax((uint32_t)rm[0], (uint32_t)rm[1])), sP, invP);
-            block_scale(__uint_as_float(umax((uint32_t)rm[2], (uint32_t)rm[3])), sdS, invdS);
+            block_scale(__uint_as_float(umax((uint32_t)rm[0], (uint32_t)rm[2])), sP, invP);
+            block_scale(__uint_as_float(umax((uint32_t)rm[1], (uint32_t)rm[3])), sdS, invdS);
             // P codes, then the dV products; the dS codes are formed while
             // they run, then the dK products, under which dV is updated
             v4i pc[2], dc[2];
@@ -1107,12 +1127,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         // P codes per 32x32 block (query half qb x this wave's keys)
         int eP[2];
         v4i pc[2];
+        float pmx[2];
+        {
+            float pm[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) pm[qb] = max3f(pm[qb], p[qb][r], p[qb][r + 1]);
+            wave_max64x2(pm[0], pm[1], pmx[0], pmx[1]);
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            uint32_t pm = 0;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) pm = umax(pm, umax(__float_as_uint(p[qb][r]), __float_as_uint(p[qb][r + 1])));
-            eP[qb] = mx_exponent(wave_max64(__uint_as_float(pm)));
+            eP[qb] = mx_exponent(pmx[qb]);
             pc[qb] = fp8_block_codes(p[qb], pow2f(eP[qb]));
             if (DUMP && dp) dump_mx_block(dp, dumpoff::F1, dumpoff::C1, dumpoff::SC, p[qb], pc[qb], eP[qb], qb, kh, h, lane, key);
         }
@@ -1132,12 +1158,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
             for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpe[qb][r];
         int eS[2];
         v4i dc[2];
+        float smx[2];
+        {
+            float m[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) m[qb] = max_abs2f(m[qb], p[qb][r], p[qb][r + 1]);
+            wave_max64x2(m[0], m[1], smx[0], smx[1]);
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            float m = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) m = max_abs2f(m, p[qb][r], p[qb][r + 1]);
-            eS[qb] = mx_exponent(wave_max64(m));
+            eS[qb] = mx_exponent(smx[qb]);
             dc[qb] = fp8_block_codes(p[qb], pow2f(eS[qb]));
             if (DUMP && dp)
                 dump_mx_block(dp, dumpoff::F2, dumpoff::C2, dumpoff::SC + 16, p[qb], dc[qb], eS[qb], qb, kh, h, lane, key);
