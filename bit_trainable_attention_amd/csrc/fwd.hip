@@ -16,10 +16,10 @@
 // partner in the other half-wave, and the P~ codes leave the accumulator
 // already in the B-operand layout of V^T P~^T.  The causal kernels are held
 // to 128 registers per wave (four waves per SIMD), the non-causal INT8 one to
-// 168 (three); the other non-causal ones take up to 256.  Causal grids start the longest
-// query groups of all heads first; non-causal ones deal the workgroups of one
-// head to one XCD when the head count allows (its K/V codes then stay in
-// that XCD's L2).
+// 168 (three); the other non-causal ones take up to 256.  Causal grids start
+// the longest query groups of all heads first; non-causal ones deal the
+// workgroups of one head to one XCD when the head count allows (its K/V
+// codes then stay in that XCD's L2).
 #include "attn.h"
 
 namespace sagebwd {
