@@ -1124,18 +1124,30 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
         v16f dpe[2];
         if (masked) dkdv_probs_mx<CAUSAL, true>(sm, buf, kop, q_w, sk_e, kbias, i, key, a.N, lane, h, p, dpe, vh, DUMP ? dp : nullptr);
         else dkdv_probs_mx<CAUSAL, false>(sm, buf, kop, q_w, sk_e, kbias, i, key, a.N, lane, h, p, dpe, vh, DUMP ? dp : nullptr);
-        // P codes per 32x32 block (query half qb x this wave's keys)
-        int eP[2];
-        v4i pc[2];
-        float pmx[2];
+        // dS = P * (dP - Delta), then the four 32x32 block maxima (P and |dS| of
+        // both query halves) reduced together, so the dS chain does not wait
+        // for the P codes and the dV products
+        float ds[2][16];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ds[qb][r] = p[qb][r] * dpe[qb][r];
+        float pmx[2], smx[2];
         {
-            float pm[2] = {0.0f, 0.0f};
+            float pm[2] = {0.0f, 0.0f}, m[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) pm[qb] = max3f(pm[qb], p[qb][r], p[qb][r + 1]);
+                for (int r = 0; r < 16; r += 2) {
+                    pm[qb] = max3f(pm[qb], p[qb][r], p[qb][r + 1]);
+                    m[qb] = max_abs2f(m[qb], ds[qb][r], ds[qb][r + 1]);
+                }
             wave_max64x2(pm[0], pm[1], pmx[0], pmx[1]);
+            wave_max64x2(m[0], m[1], smx[0], smx[1]);
         }
+        // P codes per 32x32 block (query half qb x this wave's keys)
+        int eP[2];
+        v4i pc[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             eP[qb] = mx_exponent(pmx[qb]);
@@ -1151,28 +1163,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mx(BwdArgs a) {
                 dv[db] = mfma_fp8(pa, cat8(sm.do_t[buf][(db * 2 + 0) * 64 + lane], sm.do_t[buf][(db * 2 + 1) * 64 + lane]),
                                   dv[db], pe, ebyte(do_w, 2 * h + db));
         }
-        // dS = P * (dP - Delta)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) p[qb][r] = p[qb][r] * dpe[qb][r];
         int eS[2];
         v4i dc[2];
-        float smx[2];
-        {
-            float m[2] = {0.0f, 0.0f};
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) m[qb] = max_abs2f(m[qb], p[qb][r], p[qb][r + 1]);
-            wave_max64x2(m[0], m[1], smx[0], smx[1]);
-        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             eS[qb] = mx_exponent(smx[qb]);
-            dc[qb] = fp8_block_codes(p[qb], pow2f(eS[qb]));
+            dc[qb] = fp8_block_codes(ds[qb], pow2f(eS[qb]));
             if (DUMP && dp)
-                dump_mx_block(dp, dumpoff::F2, dumpoff::C2, dumpoff::SC + 16, p[qb], dc[qb], eS[qb], qb, kh, h, lane, key);
+                dump_mx_block(dp, dumpoff::F2, dumpoff::C2, dumpoff::SC + 16, ds[qb], dc[qb], eS[qb], qb, kh, h, lane, key);
         }
         // dK += dS^T Q (and the dS column sums for the Q-smoothing term)
         {
